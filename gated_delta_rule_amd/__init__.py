@@ -1,0 +1,189 @@
+"""MI355X-native Kimi Delta Attention (KDA) operator.
+
+Python binding of the C ABI in include/kda.h (libkda.so, built in-tree by
+gated_delta_rule_amd.build).  This module only marshals arguments: torch
+supplies device memory and the current HIP stream, and every step of the
+operator runs in the library's HIP kernels.  If the library is missing the
+calls raise; there is no fallback.
+
+    o, S_T = chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None)
+    o = decode_step(q, k, v, log_alpha, beta, S)       # S updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["chunk_fwd", "decode_step", "chunk_fwd_workspace_bytes", "library_path",
+           "load_library", "KDAError", "KDA_BF16", "KDA_F32", "HEAD_DIM"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+KDA_BF16, KDA_F32 = 0, 1
+HEAD_DIM = 128
+_lib = None
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise KDAError(f"{_LIB_PATH} not found: build it with "
+                       "`python -m gated_delta_rule_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_status_str.argtypes = [ctypes.c_int]
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+    lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, ip, i32, i64, i32,
+                                  i32, i32, fp, fp, vp, sz, vp]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, i32, i32, i32, i32,
+                                    fp, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _status(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().kda_status_str(rc).decode()
+        raise KDAError(f"{what}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _in_dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise KDAError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, dtype=None, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise KDAError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise KDAError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise KDAError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise KDAError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise KDAError(f"{name} is on {t.device}, expected {device}")
+
+
+def chunk_fwd_workspace_bytes(n_seqs: int, T: int, H: int, varlen: bool) -> int:
+    return int(load_library().kda_chunk_fwd_workspace_bytes(n_seqs, T, H, HEAD_DIM,
+                                                            HEAD_DIM, int(varlen)))
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
+              output_final_state: bool = True, o=None, S_T=None, workspace=None):
+    """Chunkwise KDA prefill (see kda_chunk_fwd in include/kda.h).
+
+    Equal-length batch: q, k, log_alpha [B, T, H, 128]; v [B, T, H, 128];
+    beta [B, T, H].  Packed varlen batch: the same tensors with a token axis
+    [T_total, H, ...] (a leading axis of 1 is allowed) and cu_seqlens int32
+    [N+1] on the device.  S0: [N, H, 128, 128] float32 or None.
+    Returns (o float32 like v, S_T [N, H, 128, 128] float32 or None).
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    _check(log_alpha, "log_alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    dt = _in_dtype(q)
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        n_seqs = cu_seqlens.numel() - 1
+        T = q.numel() // (H * dk)
+        if q.dim() == 4 and q.shape[0] != 1:
+            raise KDAError("packed varlen input must have a leading batch of 1 or none")
+    else:
+        if q.dim() != 4:
+            raise KDAError("q must be [B, T, H, 128] without cu_seqlens")
+        n_seqs, T = q.shape[0], q.shape[1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:-1] != q.shape[:-1] \
+            or beta.shape != q.shape[:-1]:
+        raise KDAError("q/k/log_alpha/v/beta shapes disagree")
+    if S0 is not None:
+        _check(S0, "S0", torch.float32, dev)
+        if tuple(S0.shape) != (n_seqs, H, dk, dv):
+            raise KDAError(f"S0 must be {(n_seqs, H, dk, dv)}, got {tuple(S0.shape)}")
+    if o is None:
+        o = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    else:
+        _check(o, "o", torch.float32, dev)
+    if output_final_state and S_T is None:
+        S_T = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _check(S_T, "S_T", torch.float32, dev)
+    ws_bytes = int(lib.kda_chunk_fwd_workspace_bytes(n_seqs, T, H, dk, dv,
+                                                     int(cu_seqlens is not None)))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(log_alpha), _ptr(beta),
+                           _ptr(S0), _ptr(cu_seqlens), n_seqs, T, H, dk, dv, _ptr(o),
+                           _ptr(S_T), _ptr(workspace),
+                           0 if workspace is None else workspace.numel() * workspace.element_size(),
+                           ctypes.c_void_p(stream))
+    _status(rc, "kda_chunk_fwd")
+    return o, S_T
+
+
+def decode_step(q, k, v, log_alpha, beta, S, *, o=None):
+    """One KDA decode step (see kda_decode_step in include/kda.h).
+
+    q, k, log_alpha [B, H, 128]; v [B, H, 128]; beta [B, H];
+    S [B, H, 128, 128] float32, updated in place.  Returns o [B, H, 128] fp32.
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    _check(log_alpha, "log_alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(S, "S", torch.float32, dev)
+    dt = _in_dtype(q)
+    if q.dim() != 3:
+        raise KDAError("q must be [B, H, 128]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:-1] != q.shape[:-1] \
+            or beta.shape != q.shape[:-1] or tuple(S.shape) != (B, H, dk, dv):
+        raise KDAError("q/k/v/log_alpha/beta/S shapes disagree")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(o, "o", torch.float32, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(log_alpha), _ptr(beta),
+                             _ptr(S), B, H, dk, dv, _ptr(o), ctypes.c_void_p(stream))
+    _status(rc, "kda_decode_step")
+    return o

@@ -1,0 +1,188 @@
+// C ABI of the KDA operator: argument validation and kernel launches.
+// Everything here runs on the host; nothing is enqueued unless every check
+// passes.  See include/kda.h for the contract.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+
+namespace {
+
+constexpr int64_t kHeadDim = 128;
+constexpr int32_t kOrderMax = 4096;       // sequences sorted longest-first up to this count
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t bytes) {
+    uintptr_t a = (uintptr_t)p;
+    return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlaps(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+int64_t elem_size(int dtype) { return dtype == KDA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL_POINTER: return "KDA_ERR_NULL_POINTER: a required pointer is NULL";
+        case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: dk/dv must be 128, sizes non-negative, H >= 1";
+        case KDA_ERR_BAD_DTYPE: return "KDA_ERR_BAD_DTYPE: in_dtype must be KDA_BF16 or KDA_F32";
+        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: tensors need 16-byte alignment (beta, cu_seqlens 4-byte)";
+        case KDA_ERR_ALIASING: return "KDA_ERR_ALIASING: an output overlaps an input";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_TOO_LARGE: return "KDA_ERR_TOO_LARGE: sizes exceed the launch limits";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
+        default: return "unknown kda_status";
+    }
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H, int32_t dk,
+                                     int32_t dv, int varlen) {
+    (void)T;
+    (void)H;
+    if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim) return 0;
+    if (!varlen || n_seqs > kOrderMax) return 0;
+    return (size_t)n_seqs * sizeof(int32_t);
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                  const float* log_alpha, const float* beta, const float* S0,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int64_t T, int32_t H, int32_t dk,
+                  int32_t dv, float* o, float* S_T, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
+    if (dk != kHeadDim || dv != kHeadDim || H < 1 || n_seqs < 0 || T < 0)
+        return KDA_ERR_BAD_SHAPE;
+    const bool varlen = cu_seqlens != nullptr;
+    int64_t tokens = 0;  // rows of the token axis
+    if (varlen) {
+        tokens = T;
+    } else if (!mul_ok((int64_t)n_seqs, T, &tokens)) {
+        return KDA_ERR_TOO_LARGE;
+    }
+    if (n_seqs == 0) return KDA_OK;
+    int64_t rows = 0, elems = 0;
+    if (!mul_ok(tokens, (int64_t)H, &rows) || !mul_ok(rows, kHeadDim, &elems) ||
+        elems > INT64_MAX / 8)
+        return KDA_ERR_TOO_LARGE;
+    int64_t units = 0, st_elems = 0;
+    if (!mul_ok((int64_t)n_seqs, (int64_t)H, &units) ||
+        !mul_ok(units, kHeadDim * kHeadDim, &st_elems))
+        return KDA_ERR_TOO_LARGE;
+    if (units > INT32_MAX) return KDA_ERR_TOO_LARGE;
+
+    if (tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL_POINTER;
+
+    const int64_t es = elem_size(in_dtype);
+    if (tokens > 0) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) ||
+            !aligned(o, 16) || !aligned(beta, 4))
+            return KDA_ERR_MISALIGNED;
+    }
+    if ((S0 && !aligned(S0, 16)) || (S_T && !aligned(S_T, 16)) ||
+        (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return KDA_ERR_MISALIGNED;
+
+    // Aliasing: o and S_T against every input; S_T may equal S0 exactly.
+    const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+    const Range rla = span(log_alpha, elems * 4), rb = span(beta, rows * 4);
+    const Range ro = span(o, elems * 4);
+    const Range rs0 = span(S0, S0 ? st_elems * 4 : 0), rst = span(S_T, S_T ? st_elems * 4 : 0);
+    const Range rcu = span(cu_seqlens, varlen ? ((int64_t)n_seqs + 1) * 4 : 0);
+    const Range ins[] = {rq, rk, rv, rla, rb, rs0, rcu};
+    for (const Range& r : ins)
+        if (overlaps(ro, r)) return KDA_ERR_ALIASING;
+    if (overlaps(ro, rst)) return KDA_ERR_ALIASING;
+    const Range ins_no_s0[] = {rq, rk, rv, rla, rb, rcu};
+    for (const Range& r : ins_no_s0)
+        if (overlaps(rst, r)) return KDA_ERR_ALIASING;
+    if (S0 && S_T && S0 != (const float*)S_T && overlaps(rs0, rst)) return KDA_ERR_ALIASING;
+
+    const size_t need = kda_chunk_fwd_workspace_bytes(n_seqs, T, H, dk, dv, varlen ? 1 : 0);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return KDA_ERR_MISALIGNED;
+        const Range rw = span(workspace, (int64_t)need);
+        const Range all[] = {rq, rk, rv, rla, rb, rs0, rcu, ro, rst};
+        for (const Range& r : all)
+            if (overlaps(rw, r)) return KDA_ERR_ALIASING;
+    }
+
+    // Two value-column slices per head (16 columns per wave) when there are
+    // too few (sequence, head) units to cover the 256 compute units.
+    const int n_slices = units < 256 ? 2 : 1;
+    const int wcols = 128 / (4 * n_slices);
+    const int64_t grid = ((units + 7) / 8) * 8 * n_slices;
+    if (grid > kMaxGrid) return KDA_ERR_TOO_LARGE;
+
+    kda::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.la = log_alpha;
+    p.beta = beta;
+    p.S0 = S0;
+    p.cu = cu_seqlens;
+    p.order = need > 0 ? (const int32_t*)workspace : nullptr;
+    p.o = o;
+    p.S_T = S_T;
+    p.T = T;
+    p.n_seqs = n_seqs;
+    p.H = H;
+    p.n_slices = n_slices;
+    p.n_units = (int32_t)units;
+    hipError_t e = kda::launch_chunk_fwd(p, in_dtype == KDA_BF16, wcols, need > 0, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,
+                    const float* log_alpha, const float* beta, float* S, int32_t B, int32_t H,
+                    int32_t dk, int32_t dv, float* o, hipStream_t stream) {
+    if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
+    if (dk != kHeadDim || dv != kHeadDim || H < 1 || B < 0) return KDA_ERR_BAD_SHAPE;
+    if (B == 0) return KDA_OK;
+    const int64_t states = (int64_t)B * H;
+    if (states > kMaxGrid) return KDA_ERR_TOO_LARGE;
+    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_ERR_NULL_POINTER;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) ||
+        !aligned(S, 16) || !aligned(o, 16) || !aligned(beta, 4))
+        return KDA_ERR_MISALIGNED;
+    const int64_t es = elem_size(in_dtype);
+    const int64_t elems = states * kHeadDim;
+    const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+    const Range rla = span(log_alpha, elems * 4), rb = span(beta, states * 4);
+    const Range rs = span(S, states * kHeadDim * kHeadDim * 4), ro = span(o, elems * 4);
+    const Range ins[] = {rq, rk, rv, rla, rb};
+    for (const Range& r : ins)
+        if (overlaps(ro, r) || overlaps(rs, r)) return KDA_ERR_ALIASING;
+    if (overlaps(ro, rs)) return KDA_ERR_ALIASING;
+    hipError_t e = kda::launch_decode_step(q, k, v, in_dtype == KDA_BF16, log_alpha, beta, S,
+                                           states, o, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention operator.
+ *
+ * The operator is the per-head KDA recurrence with its readout,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                      (read after the update)
+ *
+ * with alpha_t = exp(log_alpha_t) (one decay per key channel) and beta_t a
+ * scalar write strength.  The state equation is the one stated in
+ * "Kimi K3 核心算子拆解" (devpress.csdn.net) section 2.2 and in
+ * "把注意力换成一块「会遗忘的内存」" (jokeuncle.github.io) section "第四步";
+ * the readout after the update in "Kimi K3 技术报告解读" (marsggbo.github.io)
+ * section 3.2.  Two entry points share these semantics: a chunkwise-parallel
+ * prefill over whole sequences and a one-token decode step that updates the
+ * state in place ("把注意力换成一块「会遗忘的内存」", section "层的实现":
+ * chunked path for training / prefill, recurrent path for decode).
+ *
+ * Common contract
+ *   - Head dimension: dk == dv == 128 (any other value -> KDA_ERR_BAD_SHAPE).
+ *   - q, k, v are in `in_dtype` (KDA_BF16 or KDA_F32); log_alpha, beta, the
+ *     states and o are float32.  log_alpha must lie in [-5, 0] (the lower-
+ *     bounded decay of "Kimi K3 技术报告解读" section 3.5); beta is used as
+ *     given (no clamping).  q and k are used as given (the caller normalises);
+ *     there is no query scale.  Values outside the log_alpha contract give
+ *     unspecified (possibly non-finite) results but never out-of-bounds
+ *     memory accesses.
+ *   - All tensor pointers are DEVICE pointers owned by the caller, which
+ *     allocates every buffer (including the workspace).  The library
+ *     allocates nothing, keeps no mutable global state, never synchronises
+ *     the host, and enqueues its kernels on `stream` (0 = the null stream).
+ *   - Every argument is validated before anything is enqueued; on error the
+ *     call returns a non-zero kda_status and has no effect.  Faults raised by
+ *     the device asynchronously surface at the caller's next synchronisation.
+ *   - Tensor pointers must be 16-byte aligned (beta and cu_seqlens 4-byte).
+ *   - Results are deterministic: no atomics; the same inputs and launch give
+ *     the same bits.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
+    KDA_ERR_BAD_SHAPE = 2,      /* dk/dv not 128, negative sizes, H < 1 */
+    KDA_ERR_BAD_DTYPE = 3,      /* in_dtype is not KDA_BF16 / KDA_F32 */
+    KDA_ERR_MISALIGNED = 4,     /* pointer alignment contract violated */
+    KDA_ERR_ALIASING = 5,       /* an output overlaps an input illegally */
+    KDA_ERR_WORKSPACE = 6,      /* workspace missing or too small */
+    KDA_ERR_TOO_LARGE = 7,      /* sizes beyond the launch limits */
+    KDA_ERR_HIP = 8             /* the kernel launch itself failed */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_BF16 = 0,
+    KDA_F32 = 1
+} kda_dtype;
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* kda_status_str(int status);
+
+/*
+ * Workspace size in bytes that kda_chunk_fwd needs for these sizes (0 when
+ * none is needed).  `varlen` != 0 when cu_seqlens will be passed.  The
+ * varlen path keeps a longest-first order of the sequences in the workspace
+ * (n_seqs int32).  Returns 0 for invalid sizes as well; kda_chunk_fwd then
+ * reports the real error.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
+                                     int32_t dk, int32_t dv, int varlen);
+
+/*
+ * Chunkwise prefill: runs the recurrence over whole sequences and returns
+ * every o_t and, optionally, each sequence's final state.  The chunkwise
+ * evaluation (cumulative in-chunk log-decay, k+ = k e^{g}, k- = k e^{-g},
+ * the strictly lower-triangular A_tj = beta_t k+_t . k-_j solved by forward
+ * substitution, O = Q+ S + Tril(Q+ K-^T) U and the state hand-off
+ * S <- Diag(e^{g_C}) S + K_end^T U) is the derivation of
+ * "尝试对Kimi KDA的数学推导&算子实现分析" (hjcheng0602.cn), eqs. (8)-(66); it
+ * gives the recurrence's result up to rounding.
+ *
+ * Layout (row-major, last index fastest):
+ *   cu_seqlens == NULL: n_seqs sequences of T tokens each;
+ *       q, k, log_alpha [n_seqs, T, H, dk]; v, o [n_seqs, T, H, dv];
+ *       beta [n_seqs, T, H].
+ *   cu_seqlens != NULL: n_seqs sequences packed along one token axis of
+ *       length T (the total); q, k, log_alpha [T, H, dk]; v, o [T, H, dv];
+ *       beta [T, H]; cu_seqlens int32 [n_seqs + 1] (device) with
+ *       cu_seqlens[0] = 0, non-decreasing, cu_seqlens[n_seqs] = T.  The
+ *       device clamps each range into [0, T] (a malformed table gives wrong
+ *       rows, never an out-of-bounds access).
+ *   S0  : [n_seqs, H, dk, dv] float32 initial states, or NULL for zeros.
+ *   S_T : [n_seqs, H, dk, dv] float32 final states, or NULL to skip.  S_T
+ *         may be the same pointer as S0 (in-place carry); any other overlap
+ *         with an input is rejected.
+ *   o   : must not overlap any input or S_T.
+ *   workspace: at least kda_chunk_fwd_workspace_bytes(...) bytes of device
+ *         memory (may be NULL when that is 0); contents need no
+ *         initialisation and are clobbered.
+ * Numerics: fp32 accumulation throughout; with KDA_BF16 inputs the matrix
+ * products run on bf16 matrix cores with split (hi + lo) bf16 operands
+ * where a single rounding would exceed 2e-3 relative error; with KDA_F32
+ * inputs every product runs on fp32 matrix cores.
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                  const float* log_alpha, const float* beta, const float* S0,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
+                  int32_t H, int32_t dk, int32_t dv, float* o, float* S_T,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step for B independent requests, updating their states in
+ * place: per (request, head) the state is decayed, corrected by the rank-1
+ * erase computed from the decayed state, written, and read after the update
+ * (the three-step method of "Kimi K3 核心算子拆解" section 2.3).  The state
+ * is streamed once: the readout uses
+ *     o = (Diag(alpha) S)^T q + beta (q . k) (v - x),  x = k^T Diag(alpha) S,
+ * which equals S_t^T q_t for the updated state.
+ *
+ * Layout: q, k, log_alpha [B, H, dk]; v [B, H, dv]; beta [B, H];
+ *         S [B, H, dk, dv] float32, read and overwritten in place;
+ *         o [B, H, dv] float32 (must not overlap any input or S).
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,
+                    const float* log_alpha, const float* beta, float* S,
+                    int32_t B, int32_t H, int32_t dk, int32_t dv, float* o,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */
