@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D] [--no-cpu]
+
+A step is one kda_chunk_fwd over the T=8192, H=96, d=128 bf16 prefill
+(S0 = 0, final state returned); the headline value is prefill tokens/s
+(8192 tokens per step, all 96 heads).  The same run measures the decode
+step on B=256 requests x H=96 heads with a 1.6 GB fp32 state chained over
+D steps and reports the state GB/s (state read + write per step / step
+time).  Inputs are seeded synthetic data resident in HBM before the timed
+regions; timing uses HIP events on the stream the kernels run on.
+
+Prints one JSON line (rank 0) with the metric, a roofline object for the
+prefill kernel (and one for the decode kernel under "decode"), and the fp64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix
+PREFILL_BYTES_PER_TOKEN_HEAD = 1796      # q,k,v bf16 768 + log alpha 512 + beta 4 + o fp32 512
+PREFILL_FLOPS_PER_TOKEN_HEAD = 131072    # chunkwise algorithm, 64-token chunks, d = 128
+STATE_BYTES = 128 * 128 * 4
+DECODE_INPUT_BYTES_PER_STATE = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4   # q,k,v + log alpha + beta + o
+DECODE_FLOPS_PER_STATE = 7 * 128 * 128
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, profile_json):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    on the current kernel source (else None)."""
+    try:
+        with open(profile_json) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != src_hash(kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(every (sequence, head) chain is independent, so more GPUs "
+                                   "would shard heads with no communication -- not built here)"}))
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_amd as kda
+    from gated_delta_rule_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ prefill
+    w = W.workload(1)
+    a = W.prefill_inputs(w)
+    B, T, H = w.B, w.T, w.H
+    shp = (B, T, H, 128)
+    d = {n: torch.from_numpy(a[n]).to(dev, torch.bfloat16).view(shp) for n in ("q", "k", "v")}
+    d["log_alpha"] = torch.from_numpy(a["log_alpha"]).to(dev).view(shp)
+    d["beta"] = torch.from_numpy(a["beta"]).to(dev).view(B, T, H)
+    del a
+    o = torch.empty(shp, dtype=torch.float32, device=dev)
+    S_T = torch.empty((B, H, 128, 128), dtype=torch.float32, device=dev)
+
+    def prefill():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, None, o=o, S_T=S_T)
+
+    for _ in range(args.warmup):
+        prefill()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        prefill()
+        e_b.record(stream)
+        per.append((e_a, e_b))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = ev0.elapsed_time(ev1)
+    launch_ms = [x.elapsed_time(y) for x, y in per]
+    pf_ms = total_ms / args.steps
+    pf_kernel_ms = float(np.mean(launch_ms))
+    tokens_per_s = B * T / (pf_ms * 1e-3)
+    pf_bytes = B * T * H * PREFILL_BYTES_PER_TOKEN_HEAD + B * H * STATE_BYTES
+    pf_flops = B * T * H * PREFILL_FLOPS_PER_TOKEN_HEAD
+    pf_gbps = pf_bytes / (pf_kernel_ms * 1e-3) / 1e9
+    pf_tflops = pf_flops / (pf_kernel_ms * 1e-3) / 1e12
+    traffic = measured_traffic(os.path.join(ROOT, "gated_delta_rule_amd", "csrc", "kda_prefill.hip"),
+                               os.path.join(ROOT, "profiles", "chunk_fwd_workload1_traffic.json"))
+    del d, o, S_T
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- decode
+    wd = W.workload(4)
+    Bd, Hd = wd.B, wd.H
+    S = torch.from_numpy(W.decode_state(wd)).to(dev)
+    steps_d = max(1, args.decode_steps)
+    ins = []
+    for s in range(steps_d):
+        x = W.decode_inputs(wd, s)
+        e = {n: torch.from_numpy(x[n]).to(dev, torch.bfloat16) for n in ("q", "k", "v")}
+        e["log_alpha"] = torch.from_numpy(x["log_alpha"]).to(dev)
+        e["beta"] = torch.from_numpy(x["beta"]).to(dev)
+        ins.append(e)
+    od = torch.empty((Bd, Hd, 128), dtype=torch.float32, device=dev)
+
+    def dstep(e):
+        kda.decode_step(e["q"], e["k"], e["v"], e["log_alpha"], e["beta"], S, o=od)
+
+    for i in range(min(args.warmup, steps_d)):
+        dstep(ins[i])
+    torch.cuda.synchronize()
+    per_d = []
+    ev0.record(stream)
+    for e in ins:
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        dstep(e)
+        e_b.record(stream)
+        per_d.append((e_a, e_b))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_total_ms = ev0.elapsed_time(ev1)
+    dec_ms = dec_total_ms / steps_d
+    dec_kernel_ms = float(np.mean([x.elapsed_time(y) for x, y in per_d]))
+    n_states = Bd * Hd
+    state_gbps = 2 * n_states * STATE_BYTES / (dec_kernel_ms * 1e-3) / 1e9
+    dec_bytes = n_states * (2 * STATE_BYTES + DECODE_INPUT_BYTES_PER_STATE)
+    dec_gbps_all = dec_bytes / (dec_kernel_ms * 1e-3) / 1e9
+    dec_traffic = measured_traffic(os.path.join(ROOT, "gated_delta_rule_amd", "csrc", "kda_decode.hip"),
+                                   os.path.join(ROOT, "profiles", "decode_step_workload4_traffic.json"))
+    del S, ins
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        threads = oracle.max_threads()
+        # calibrate on a few heads, then run a sample sized to --cpu-seconds
+        cal_heads = max(1, min(H, threads))
+        a = W.prefill_inputs(w, heads=list(range(cal_heads)))
+        t0 = time.perf_counter()
+        oracle.forward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], None, a["cu_seqlens"])
+        t_cal = time.perf_counter() - t0
+        n_heads = int(min(H, max(cal_heads, cal_heads * args.cpu_seconds / max(t_cal, 1e-3))))
+        n_heads = max(cal_heads, (n_heads // threads) * threads) if n_heads >= threads else n_heads
+        if n_heads > cal_heads:
+            a = W.prefill_inputs(w, heads=list(range(n_heads)))
+            t0 = time.perf_counter()
+            oracle.forward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], None, a["cu_seqlens"])
+            t_cpu = time.perf_counter() - t0
+        else:
+            t_cpu = t_cal
+        cpu = {"value": T * (n_heads / H) / t_cpu, "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"fp64 token-by-token recurrence (C, OpenMP over heads) on {n_heads} of "
+                         f"{H} heads x {T} tokens of the same workload, {t_cpu:.1f} s wall; "
+                         f"tokens/s counts a token once across all {H} heads; "
+                         f"{cores} cores in the affinity mask"}
+
+    out = {
+        "metric": "KDA prefill tokens/s (H=96,d=128,T=8K) + decode-step state GB/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
+                "log_alpha=-5*sigmoid(N(0,1)), beta=sigmoid(N(0,1)))",
+        "config": {"workload": "KDA prefill B=1 T=8192 H=96 d=128, bf16 q/k/v, fp32 gates, "
+                               "S0=0, fp32 o and final state",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": 128},
+        "roofline": {"bound": "hbm", "achieved": pf_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": pf_gbps / PEAK_HBM_GBPS, "traffic": traffic,
+                     "kernel": "chunk_fwd_kernel", "kernel_ms": pf_kernel_ms,
+                     "algorithmic_bytes": pf_bytes, "algorithmic_flops": pf_flops,
+                     "mfma_tflops_algorithmic": pf_tflops,
+                     "mfma_frac_algorithmic": pf_tflops / PEAK_BF16_TFLOPS},
+        "decode": {
+            "metric": "decode-step state GB/s", "value": state_gbps, "unit": "GB/s",
+            "ms_per_step": dec_ms, "steps": steps_d,
+            "config": {"workload": "KDA decode B=256 H=96 d=128, bf16 q/k/v, fp32 gates, "
+                                   "fp32 state [256,96,128,128] ~N(0,0.02^2), chained steps"},
+            "roofline": {"bound": "hbm", "achieved": dec_gbps_all, "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": dec_gbps_all / PEAK_HBM_GBPS,
+                         "traffic": dec_traffic, "kernel": "decode_step_kernel",
+                         "kernel_ms": dec_kernel_ms, "algorithmic_bytes": dec_bytes,
+                         "algorithmic_flops": n_states * DECODE_FLOPS_PER_STATE},
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed_prefill": t_wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
