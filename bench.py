@@ -45,8 +45,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target CPU time of the oracle sample")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one path only (for profiler runs); prints no JSON line")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the repeated oracle runs")
     return ap.parse_args()
 
 
@@ -68,6 +70,20 @@ def measured_traffic(kernel_file, profile_json):
     return rec.get("hbm_bytes_per_launch")
 
 
+def run_decode_only(args, torch, kda, W, dev):
+    wd = W.workload(4)
+    S = torch.from_numpy(W.decode_state(wd)).to(dev)
+    x = W.decode_inputs(wd, 0)
+    e = {n: torch.from_numpy(x[n]).to(dev, torch.bfloat16) for n in ("q", "k", "v")}
+    e["log_alpha"] = torch.from_numpy(x["log_alpha"]).to(dev)
+    e["beta"] = torch.from_numpy(x["beta"]).to(dev)
+    od = torch.empty((wd.B, wd.H, 128), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup + args.steps):
+        kda.decode_step(e["q"], e["k"], e["v"], e["log_alpha"], e["beta"], S, o=od)
+    torch.cuda.synchronize()
+    print(f"decode only: {args.warmup + args.steps} launches", flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -86,6 +102,9 @@ def main():
 
     # ------------------------------------------------------------ prefill
     w = W.workload(1)
+    if args.only == "decode":
+        run_decode_only(args, torch, kda, W, dev)
+        return
     a = W.prefill_inputs(w)
     B, T, H = w.B, w.T, w.H
     shp = (B, T, H, 128)
@@ -129,6 +148,9 @@ def main():
                                os.path.join(ROOT, "profiles", "chunk_fwd_workload1_traffic.json"))
     del d, o, S_T
     torch.cuda.empty_cache()
+    if args.only == "prefill":
+        print(f"prefill only: {pf_kernel_ms:.4f} ms per launch, {tokens_per_s:.4g} tokens/s", flush=True)
+        return
 
     # ------------------------------------------------------------- decode
     wd = W.workload(4)
@@ -178,25 +200,20 @@ def main():
         import oracle
         cores = len(os.sched_getaffinity(0))
         threads = oracle.max_threads()
-        # calibrate on a few heads, then run a sample sized to --cpu-seconds
-        cal_heads = max(1, min(H, threads))
-        a = W.prefill_inputs(w, heads=list(range(cal_heads)))
-        t0 = time.perf_counter()
-        oracle.forward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], None, a["cu_seqlens"])
-        t_cal = time.perf_counter() - t0
-        n_heads = int(min(H, max(cal_heads, cal_heads * args.cpu_seconds / max(t_cal, 1e-3))))
-        n_heads = max(cal_heads, (n_heads // threads) * threads) if n_heads >= threads else n_heads
-        if n_heads > cal_heads:
-            a = W.prefill_inputs(w, heads=list(range(n_heads)))
+        # the whole workload's heads, repeated until --cpu-seconds of wall time
+        a = W.prefill_inputs(w)
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and reps < 50:
             t0 = time.perf_counter()
             oracle.forward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], None, a["cu_seqlens"])
-            t_cpu = time.perf_counter() - t0
-        else:
-            t_cpu = t_cal
+            t_cpu += time.perf_counter() - t0
+            reps += 1
+        n_heads = H
+        t_cpu /= reps
         cpu = {"value": T * (n_heads / H) / t_cpu, "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"fp64 token-by-token recurrence (C, OpenMP over heads) on {n_heads} of "
-                         f"{H} heads x {T} tokens of the same workload, {t_cpu:.1f} s wall; "
+               "sample": f"fp64 token-by-token recurrence (C, OpenMP over heads) on all {n_heads} "
+                         f"heads x {T} tokens of the same workload, {reps} runs, {t_cpu:.2f} s wall each; "
                          f"tokens/s counts a token once across all {H} heads; "
                          f"{cores} cores in the affinity mask"}
 

@@ -13,22 +13,36 @@
 //     walks the sequence's chunks serially.  The recurrence acts on S from
 //     the left, so value columns evolve independently: each wave owns
 //     WCOLS columns of the 128 x 128 fp32 state and keeps them in MFMA
-//     accumulator registers for the whole sequence; S never leaves the CU
-//     until the final state is written.
-//   * C = 32 tokens per chunk, split into two 16-token sub-tiles.  Every
-//     e^{g_t - g_j} product is evaluated as (x e^{g_t - r}) (k e^{r - g_j})
-//     with r the cumulative decay at a sub-tile boundary, so with
-//     log alpha >= -5 ("Kimi K3 技术报告解读" section 3.5: a 16-token tile
-//     stays within (-80, 0)) every factor lies in [e^-80, e^80]: no
-//     overflow, and an underflowing factor multiplies one that is <= 1.
-//   * Precision (bf16 inputs): products that can dominate an output use
-//     split bf16 operands (hi + lo, 16 significant bits): the L / M tiles,
-//     R, U, M and K_end.  K+, Q+, S and the diagonal blocks of T are
-//     rounded once.  fp32 inputs use exact fp32 MFMA (16x16x4) throughout.
-//   * Chunk-local tiles go through LDS twice-buffered so the next chunk's
-//     decay scan never waits for the previous chunk's readers; two
-//     workgroup barriers per chunk.  The next chunk's inputs are loaded
-//     into registers while the current chunk computes.
+//     accumulator registers for the whole sequence.
+//   * C = 32 tokens per chunk.  Every decay product is factored about the
+//     cumulative decay E0 at the end of the chunk's first 16 tokens:
+//         X = k e^{g - E0},  QX = q e^{g - E0},  Y = k e^{E0 - g},
+//     so k+_t . k-_j = X_t . Y_j for all j <= t in the chunk.  With
+//     log alpha >= -5 ("Kimi K3 技术报告解读" section 3.5: 16 tokens stay
+//     within (-80, 0)) every factor lies in [e^-80, e^80] and each product
+//     with j <= t is <= 1: no overflow, and an underflowing factor only
+//     ever multiplies one that is <= 1.  The chunk-level operands follow
+//     by per-channel scalings of the state instead of more tiles:
+//         K+ S = X (e^{E0} S),  Q+ S = QX (e^{E0} S),
+//         S_next = e^{E1 - E0} (e^{E0} S + Y^T U)   (E1 = g_C).
+//   * The decay scan and the operand tiles are produced once per chunk by
+//     all 256 threads (two key channels and 8 tokens each; the two halves
+//     of a 16-token sub-tile exchange partial sums across the wave) directly
+//     in the MFMA operand layouts (token-major rows for the products over
+//     channels, channel-major rows of Y for the product over tokens), so
+//     the matrix loops only load and issue.  Inputs arrive through buffer
+//     loads whose range ends at the sequence's last token (out-of-range
+//     rows read as zero, no branches).
+//   * bf16 inputs: X (for L and K+ S), QX (for Q+ S) and T are rounded
+//     once; QX and Y are split into hi + lo bf16 pairs for
+//     M = Tril(QX Y^T) (whose near-diagonal entries dominate o), and the
+//     state (in K+ S, Q+ S), V - K+S, U, M and Y^T (state update) are split
+//     as well.  fp32 inputs
+//     use fp32 MFMA (16x16x4) everywhere with fp32 tiles.
+//   * Two workgroup barriers per chunk.  The state-dependent chain of
+//     chunk c and the decay scan of chunk c+1 share a barrier interval, so
+//     each wave interleaves matrix-core and vector work.  Inputs are
+//     prefetched into registers one chunk ahead.
 //   * Grid: blockIdx -> (unit, slice) so that the slices of one head land
 //     on the same XCD (blockIdx % 8) and share its L2; units are taken
 //     longest sequence first when a sorted order is supplied.
@@ -39,35 +53,134 @@
 
 namespace kda {
 
-constexpr int CH = 32;        // chunk length (tokens)
-constexpr int DK = 128;       // key / value head dimension
-constexpr int LDT = DK + 4;   // LDS row stride of token-major [CH][DK] tiles (floats)
-constexpr int LDM = CH + 4;   // LDS row stride of [CH][CH] tiles (floats)
+constexpr int CH = 32;          // chunk length (tokens)
+constexpr int DK = 128;         // key / value head dimension
+constexpr int LDM = CH + 4;     // row stride of fp32 [CH][CH] tiles
 constexpr int PF_THREADS = 256;
+constexpr float LOG2E = 1.4426950408889634f;
 
+template <bool F32>
+struct Tiles {
+    typedef typename std::conditional<F32, float, __bf16>::type Op;   // operand element
+    static constexpr int LDR = F32 ? DK + 4 : DK + 8;     // token-major row stride
+    static constexpr int LDY = F32 ? CH + 4 : CH + 8;     // channel-major row stride
+};
+
+// 8 operand values for one lane from a row of operand-type LDS data.
+// contiguous: p[0..7];  tile order: p[0..3] and p[16..19].
+template <bool F32>
+struct Frag {
+    typename std::conditional<F32, float[8], bf16x8>::type v;
+};
+
+__device__ __forceinline__ void load_contig(Frag<false>& f, const __bf16* p) {
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void load_tile(Frag<false>& f, const __bf16* p) {
+    bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+    bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+    f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void load_contig(Frag<true>& f, const float* p) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void load_tile(Frag<true>& f, const float* p) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 16);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// acc += A * B for one 16 x 16 x 32 slab.
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<false>& a, const Frag<false>& b) {
+    acc = mfma32(a.v, b.v, acc);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<true>& a, const Frag<true>& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = mfma4f(a.v[e], b.v[e], acc);
+}
 
 template <typename InT>
-struct PairOf;
-template <>
-struct PairOf<__bf16> {
-    typedef uint32_t type;  // two packed bf16
-};
-template <>
-struct PairOf<float> {
-    typedef float2 type;
-};
+__device__ __forceinline__ float in_f32(InT x) {
+    return to_f32(x);
+}
 
-__device__ __forceinline__ float2 unpack2(uint32_t u) {
+// Raw buffer resource over `bytes` bytes from `base`: loads at offsets
+// beyond the range return 0, which masks the tokens past a sequence's end
+// without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ float2 bf2_to_f2(uint32_t u) {
     return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
 }
-__device__ __forceinline__ float2 unpack2(float2 f) { return f; }
+__device__ __forceinline__ uint32_t f2_to_bf2(float a, float b) {
+    bf16x2_t r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Pack the low (sel = 0x05040100) or high (0x07060302) bf16 halves of two
+// dwords into one dword: result = {b.half, a.half}.
+__device__ __forceinline__ uint32_t perm2(uint32_t a, uint32_t b, uint32_t sel) {
+    return __builtin_amdgcn_perm(a, b, sel);
+}
+constexpr uint32_t LO_HALVES = 0x05040100u, HI_HALVES = 0x07060302u;
+
+// Broadcast lane qc of every quad (4 consecutive lanes) to the whole quad.
+__device__ __forceinline__ float quad_bcast(float x, int qc) {
+    const int v = __float_as_int(x);
+    switch (qc) {
+        case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false));
+        case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false));
+        case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xaa, 0xf, 0xf, false));
+        default: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xff, 0xf, 0xf, false));
+    }
+}
+
+// (I + L)^{-1} of a 16 x 16 strictly lower-triangular L (LDS, row stride
+// LDM, upper part stored as zeros) by forward substitution on one wave:
+// lane 4j + q owns rows q, q+4, q+8, q+12 of column j; at step c the owner
+// of x_c broadcasts it to its quad with a DPP quad permute.  The result is
+// written to T (same layout).
+__device__ __forceinline__ void invert16(const float* L, float* T, int lane) {
+    const int j = lane >> 2, q = lane & 3;
+    float Lr[4][16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int c4 = 0; c4 < 16; c4 += 4) {
+            const float4 t4 = *reinterpret_cast<const float4*>(L + (q + 4 * k) * LDM + c4);
+            Lr[k][c4] = t4.x; Lr[k][c4 + 1] = t4.y; Lr[k][c4 + 2] = t4.z; Lr[k][c4 + 3] = t4.w;
+        }
+    float x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (q + 4 * k == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int c = 0; c < 15; ++c) {
+        const float xc = quad_bcast(x[c >> 2], c & 3);
+        // L[i][c] is zero for i <= c, so rows at or above c are unchanged.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] -= Lr[k][c] * xc;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) T[(q + 4 * k) * LDM + j] = x[k];
+}
 
 template <typename InT, int WCOLS>
 __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) {
     constexpr bool F32 = std::is_same<InT, float>::value;
     constexpr int NCT = WCOLS / 16;   // 16-column tiles per wave
     constexpr int DVW = 4 * WCOLS;    // value columns per workgroup
-    typedef typename PairOf<InT>::type Pair;
+    constexpr int ES = (int)sizeof(InT);
+    typedef Tiles<F32> TL;
+    typedef typename TL::Op Op;
+    constexpr int LDR = TL::LDR, LDY = TL::LDY;
 
     // ---------------------------------------------------------------- work item
     const int blk = blockIdx.x;
@@ -89,10 +202,9 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
         t0 = (int64_t)n * Tt;
         t1 = t0 + Tt;
     }
+    const int64_t nch = (t1 - t0 + CH - 1) / CH;
     const int H = p.H;
-    const InT* __restrict__ qg = (const InT*)p.q;
-    const InT* __restrict__ kg = (const InT*)p.k;
-    const InT* __restrict__ vg = (const InT*)p.v;
+    const int rowel = H * DK;   // elements between consecutive tokens
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -101,18 +213,22 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     const int ln = lane & 15;    // row / column within a 16-wide tile
     const int col0 = slice * DVW + wave * WCOLS;   // first value column of this wave
 
-    __shared__ __attribute__((aligned(16))) float sKs[2][CH * LDT];  // k e^{g - r_start}
-    __shared__ __attribute__((aligned(16))) float sQs[2][CH * LDT];  // q e^{g - r_start}
-    __shared__ __attribute__((aligned(16))) float sKh[2][CH * LDT];  // k e^{r_end - g}
-    // per channel: 0: e^{D0}, 1: e^{-D0}, 2: e^{D1}, 3: e^{-D1} where
-    // D_b >= 0 is the decay magnitude accumulated over sub-tile b.
-    __shared__ __attribute__((aligned(16))) float sVec[2][4][DK];
-    __shared__ __attribute__((aligned(16))) float sL[CH * LDM];
-    __shared__ __attribute__((aligned(16))) float sT[CH * LDM];
-    __shared__ __attribute__((aligned(16))) float sM[CH * LDM];
+    // ------------------------------------------------------------------ LDS
+    __shared__ __attribute__((aligned(16))) Op sX[CH * LDR];     // k e^{g - E0}
+    __shared__ __attribute__((aligned(16))) Op sQX[CH * LDR];    // q e^{g - E0} (hi)
+    __shared__ __attribute__((aligned(16))) Op sY[CH * LDR];     // k e^{E0 - g} (hi)
+    __shared__ __attribute__((aligned(16))) Op sQXl[F32 ? 4 : CH * LDR];   // lo parts
+    __shared__ __attribute__((aligned(16))) Op sYl[F32 ? 4 : CH * LDR];
+    __shared__ __attribute__((aligned(16))) Op sYt[2][DK * LDY];               // Y^T hi
+    __shared__ __attribute__((aligned(16))) Op sYtl[2][F32 ? 4 : DK * LDY];    // Y^T lo
+    __shared__ __attribute__((aligned(16))) float sVec[2][2][DK];  // e^{E0}, e^{E1 - E0}
+    __shared__ __attribute__((aligned(16))) float sL[CH * LDM];    // beta-scaled L blocks 00, 11
+    __shared__ __attribute__((aligned(16))) float sT[CH * LDM];    // T00, T11 and W = -T11 L10
+    // M = Tril(Q+ K-^T): bf16 path as packed (hi | lo << 16) pairs, fp32 path as floats.
+    __shared__ __attribute__((aligned(16))) uint32_t sM[CH * LDM];
 
     // M's upper-right 16 x 16 block is identically zero; never rewritten.
-    sM[(tid >> 4) * LDM + 16 + (tid & 15)] = 0.f;
+    sM[(tid >> 4) * LDM + 16 + (tid & 15)] = 0u;
 
     // ------------------------------------------------------------ state in
     f32x4 S[8][NCT];
@@ -127,170 +243,275 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                                            ct * 16 + ln]
                                     : 0.f;
 
-    // -------------------------------------------------------- input loaders
-    // Decay-scan role of this thread: wave>>1 selects k (0) or q (1),
-    // wave&1 the sub-tile, lane the channel pair (2 lane, 2 lane + 1).
-    const int kind = wave >> 1;
-    const int sb = wave & 1;
-    const InT* __restrict__ xg = kind ? qg : kg;
-    Pair px[16];
-    float2 pla[16];
-    auto load_scan = [&](int64_t c0) {
+    // --------------------------------------------------------- input loaders
+    // Valid tokens of the chunk starting at token c, and the bytes of a
+    // tensor's rows of head h from token c through the last valid one.
+    auto n_valid = [&](int64_t c) -> int {
+        const int64_t nv = t1 - c;
+        return nv <= 0 ? 0 : (nv < CH ? (int)nv : CH);
+    };
+    auto span_bytes = [&](int nv, int es) -> int {
+        return nv <= 0 ? 0 : ((nv - 1) * rowel + DK) * es;
+    };
+    // Scan role: sub-tile sb, channel pair (2 cp, 2 cp + 1), half hf of the
+    // sub-tile (tokens 16 sb + 8 hf + tau, tau < 8).
+    const int sb = wave >> 1;
+    const int cp = (wave & 1) * 32 + (lane & 31);
+    const int hf = lane >> 5;
+    const int sc = 2 * cp;
+    typedef typename std::conditional<F32, float2, uint32_t>::type Pair;
+    Pair xk[8], xq[8];
+    float2 xl[8];
+    auto load_scan = [&](int64_t cidx) {
+        const int64_t c = t0 + cidx * CH;
+        const int nv = n_valid(c);
+        const size_t eoff = ((size_t)c * H + h) * DK;
+        const auto rk = make_rsrc((const InT*)p.k + eoff, span_bytes(nv, ES));
+        const auto rq = make_rsrc((const InT*)p.q + eoff, span_bytes(nv, ES));
+        const auto rl = make_rsrc(p.la + eoff, span_bytes(nv, 4));
 #pragma unroll
-        for (int tau = 0; tau < 16; ++tau) {
-            const int64_t tok = c0 + sb * 16 + tau;
-            if (tok < t1) {
-                const size_t off = ((size_t)tok * H + h) * DK + 2 * lane;
-                px[tau] = *reinterpret_cast<const Pair*>(xg + off);
-                pla[tau] = *reinterpret_cast<const float2*>(p.la + off);
+        for (int tau = 0; tau < 8; ++tau) {
+            const int el = (sb * 16 + hf * 8 + tau) * rowel + sc;
+            if constexpr (F32) {
+                auto a = __builtin_amdgcn_raw_buffer_load_b64(rk, el * 4, 0, 0);
+                auto b = __builtin_amdgcn_raw_buffer_load_b64(rq, el * 4, 0, 0);
+                xk[tau] = make_float2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+                xq[tau] = make_float2(__uint_as_float(b[0]), __uint_as_float(b[1]));
             } else {
-                px[tau] = Pair{};
-                pla[tau] = make_float2(0.f, 0.f);
+                xk[tau] = __builtin_amdgcn_raw_buffer_load_b32(rk, el * 2, 0, 0);
+                xq[tau] = __builtin_amdgcn_raw_buffer_load_b32(rq, el * 2, 0, 0);
             }
+            auto lv = __builtin_amdgcn_raw_buffer_load_b64(rl, el * 4, 0, 0);
+            xl[tau] = make_float2(__uint_as_float(lv[0]), __uint_as_float(lv[1]));
         }
     };
     // Values and beta in C layout for this wave's columns.
-    InT pv[2][NCT][4];
+    float pv[2][NCT][4];
     float pb[2][4];
-    auto load_vb = [&](int64_t c0) {
+    auto load_vb = [&](int64_t cidx, float (&v)[2][NCT][4], float (&b)[2][4]) {
+        const int64_t c = t0 + cidx * CH;
+        const int nv = n_valid(c);
+        const auto rv = make_rsrc((const InT*)p.v + ((size_t)c * H + h) * DK, span_bytes(nv, ES));
+        const auto rb = make_rsrc(p.beta + (size_t)c * H + h, nv <= 0 ? 0 : ((nv - 1) * H + 1) * 4);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t tok = c0 + tb * 16 + g * 4 + r;
-                const bool ok = tok < t1;
-                pb[tb][r] = ok ? p.beta[(size_t)tok * H + h] : 0.f;
+                const int row = tb * 16 + g * 4 + r;
+                b[tb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, row * H * 4, 0, 0));
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    pv[tb][ct][r] = ok ? vg[((size_t)tok * H + h) * DK + col0 + ct * 16 + ln]
-                                       : (InT)0.f;
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const int el = row * rowel + col0 + ct * 16 + ln;
+                    if constexpr (F32)
+                        v[tb][ct][r] = __uint_as_float(
+                            __builtin_amdgcn_raw_buffer_load_b32(rv, el * 4, 0, 0));
+                    else
+                        v[tb][ct][r] = __uint_as_float(
+                            (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, el * 2, 0, 0) << 16);
+                }
             }
     };
 
-    load_scan(t0);
-    load_vb(t0);
-
-    int buf = 0;
-    for (int64_t c0 = t0; c0 < t1; c0 += CH, buf ^= 1) {
-        const int nvalid = (int)((t1 - c0) < CH ? (t1 - c0) : CH);
-        float* Ks = sKs[buf];
-        float* Qs = sQs[buf];
-        float* Kh = sKh[buf];
-        float(*Vec)[DK] = sVec[buf];
-
-        // ------------------------------------------------ 1. decay scan
-        // s_tau = sum of log alpha over the sub-tile up to token tau;
-        // tile values x e^{s_tau} (<= 1) and, for k, k e^{s_15 - s_tau} (<= 1).
-        {
-            float cs0[16], cs1[16];
-            float a0 = 0.f, a1 = 0.f;
+    // ------------------------------------------------------------ decay scan
+    // Writes X, QX, Y (token-major, hi and lo where split), Y^T (channel-
+    // major, buffer `buf`) and the per-channel scalings of buffer `buf`.
+    auto scan = [&](int buf) {
+        float cs0[8], cs1[8];
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-            for (int tau = 0; tau < 16; ++tau) {
-                a0 += pla[tau].x;
-                a1 += pla[tau].y;
-                cs0[tau] = a0;
-                cs1[tau] = a1;
-            }
-            float* dst = kind ? Qs : Ks;
-#pragma unroll
-            for (int tau = 0; tau < 16; ++tau) {
-                const float2 x = unpack2(px[tau]);
-                const int row = sb * 16 + tau;
-                *reinterpret_cast<float2*>(dst + row * LDT + 2 * lane) =
-                    make_float2(x.x * expf(cs0[tau]), x.y * expf(cs1[tau]));
-                if (kind == 0)
-                    *reinterpret_cast<float2*>(Kh + row * LDT + 2 * lane) =
-                        make_float2(x.x * expf(a0 - cs0[tau]), x.y * expf(a1 - cs1[tau]));
-            }
-            if (kind == 0) {
-                *reinterpret_cast<float2*>(&Vec[2 * sb][2 * lane]) = make_float2(expf(-a0), expf(-a1));
-                *reinterpret_cast<float2*>(&Vec[2 * sb + 1][2 * lane]) = make_float2(expf(a0), expf(a1));
-            }
+        for (int tau = 0; tau < 8; ++tau) {
+            a0 += xl[tau].x * LOG2E;
+            a1 += xl[tau].y * LOG2E;
+            cs0[tau] = a0;
+            cs1[tau] = a1;
         }
-        if (c0 + CH < t1) load_scan(c0 + CH);   // next chunk's k/q/log alpha
-        __syncthreads();
-
-        // ------------------------------- 2. L and M tiles; K+ S and Q+ S
-        // Block (b, a) of a C x C tile: left rows of sub-tile b (x e^{g - r_start(b)},
-        // times e^{D_b} on the diagonal block so the reference is r_end(b) =
-        // r_end(a)), right rows k e^{r_end(a) - g} of sub-tile a.
-        auto block_mma = [&](const float* left, int lrow0, const float* scale, int rrow0) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // the two halves of the sub-tile live in lanes l and l ^ 32
+        const float o0 = __shfl_xor(a0, 32), o1 = __shfl_xor(a1, 32);
+        const float pre0 = hf ? o0 : 0.f, pre1 = hf ? o1 : 0.f;
+        const float tot0 = hf ? o0 + a0 : a0 + o0, tot1 = hf ? o1 + a1 : a1 + o1;
+        const float ref0 = sb == 0 ? tot0 : 0.f, ref1 = sb == 0 ? tot1 : 0.f;
+        if (hf == 0)
+            *reinterpret_cast<float2*>(&sVec[buf][sb][sc]) =
+                make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
+        const int tc = sb * 16 + hf * 8;
+        if constexpr (F32) {
+            float y0[8], y1[8];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int kk = ks * 32 + g * 8;
-                float a[8], b[8];
-                const float4* la4 = reinterpret_cast<const float4*>(left + (lrow0 + ln) * LDT + kk);
-                const float4* rb4 = reinterpret_cast<const float4*>(Kh + (rrow0 + ln) * LDT + kk);
-                float4 a0 = la4[0], a1 = la4[1], b0 = rb4[0], b1 = rb4[1];
-                a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
-                a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
-                b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
-                b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
-                if (scale) {
-                    const float4* s4 = reinterpret_cast<const float4*>(scale + kk);
-                    float4 s0 = s4[0], s1 = s4[1];
-                    a[0] *= s0.x; a[1] *= s0.y; a[2] *= s0.z; a[3] *= s0.w;
-                    a[4] *= s1.x; a[5] *= s1.y; a[6] *= s1.z; a[7] *= s1.w;
-                }
-                mma_k32<F32, SPLIT2>(acc, a, b);
+            for (int tau = 0; tau < 8; ++tau) {
+                const float d0 = cs0[tau] + pre0 - ref0, d1 = cs1[tau] + pre1 - ref1;
+                const float fx0 = __builtin_amdgcn_exp2f(d0), fx1 = __builtin_amdgcn_exp2f(d1);
+                const float fy0 = __builtin_amdgcn_exp2f(-d0), fy1 = __builtin_amdgcn_exp2f(-d1);
+                const float2 kf = xk[tau], qf = xq[tau];
+                const int row = tc + tau;
+                *reinterpret_cast<float2*>(&sX[row * LDR + sc]) = make_float2(kf.x * fx0, kf.y * fx1);
+                *reinterpret_cast<float2*>(&sQX[row * LDR + sc]) = make_float2(qf.x * fx0, qf.y * fx1);
+                y0[tau] = kf.x * fy0;
+                y1[tau] = kf.y * fy1;
+                *reinterpret_cast<float2*>(&sY[row * LDR + sc]) = make_float2(y0[tau], y1[tau]);
             }
-            return acc;
-        };
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                *reinterpret_cast<float4*>(&sYt[buf][sc * LDY + tc + 4 * i]) =
+                    make_float4(y0[4 * i], y0[4 * i + 1], y0[4 * i + 2], y0[4 * i + 3]);
+                *reinterpret_cast<float4*>(&sYt[buf][(sc + 1) * LDY + tc + 4 * i]) =
+                    make_float4(y1[4 * i], y1[4 * i + 1], y1[4 * i + 2], y1[4 * i + 3]);
+            }
+        } else {
+            uint32_t yh[8], yl[8];
+#pragma unroll
+            for (int tau = 0; tau < 8; ++tau) {
+                const float d0 = cs0[tau] + pre0 - ref0, d1 = cs1[tau] + pre1 - ref1;
+                const float fx0 = __builtin_amdgcn_exp2f(d0), fx1 = __builtin_amdgcn_exp2f(d1);
+                const float fy0 = __builtin_amdgcn_exp2f(-d0), fy1 = __builtin_amdgcn_exp2f(-d1);
+                const float2 kf = bf2_to_f2(xk[tau]), qf = bf2_to_f2(xq[tau]);
+                const float X0 = kf.x * fx0, X1 = kf.y * fx1;
+                const float Q0 = qf.x * fx0, Q1 = qf.y * fx1;
+                const float Y0 = kf.x * fy0, Y1 = kf.y * fy1;
+                const uint32_t qh = f2_to_bf2(Q0, Q1);
+                yh[tau] = f2_to_bf2(Y0, Y1);
+                const float2 qhf = bf2_to_f2(qh), yhf = bf2_to_f2(yh[tau]);
+                yl[tau] = f2_to_bf2(Y0 - yhf.x, Y1 - yhf.y);
+                const int row = tc + tau;
+                *reinterpret_cast<uint32_t*>(&sX[row * LDR + sc]) = f2_to_bf2(X0, X1);
+                *reinterpret_cast<uint32_t*>(&sQX[row * LDR + sc]) = qh;
+                *reinterpret_cast<uint32_t*>(&sQXl[row * LDR + sc]) = f2_to_bf2(Q0 - qhf.x, Q1 - qhf.y);
+                *reinterpret_cast<uint32_t*>(&sY[row * LDR + sc]) = yh[tau];
+                *reinterpret_cast<uint32_t*>(&sYl[row * LDR + sc]) = yl[tau];
+            }
+            // Y^T rows sc and sc + 1: regroup the channel pairs into runs of
+            // 8 tokens per channel.
+            uint4 h0, h1, l0, l1;
+            h0.x = perm2(yh[1], yh[0], LO_HALVES); h0.y = perm2(yh[3], yh[2], LO_HALVES);
+            h0.z = perm2(yh[5], yh[4], LO_HALVES); h0.w = perm2(yh[7], yh[6], LO_HALVES);
+            h1.x = perm2(yh[1], yh[0], HI_HALVES); h1.y = perm2(yh[3], yh[2], HI_HALVES);
+            h1.z = perm2(yh[5], yh[4], HI_HALVES); h1.w = perm2(yh[7], yh[6], HI_HALVES);
+            l0.x = perm2(yl[1], yl[0], LO_HALVES); l0.y = perm2(yl[3], yl[2], LO_HALVES);
+            l0.z = perm2(yl[5], yl[4], LO_HALVES); l0.w = perm2(yl[7], yl[6], LO_HALVES);
+            l1.x = perm2(yl[1], yl[0], HI_HALVES); l1.y = perm2(yl[3], yl[2], HI_HALVES);
+            l1.z = perm2(yl[5], yl[4], HI_HALVES); l1.w = perm2(yl[7], yl[6], HI_HALVES);
+            *reinterpret_cast<uint4*>(&sYt[buf][sc * LDY + tc]) = h0;
+            *reinterpret_cast<uint4*>(&sYt[buf][(sc + 1) * LDY + tc]) = h1;
+            *reinterpret_cast<uint4*>(&sYtl[buf][sc * LDY + tc]) = l0;
+            *reinterpret_cast<uint4*>(&sYtl[buf][(sc + 1) * LDY + tc]) = l1;
+        }
+    };
 
+    // 16 x 16 block of A B^T over the 128 channels (contiguous k order);
+    // with `split`: A B^T = Ah Bh^T + Ah Bl^T + Al Bh^T.
+    auto block = [&](const Op* A, const Op* Al, int arow0, const Op* B, const Op* Bl, int brow0,
+                     bool split) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ao = (arow0 + ln) * LDR + ks * 32 + g * 8;
+            const int bo = (brow0 + ln) * LDR + ks * 32 + g * 8;
+            Frag<F32> a, b;
+            load_contig(a, A + ao);
+            load_contig(b, B + bo);
+            if constexpr (!F32) {
+                if (split) {
+                    Frag<F32> al, bl;
+                    load_contig(al, Al + ao);
+                    load_contig(bl, Bl + bo);
+                    mma(acc, al, b);
+                    mma(acc, a, bl);
+                }
+            }
+            mma(acc, a, b);
+        }
+        return acc;
+    };
+    // Store an M block (C layout) at rows r0, columns c0, keeping j <= t if diag.
+    auto store_m = [&](const f32x4& m, int r0, int c0, bool diag) {
+        uint32_t w[4];
+        if constexpr (F32) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                w[r] = __float_as_uint((!diag || ln <= g * 4 + r) ? m[r] : 0.f);
+        } else {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (!diag || ln <= g * 4 + r) ? m[r] : 0.f;
+            const uint32_t h01 = f2_to_bf2(v[0], v[1]), h23 = f2_to_bf2(v[2], v[3]);
+            const float2 f01 = bf2_to_f2(h01), f23 = bf2_to_f2(h23);
+            const uint32_t l01 = f2_to_bf2(v[0] - f01.x, v[1] - f01.y);
+            const uint32_t l23 = f2_to_bf2(v[2] - f23.x, v[3] - f23.y);
+            w[0] = perm2(l01, h01, LO_HALVES);
+            w[1] = perm2(l01, h01, HI_HALVES);
+            w[2] = perm2(l23, h23, LO_HALVES);
+            w[3] = perm2(l23, h23, HI_HALVES);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sM[(r0 + g * 4 + r) * LDM + c0 + ln] = w[r];
+    };
+
+    // ------------------------------------------------------------- prologue
+    load_scan(0);
+    load_vb(0, pv, pb);
+    scan(0);
+    load_scan(1);
+    __syncthreads();
+
+    for (int64_t cidx = 0; cidx < nch; ++cidx) {
+        const int buf = (int)(cidx & 1);
+        const int64_t c0 = t0 + cidx * CH;
+        const int nvalid = n_valid(c0);
+
+        // ------------------------ L, M tiles, diagonal inverses and W
         if (wave == 0) {
-            // L00, L11 -> invert the two unit-lower-triangular diagonal blocks.
-            f32x4 l00 = block_mma(Ks, 0, Vec[0], 0);
-            f32x4 l11 = block_mma(Ks, 16, Vec[2], 16);
+            const f32x4 l00 = block(sX, sX, 0, sY, sY, 0, false);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = g * 4 + r;
                 sL[row * LDM + ln] = ln < row ? pb[0][r] * l00[r] : 0.f;
+            }
+            const f32x4 m00 = block(sQX, sQXl, 0, sY, sYl, 0, true);
+            wave_lds_sync();
+            invert16(sL, sT, lane);
+            store_m(m00, 0, 0, true);
+        } else if (wave == 1) {
+            const f32x4 l11 = block(sX, sX, 16, sY, sY, 16, false);
+            f32x4 l10 = block(sX, sX, 16, sY, sY, 0, false);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = g * 4 + r;
                 sL[(16 + row) * LDM + 16 + ln] = ln < row ? pb[1][r] * l11[r] : 0.f;
+                l10[r] *= pb[1][r];
             }
             wave_lds_sync();
-            if (lane < 32) {
-                // Column j of (I + L_bb)^{-1} by forward substitution.
-                const int bb = lane >> 4, j = lane & 15;
-                const float* Lb = sL + (16 * bb) * LDM + 16 * bb;
-                float x[16];
+            invert16(sL + 16 * LDM + 16, sT + 16 * LDM + 16, lane);
+            wave_lds_sync();
+            // W = -T11 L10 (fp32 matrix cores; L10 is already in B layout)
+            f32x4 wacc = {0.f, 0.f, 0.f, 0.f};
+            const float4 t4 = *reinterpret_cast<const float4*>(sT + (16 + ln) * LDM + 16 + g * 4);
+            wacc = mfma4f(t4.x, l10[0], wacc);
+            wacc = mfma4f(t4.y, l10[1], wacc);
+            wacc = mfma4f(t4.z, l10[2], wacc);
+            wacc = mfma4f(t4.w, l10[3], wacc);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
-#pragma unroll
-                for (int c = 0; c < 15; ++c) {
-                    const float xc = x[c];
-#pragma unroll
-                    for (int i = c + 1; i < 16; ++i) x[i] -= Lb[i * LDM + c] * xc;
-                }
-                float* Tb = sT + (16 * bb) * LDM + 16 * bb;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) Tb[i * LDM + j] = x[i];
-            }
-        } else if (wave == 1) {
-            f32x4 l10 = block_mma(Ks, 16, nullptr, 0);
-            f32x4 m00 = block_mma(Qs, 0, Vec[0], 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = g * 4 + r;
-                sL[(16 + row) * LDM + ln] = pb[1][r] * l10[r];
-                sM[row * LDM + ln] = ln <= row ? m00[r] : 0.f;
-            }
+            for (int r = 0; r < 4; ++r) sT[(16 + g * 4 + r) * LDM + ln] = -wacc[r];
         } else if (wave == 2) {
-            f32x4 m10 = block_mma(Qs, 16, nullptr, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sM[(16 + g * 4 + r) * LDM + ln] = m10[r];
+            store_m(block(sQX, sQXl, 16, sY, sYl, 0, true), 16, 0, false);
         } else {
-            f32x4 m11 = block_mma(Qs, 16, Vec[2], 16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = g * 4 + r;
-                sM[(16 + row) * LDM + 16 + ln] = ln <= row ? m11[r] : 0.f;
-            }
+            store_m(block(sQX, sQXl, 16, sY, sYl, 16, true), 16, 16, true);
         }
 
-        // K+ S -> R and Q+ S -> O for this wave's columns (state at chunk start).
-        // k+ of sub-tile 1 = (k e^{g - r_end(0)}) e^{-D0}.
+        // -------------------- K+ S -> R and Q+ S -> O with S~ = e^{E0} S
         f32x4 R[2][NCT], O[2][NCT];
+        {
+            const float* e0 = sVec[buf][0];
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const float4 sc4 = *reinterpret_cast<const float4*>(e0 + it * 16 + g * 4);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    S[it][ct][0] *= sc4.x;
+                    S[it][ct][1] *= sc4.y;
+                    S[it][ct][2] *= sc4.z;
+                    S[it][ct][3] *= sc4.w;
+                }
+            }
+        }
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -300,47 +521,47 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
             }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            Frag8 bS[NCT];
+            Frag<F32> bS[NCT], bSl[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
+                float f[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    bS[ct].f[r] = S[2 * ks][ct][r];
-                    bS[ct].f[4 + r] = S[2 * ks + 1][ct][r];
+                    f[r] = S[2 * ks][ct][r];
+                    f[4 + r] = S[2 * ks + 1][ct][r];
                 }
-                prep8<F32, PLAIN>(bS[ct]);
+                if constexpr (F32) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bS[ct].v[e] = f[e];
+                } else {
+                    SplitBF<8> s8 = split8(f);
+                    bS[ct].v = s8.hi;
+                    bSl[ct].v = s8.lo;
+                }
             }
-            const int k0 = ks * 32 + g * 4;
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-                Frag8 aK, aQ;
-                const float* kr = Ks + (tb * 16 + ln) * LDT;
-                const float* qr = Qs + (tb * 16 + ln) * LDT;
-                float4 k0v = *reinterpret_cast<const float4*>(kr + k0);
-                float4 k1v = *reinterpret_cast<const float4*>(kr + k0 + 16);
-                float4 q0v = *reinterpret_cast<const float4*>(qr + k0);
-                float4 q1v = *reinterpret_cast<const float4*>(qr + k0 + 16);
-                float4 s0v = make_float4(1.f, 1.f, 1.f, 1.f), s1v = s0v;
-                if (tb == 1) {
-                    s0v = *reinterpret_cast<const float4*>(&Vec[1][k0]);
-                    s1v = *reinterpret_cast<const float4*>(&Vec[1][k0 + 16]);
-                }
-                aK.f[0] = k0v.x * s0v.x; aK.f[1] = k0v.y * s0v.y; aK.f[2] = k0v.z * s0v.z; aK.f[3] = k0v.w * s0v.w;
-                aK.f[4] = k1v.x * s1v.x; aK.f[5] = k1v.y * s1v.y; aK.f[6] = k1v.z * s1v.z; aK.f[7] = k1v.w * s1v.w;
-                aQ.f[0] = q0v.x * s0v.x; aQ.f[1] = q0v.y * s0v.y; aQ.f[2] = q0v.z * s0v.z; aQ.f[3] = q0v.w * s0v.w;
-                aQ.f[4] = q1v.x * s1v.x; aQ.f[5] = q1v.y * s1v.y; aQ.f[6] = q1v.z * s1v.z; aQ.f[7] = q1v.w * s1v.w;
-                prep8<F32, PLAIN>(aK);
-                prep8<F32, PLAIN>(aQ);
+                Frag<F32> aK, aQ;
+                load_tile(aK, sX + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
+                load_tile(aQ, sQX + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
-                    mma_k32<F32, PLAIN>(R[tb][ct], aK, bS[ct]);
-                    mma_k32<F32, PLAIN>(O[tb][ct], aQ, bS[ct]);
+                    if constexpr (!F32) {
+                        mma(R[tb][ct], aK, bSl[ct]);
+                        mma(O[tb][ct], aQ, bSl[ct]);
+                    }
+                    mma(R[tb][ct], aK, bS[ct]);
+                    mma(O[tb][ct], aQ, bS[ct]);
                 }
             }
         }
         __syncthreads();
 
-        // --------------------------------------- 3. U, O and the state update
+        // ----------------------------- U, O, the state update; next scan
+        float nv[2][NCT][4];
+        float nb[2][4];
+        load_vb(cidx + 1, nv, nb);
+
         // R' = B_beta (V - K+ S)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -348,99 +569,135 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    R[tb][ct][r] = pb[tb][r] * (to_f32(pv[tb][ct][r]) - R[tb][ct][r]);
+                    R[tb][ct][r] = pb[tb][r] * (pv[tb][ct][r] - R[tb][ct][r]);
 
-        // Block forward substitution with the diagonal inverses:
-        // U0 = T00 R'0 ; U1 = T11 (R'1 - L10 U0).
+        // U0 = T00 R'0 ; U1 = T11 R'1 + W U0   (W = -T11 L10)
         f32x4 U0[NCT], U1[NCT];
         {
-            float t00[4], nl10[4], t11[4];
+            float t00[4], t11[4], wm[4];
             float4 a = *reinterpret_cast<const float4*>(sT + ln * LDM + g * 4);
             t00[0] = a.x; t00[1] = a.y; t00[2] = a.z; t00[3] = a.w;
-            a = *reinterpret_cast<const float4*>(sL + (16 + ln) * LDM + g * 4);
-            nl10[0] = -a.x; nl10[1] = -a.y; nl10[2] = -a.z; nl10[3] = -a.w;
             a = *reinterpret_cast<const float4*>(sT + (16 + ln) * LDM + 16 + g * 4);
             t11[0] = a.x; t11[1] = a.y; t11[2] = a.z; t11[3] = a.w;
+            a = *reinterpret_cast<const float4*>(sT + (16 + ln) * LDM + g * 4);
+            wm[0] = a.x; wm[1] = a.y; wm[2] = a.z; wm[3] = a.w;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 float b[4];
                 U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) b[r] = R[0][ct][r];
                 mma_k16<F32, SPLITB>(U0[ct], t00, b);
-                f32x4 X = R[1][ct];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) b[r] = R[1][ct][r];
+                mma_k16<F32, SPLITB>(U1[ct], t11, b);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) b[r] = U0[ct][r];
-                mma_k16<F32, SPLITB>(X, nl10, b);
-                U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) b[r] = X[r];
-                mma_k16<F32, SPLITB>(U1[ct], t11, b);
+                mma_k16<F32, SPLITB>(U1[ct], wm, b);
             }
         }
 
-        // U as the B operand of M U and K_end^T U (tile order: U0 rows then U1 rows).
-        Frag8 bU[NCT];
+        // U as the B operand of M U and Y^T U (tile order: U0 rows, U1 rows).
+        Frag<F32> bUh[NCT], bUl[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
+            float f[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                bU[ct].f[r] = U0[ct][r];
-                bU[ct].f[4 + r] = U1[ct][r];
+                f[r] = U0[ct][r];
+                f[4 + r] = U1[ct][r];
             }
-            prep8<F32, SPLIT2>(bU[ct]);
+            if constexpr (F32) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bUh[ct].v[e] = f[e];
+            } else {
+                SplitBF<8> s8 = split8(f);
+                bUh[ct].v = s8.hi;
+                bUl[ct].v = s8.lo;
+            }
         }
 
-        // O = Q+ S + M U, written for the valid rows.
+        // O = Q+ S + M U; rows past the sequence end fall outside the store range.
+        {
+            const auto ro = make_rsrc(p.o + ((size_t)c0 * H + h) * DK, span_bytes(nvalid, 4));
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            Frag8 aM;
-            const float* mr = sM + (tb * 16 + ln) * LDM + g * 4;
-            float4 m0 = *reinterpret_cast<const float4*>(mr);
-            float4 m1 = *reinterpret_cast<const float4*>(mr + 16);
-            aM.f[0] = m0.x; aM.f[1] = m0.y; aM.f[2] = m0.z; aM.f[3] = m0.w;
-            aM.f[4] = m1.x; aM.f[5] = m1.y; aM.f[6] = m1.z; aM.f[7] = m1.w;
-            prep8<F32, SPLIT2>(aM);
+            for (int tb = 0; tb < 2; ++tb) {
+                Frag<F32> aM, aMl;
+                {
+                    const uint32_t* mr = sM + (tb * 16 + ln) * LDM + g * 4;
+                    const uint4 m0 = *reinterpret_cast<const uint4*>(mr);
+                    const uint4 m1 = *reinterpret_cast<const uint4*>(mr + 16);
+                    if constexpr (F32) {
+                        aM.v[0] = __uint_as_float(m0.x); aM.v[1] = __uint_as_float(m0.y);
+                        aM.v[2] = __uint_as_float(m0.z); aM.v[3] = __uint_as_float(m0.w);
+                        aM.v[4] = __uint_as_float(m1.x); aM.v[5] = __uint_as_float(m1.y);
+                        aM.v[6] = __uint_as_float(m1.z); aM.v[7] = __uint_as_float(m1.w);
+                    } else {
+                        uint4 hv, lv;
+                        hv.x = perm2(m0.y, m0.x, LO_HALVES); hv.y = perm2(m0.w, m0.z, LO_HALVES);
+                        hv.z = perm2(m1.y, m1.x, LO_HALVES); hv.w = perm2(m1.w, m1.z, LO_HALVES);
+                        lv.x = perm2(m0.y, m0.x, HI_HALVES); lv.y = perm2(m0.w, m0.z, HI_HALVES);
+                        lv.z = perm2(m1.y, m1.x, HI_HALVES); lv.w = perm2(m1.w, m1.z, HI_HALVES);
+                        aM.v = __builtin_bit_cast(bf16x8, hv);
+                        aMl.v = __builtin_bit_cast(bf16x8, lv);
+                    }
+                }
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                mma_k32<F32, SPLIT2>(O[tb][ct], aM, bU[ct]);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    if constexpr (!F32) {
+                        mma(O[tb][ct], aMl, bUh[ct]);
+                        mma(O[tb][ct], aM, bUl[ct]);
+                    }
+                    mma(O[tb][ct], aM, bUh[ct]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = tb * 16 + g * 4 + r;
-                    if (row < nvalid)
-                        p.o[((size_t)(c0 + row) * H + h) * DK + col0 + ct * 16 + ln] = O[tb][ct][r];
+                    for (int r = 0; r < 4; ++r) {
+                        const int el = (tb * 16 + g * 4 + r) * rowel + col0 + ct * 16 + ln;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[tb][ct][r]), ro,
+                                                              el * 4, 0, 0);
+                    }
                 }
             }
         }
 
-        // S <- Diag(e^{g_C}) S + K_end^T U with e^{g_C} = e^{-D0} e^{-D1} and
-        // k_end = (k e^{r_end(b) - g}) times e^{-D1} for sub-tile 0.
+        // S <- e^{E1 - E0} (S~ + Y^T U)
+        {
+            const float* e1 = sVec[buf][1];
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int i = it * 16 + ln;
-            const float e1 = Vec[3][i];
-            Frag8 aKe;
+            for (int it = 0; it < 8; ++it) {
+                Frag<F32> aY, aYl;
+                load_tile(aY, &sYt[buf][(it * 16 + ln) * LDY + g * 4]);
+                if constexpr (!F32) load_tile(aYl, &sYtl[buf][(it * 16 + ln) * LDY + g * 4]);
+                const float4 sc4 = *reinterpret_cast<const float4*>(e1 + it * 16 + g * 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                aKe.f[e] = Kh[(g * 4 + e) * LDT + i] * e1;
-                aKe.f[4 + e] = Kh[(16 + g * 4 + e) * LDT + i];
-            }
-            prep8<F32, SPLIT2>(aKe);
-            float dec[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = it * 16 + g * 4 + r;
-                dec[r] = Vec[1][row] * Vec[3][row];
-            }
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) S[it][ct][r] *= dec[r];
-                mma_k32<F32, SPLIT2>(S[it][ct], aKe, bU[ct]);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    if constexpr (!F32) {
+                        mma(S[it][ct], aYl, bUh[ct]);
+                        mma(S[it][ct], aY, bUl[ct]);
+                    }
+                    mma(S[it][ct], aY, bUh[ct]);
+                    S[it][ct][0] *= sc4.x;
+                    S[it][ct][1] *= sc4.y;
+                    S[it][ct][2] *= sc4.z;
+                    S[it][ct][3] *= sc4.w;
+                }
             }
         }
 
-        if (c0 + CH < t1) load_vb(c0 + CH);   // next chunk's v / beta
+        // Decay scan of the next chunk (its tiles are free: all waves passed
+        // the barrier after their last read), then prefetch the one after.
+        scan(buf ^ 1);
+        load_scan(cidx + 2);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pb[tb][r] = nb[tb][r];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) pv[tb][ct][r] = nv[tb][ct][r];
+            }
+        }
+        __syncthreads();
     }
 
     // ------------------------------------------------------------ state out
@@ -458,7 +715,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
 
 // Longest-first order of the packed sequences: order[rank] = sequence, with
 // rank = number of sequences that are longer, or as long with a smaller
-// index.  O(n^2) comparisons, used only for n <= kOrderMax.
+// index.  O(n^2) comparisons, used only for small n.
 __global__ void seq_order_kernel(const int32_t* __restrict__ cu, int32_t n, int64_t T,
                                  int32_t* __restrict__ order) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
