@@ -1,0 +1,130 @@
+"""The C-ABI library on the host: it loads, exports every symbol that
+include/kda.h declares, and rejects invalid arguments with the documented
+status codes before touching the GPU (no call here reaches a kernel launch).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULLP, SHAPE, DTYPE, ALIGN, ALIAS, WS, LARGE, HIPERR = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.library_path()):
+        from gated_delta_rule_amd import build
+        build.build()
+    return kda.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def header_status_codes():
+    text = open(HEADER).read()
+    return dict((m[0], int(m[1])) for m in re.findall(r"\b(KDA_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", text))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert names == sorted(["kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_bytes",
+                            "kda_chunk_fwd", "kda_decode_step"])
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    ver = int(re.search(r"#define KDA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.kda_abi_version() == ver
+    codes = header_status_codes()
+    assert codes["KDA_OK"] == OK and codes["KDA_ERR_HIP"] == HIPERR
+    for name, code in codes.items():
+        s = lib.kda_status_str(code).decode()
+        assert s.startswith(name)
+    assert lib.kda_status_str(12345).decode() == "unknown kda_status"
+
+
+def test_workspace_query(lib):
+    ws = lib.kda_chunk_fwd_workspace_bytes
+    assert ws(32, 270000, 96, 128, 128, 1) == 32 * 4
+    assert ws(32, 270000, 96, 128, 128, 0) == 0
+    assert ws(5000, 10 ** 6, 16, 128, 128, 1) == 0        # beyond the sorted-order limit
+    assert ws(32, 1000, 96, 64, 128, 1) == 0              # invalid head size
+    assert ws(-1, 1000, 96, 128, 128, 1) == 0
+
+
+# Fake, never-dereferenced device addresses for validation-only calls.
+A = 0x7F0000000000
+P = {n: A + i * 0x100000000 for i, n in enumerate(["q", "k", "v", "la", "b", "s0", "o", "st", "cu", "ws"])}
+
+
+def chunk(lib, **kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], dtype=0, la=P["la"], b=P["b"], s0=None, cu=None,
+             n=2, T=64, H=4, dk=128, dv=128, o=P["o"], st=P["st"], ws=None, wsb=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.kda_chunk_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), a["dtype"], vp(a["la"]),
+                             vp(a["b"]), vp(a["s0"]), vp(a["cu"]), a["n"], a["T"], a["H"], a["dk"],
+                             a["dv"], vp(a["o"]), vp(a["st"]), vp(a["ws"]), a["wsb"], None)
+
+
+def decode(lib, **kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], dtype=0, la=P["la"], b=P["b"], S=P["st"], B=8, H=4,
+             dk=128, dv=128, o=P["o"])
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.kda_decode_step(vp(a["q"]), vp(a["k"]), vp(a["v"]), a["dtype"], vp(a["la"]),
+                               vp(a["b"]), vp(a["S"]), a["B"], a["H"], a["dk"], a["dv"],
+                               vp(a["o"]), None)
+
+
+def test_chunk_fwd_validation(lib):
+    assert chunk(lib, dtype=7) == DTYPE
+    assert chunk(lib, dk=64) == SHAPE
+    assert chunk(lib, dv=256) == SHAPE
+    assert chunk(lib, H=0) == SHAPE
+    assert chunk(lib, T=-1) == SHAPE
+    assert chunk(lib, n=-1) == SHAPE
+    assert chunk(lib, q=None) == NULLP
+    assert chunk(lib, o=None) == NULLP
+    assert chunk(lib, b=None) == NULLP
+    assert chunk(lib, k=P["k"] + 2) == ALIGN
+    assert chunk(lib, s0=P["s0"] + 8) == ALIGN
+    assert chunk(lib, o=P["q"] + 64) == ALIAS          # o inside q
+    assert chunk(lib, st=P["v"]) == ALIAS              # S_T on top of v
+    assert chunk(lib, s0=P["s0"], st=P["s0"] + 1024) == ALIAS   # partial S0/S_T overlap
+    assert chunk(lib, cu=P["cu"], ws=None) == WS       # packed batch needs the order workspace
+    assert chunk(lib, cu=P["cu"], ws=P["ws"], wsb=4) == WS
+    assert chunk(lib, n=2 ** 31 - 1, T=2 ** 40) == LARGE
+    assert chunk(lib, n=0) == OK                        # empty batch: nothing to do
+    assert chunk(lib, n=3, T=0, q=None, k=None, v=None, la=None, b=None, o=None,
+                 st=P["st"] + 2) == ALIGN               # state pointers still checked
+
+
+def test_decode_validation(lib):
+    assert decode(lib, dtype=2) == DTYPE
+    assert decode(lib, dk=127) == SHAPE
+    assert decode(lib, H=0) == SHAPE
+    assert decode(lib, B=-3) == SHAPE
+    assert decode(lib, S=None) == NULLP
+    assert decode(lib, la=P["la"] + 4) == ALIGN
+    assert decode(lib, o=P["S"] if "S" in P else P["st"]) == ALIAS
+    assert decode(lib, S=P["k"]) == ALIAS
+    assert decode(lib, B=0) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kda, "_lib", None)
+    monkeypatch.setattr(kda, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(kda.KDAError):
+        kda.load_library()
