@@ -11,19 +11,25 @@
 //   q^T S_t = q^T S' + beta (q . k) (v - x)^T,   x = k^T S',
 // so one sweep over S produces both reductions x = k^T S' and y = q^T S'.
 //
-// Work decomposition: one 256-thread workgroup per (request, head) state of
-// 128 x 128 fp32 (64 KB).  Thread t owns value columns 4*(t & 31) .. +3 and
-// key rows 8 r + (t >> 5), r = 0..15, so each wave's 16 float4 loads cover
-// two adjacent 512-byte rows (1 KB contiguous) per instruction.  Reductions
-// over the 128 key rows: within a wave by a lane exchange (rows differ in
-// t >> 5 parity), across the four waves through LDS.  The launch is HBM
-// bound (about 0.86 flop per byte).
+// Work decomposition: one 1024-thread workgroup (16 waves) per (request,
+// head) state of 128 x 128 fp32.  Thread t owns value columns 4*(t & 31)..+3
+// and key rows (t >> 5) + 32 r, r = 0..3, so every wave instruction touches
+// two adjacent 512-byte rows (1 KB contiguous) and each thread keeps only 4
+// float4 of the state in flight (this shape measured fastest on MI355X HBM
+// for a read-then-write-in-place stream).  The state is streamed with
+// nontemporal loads and stores: it is touched once per step and is far
+// larger than the caches.  Reductions over the 128 key rows: lanes l and
+// l ^ 32 first, then the 16 waves through LDS in two levels.  The launch is
+// HBM bound (about 0.86 flop per byte).
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 
-constexpr int DEC_THREADS = 256;
+constexpr int DEC_THREADS = 1024;
+constexpr int DEC_WAVES = DEC_THREADS / 64;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <typename InT>
 __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
@@ -31,99 +37,98 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_step_kernel(
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     float* __restrict__ S, float* __restrict__ o) {
     const int tid = threadIdx.x;
-    const int cg = tid & 31;       // column group: columns 4cg .. 4cg+3
-    const int rg = tid >> 5;       // row group: rows 8r + rg
+    const int c4 = tid & 31;       // float4 column
+    const int rg = tid >> 5;       // row group: rows rg + 32 r
     const int wave = tid >> 6;
+    const int lane = tid & 63;
     const size_t bh = blockIdx.x;
 
     __shared__ float s_k[128], s_q[128], s_a[128], s_v[128];
-    __shared__ float s_red[4][32][9];  // per wave: x[4], y[4] per column group
+    __shared__ float s_red[DEC_WAVES][32][9];   // per wave, per float4 column: x[4], y[4]
+    __shared__ float s_xy[2][128];              // reduced x, y per value column
 
-    float4* Sp = reinterpret_cast<float4*>(S + bh * (128 * 128));
+    f32x4v* Sp = reinterpret_cast<f32x4v*>(S + bh * (128 * 128));
 
     // Issue the state stream first; it dominates the step.
-    float4 s[16];
+    f32x4v s[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = Sp[(8 * r + rg) * 32 + cg];
+    for (int r = 0; r < 4; ++r) s[r] = __builtin_nontemporal_load(Sp + (rg + 32 * r) * 32 + c4);
 
     if (tid < 128) {
         s_k[tid] = to_f32(k[bh * 128 + tid]);
-        s_q[tid] = to_f32(q[bh * 128 + tid]);
-        s_a[tid] = expf(log_alpha[bh * 128 + tid]);
-    } else {
-        s_v[tid - 128] = to_f32(v[bh * 128 + tid - 128]);
+    } else if (tid < 256) {
+        s_q[tid - 128] = to_f32(q[bh * 128 + tid - 128]);
+    } else if (tid < 384) {
+        s_a[tid - 256] = expf(log_alpha[bh * 128 + tid - 256]);
+    } else if (tid < 512) {
+        s_v[tid - 384] = to_f32(v[bh * 128 + tid - 384]);
     }
     const float b = beta[bh];
     __syncthreads();
 
     // q . k, reduced redundantly by every wave (no extra barrier).
-    const int lane = tid & 63;
     float qk = s_q[lane] * s_k[lane] + s_q[lane + 64] * s_k[lane + 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) qk += __shfl_xor(qk, off);
 
     // Decay, then partial x = k^T S' and y = q^T S' over this thread's rows.
     float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
-    float kr[16];
+    float kr[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 8 * r + rg;
+    for (int r = 0; r < 4; ++r) {
+        const int row = rg + 32 * r;
         const float a = s_a[row], kk = s_k[row], qq = s_q[row];
         kr[r] = kk;
-        s[r].x *= a;
-        s[r].y *= a;
-        s[r].z *= a;
-        s[r].w *= a;
-        x[0] += kk * s[r].x;
-        x[1] += kk * s[r].y;
-        x[2] += kk * s[r].z;
-        x[3] += kk * s[r].w;
-        y[0] += qq * s[r].x;
-        y[1] += qq * s[r].y;
-        y[2] += qq * s[r].z;
-        y[3] += qq * s[r].w;
+        s[r] *= a;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            x[c] += kk * s[r][c];
+            y[c] += qq * s[r][c];
+        }
     }
-    // Lanes l and l ^ 32 hold the same columns for row groups 2w and 2w+1.
+    // Lanes l and l ^ 32 hold the same columns for adjacent row groups.
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         x[c] += __shfl_xor(x[c], 32);
         y[c] += __shfl_xor(y[c], 32);
     }
-    if ((tid & 32) == 0) {
+    if (lane < 32) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            s_red[wave][cg][c] = x[c];
-            s_red[wave][cg][4 + c] = y[c];
+            s_red[wave][c4][c] = x[c];
+            s_red[wave][c4][4 + c] = y[c];
         }
     }
     __syncthreads();
+    if (tid < 256) {
+        // thread (value slot e = tid >> 5, float4 column c = tid & 31) sums the 16 waves
+        const int e = tid >> 5, c = tid & 31;
+        float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        x[c] = (s_red[0][cg][c] + s_red[1][cg][c]) + (s_red[2][cg][c] + s_red[3][cg][c]);
-        y[c] = (s_red[0][cg][4 + c] + s_red[1][cg][4 + c]) +
-               (s_red[2][cg][4 + c] + s_red[3][cg][4 + c]);
+        for (int w = 0; w < DEC_WAVES; ++w) acc += s_red[w][c][e];
+        s_xy[e >> 2][4 * c + (e & 3)] = acc;
     }
+    __syncthreads();
+    const float4 xv = *reinterpret_cast<const float4*>(&s_xy[0][4 * c4]);
+    const float4 yv = *reinterpret_cast<const float4*>(&s_xy[1][4 * c4]);
+    const float4 vv = *reinterpret_cast<const float4*>(&s_v[4 * c4]);
 
     // u = beta (v - x); S_t = S' + k u^T; o = y + (q . k) u.
-    float u[4];
+    float u[4] = {b * (vv.x - xv.x), b * (vv.y - xv.y), b * (vv.z - xv.z), b * (vv.w - xv.w)};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) u[c] = b * (s_v[4 * cg + c] - x[c]);
+    for (int r = 0; r < 4; ++r) {
+        f32x4v w = s[r];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        float4 w = s[r];
-        w.x += kr[r] * u[0];
-        w.y += kr[r] * u[1];
-        w.z += kr[r] * u[2];
-        w.w += kr[r] * u[3];
-        Sp[(8 * r + rg) * 32 + cg] = w;
+        for (int c = 0; c < 4; ++c) w[c] += kr[r] * u[c];
+        __builtin_nontemporal_store(w, Sp + (rg + 32 * r) * 32 + c4);
     }
     if (rg == 0) {
         float4 ov;
-        ov.x = y[0] + qk * u[0];
-        ov.y = y[1] + qk * u[1];
-        ov.z = y[2] + qk * u[2];
-        ov.w = y[3] + qk * u[3];
-        reinterpret_cast<float4*>(o + bh * 128)[cg] = ov;
+        ov.x = yv.x + qk * u[0];
+        ov.y = yv.y + qk * u[1];
+        ov.z = yv.z + qk * u[2];
+        ov.w = yv.w + qk * u[3];
+        reinterpret_cast<float4*>(o + bh * 128)[c4] = ov;
     }
 }
 
