@@ -56,7 +56,7 @@ namespace kda {
 constexpr int CH = 32;          // chunk length (tokens)
 constexpr int DK = 128;         // key / value head dimension
 constexpr int LDM = CH + 4;     // row stride of fp32 [CH][CH] tiles
-constexpr int PF_THREADS = 256;
+constexpr int PF_THREADS = 512;   // 4 consumer + 4 producer waves
 constexpr float LOG2E = 1.4426950408889634f;
 
 template <bool F32>
@@ -175,7 +175,7 @@ __device__ __forceinline__ void invert16(const float* L, float* T, int lane) {
 template <typename InT, int WCOLS>
 __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) {
     constexpr bool F32 = std::is_same<InT, float>::value;
-    constexpr int NCT = WCOLS / 16;   // 16-column tiles per wave
+    constexpr int NCT = WCOLS / 16;   // 16-column tiles per consumer wave
     constexpr int DVW = 4 * WCOLS;    // value columns per workgroup
     constexpr int ES = (int)sizeof(InT);
     typedef Tiles<F32> TL;
@@ -208,44 +208,33 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const bool consumer = wave < 4;
+    const int role = wave & 3;   // consumer column block / producer role
     const int g = lane >> 4;     // lane group
     const int ln = lane & 15;    // row / column within a 16-wide tile
-    const int col0 = slice * DVW + wave * WCOLS;   // first value column of this wave
+    const int col0 = slice * DVW + role * WCOLS;   // first value column (consumers)
 
     // ------------------------------------------------------------------ LDS
-    __shared__ __attribute__((aligned(16))) Op sX[CH * LDR];     // k e^{g - E0}
-    __shared__ __attribute__((aligned(16))) Op sQX[CH * LDR];    // q e^{g - E0} (hi)
-    __shared__ __attribute__((aligned(16))) Op sY[CH * LDR];     // k e^{E0 - g} (hi)
+    // Buffers indexed [chunk & 1] are written by the producers one step
+    // before the consumers read them; the others live within one step.
+    __shared__ __attribute__((aligned(16))) Op sX[2][CH * LDR];    // k e^{g - E0}
+    __shared__ __attribute__((aligned(16))) Op sQX[2][CH * LDR];   // q e^{g - E0} (hi)
+    __shared__ __attribute__((aligned(16))) Op sY[CH * LDR];       // k e^{E0 - g} (hi)
     __shared__ __attribute__((aligned(16))) Op sQXl[F32 ? 4 : CH * LDR];   // lo parts
     __shared__ __attribute__((aligned(16))) Op sYl[F32 ? 4 : CH * LDR];
     __shared__ __attribute__((aligned(16))) Op sYt[2][DK * LDY];               // Y^T hi
     __shared__ __attribute__((aligned(16))) Op sYtl[2][F32 ? 4 : DK * LDY];    // Y^T lo
     __shared__ __attribute__((aligned(16))) float sVec[2][2][DK];  // e^{E0}, e^{E1 - E0}
     __shared__ __attribute__((aligned(16))) float sL[CH * LDM];    // beta-scaled L blocks 00, 11
-    __shared__ __attribute__((aligned(16))) float sT[CH * LDM];    // T00, T11 and W = -T11 L10
+    __shared__ __attribute__((aligned(16))) float sT[2][CH * LDM]; // T00, T11 and W = -T11 L10
     // M = Tril(Q+ K-^T): bf16 path as packed (hi | lo << 16) pairs, fp32 path as floats.
-    __shared__ __attribute__((aligned(16))) uint32_t sM[CH * LDM];
+    __shared__ __attribute__((aligned(16))) uint32_t sM[2][CH * LDM];
 
     // M's upper-right 16 x 16 block is identically zero; never rewritten.
-    sM[(tid >> 4) * LDM + 16 + (tid & 15)] = 0u;
+    if (tid < 256) sM[0][(tid >> 4) * LDM + 16 + (tid & 15)] = 0u;
+    else sM[1][((tid - 256) >> 4) * LDM + 16 + (tid & 15)] = 0u;
 
-    // ------------------------------------------------------------ state in
-    f32x4 S[8][NCT];
-    const size_t sbase = ((size_t)n * H + h) * (DK * DK);
-#pragma unroll
-    for (int it = 0; it < 8; ++it)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[it][ct][r] = p.S0 ? p.S0[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 +
-                                           ct * 16 + ln]
-                                    : 0.f;
-
-    // --------------------------------------------------------- input loaders
-    // Valid tokens of the chunk starting at token c, and the bytes of a
-    // tensor's rows of head h from token c through the last valid one.
     auto n_valid = [&](int64_t c) -> int {
         const int64_t nv = t1 - c;
         return nv <= 0 ? 0 : (nv < CH ? (int)nv : CH);
@@ -253,15 +242,57 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     auto span_bytes = [&](int nv, int es) -> int {
         return nv <= 0 ? 0 : ((nv - 1) * rowel + DK) * es;
     };
+    // beta of a chunk in C layout (rows tb*16 + 4g + r), 0 past the end.
+    auto load_beta = [&](int64_t cidx, float (&b)[2][4]) {
+        const int64_t c = t0 + cidx * CH;
+        const int nv = n_valid(c);
+        const auto rb = make_rsrc(p.beta + (size_t)c * H + h, nv <= 0 ? 0 : ((nv - 1) * H + 1) * 4);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                b[tb][r] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rb, (tb * 16 + g * 4 + r) * H * 4, 0, 0));
+    };
+
+    // ======================================================== consumer state
+    f32x4 S[8][NCT];
+    const size_t sbase = ((size_t)n * H + h) * (DK * DK);
+    float pv[2][NCT][4], pb[2][4];
+    auto load_v = [&](int64_t cidx, float (&v)[2][NCT][4]) {
+        const int64_t c = t0 + cidx * CH;
+        const int nv = n_valid(c);
+        const auto rv = make_rsrc((const InT*)p.v + ((size_t)c * H + h) * DK, span_bytes(nv, ES));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const int el = (tb * 16 + g * 4 + r) * rowel + col0 + ct * 16 + ln;
+                    if constexpr (F32)
+                        v[tb][ct][r] = __uint_as_float(
+                            __builtin_amdgcn_raw_buffer_load_b32(rv, el * 4, 0, 0));
+                    else
+                        v[tb][ct][r] = __uint_as_float(
+                            (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, el * 2, 0, 0) << 16);
+                }
+    };
+    // Chain values carried from phase A to phase B of a step.
+    f32x4 O[2][NCT], U0[NCT], U1[NCT];
+    Frag<F32> bUh[NCT], bUl[NCT];
+
+    // ======================================================== producer state
     // Scan role: sub-tile sb, channel pair (2 cp, 2 cp + 1), half hf of the
     // sub-tile (tokens 16 sb + 8 hf + tau, tau < 8).
-    const int sb = wave >> 1;
-    const int cp = (wave & 1) * 32 + (lane & 31);
+    const int sb = role >> 1;
+    const int cp = (role & 1) * 32 + (lane & 31);
     const int hf = lane >> 5;
     const int sc = 2 * cp;
     typedef typename std::conditional<F32, float2, uint32_t>::type Pair;
     Pair xk[8], xq[8];
     float2 xl[8];
+    float pbp[2][4];   // beta of the chunk being prepared
     auto load_scan = [&](int64_t cidx) {
         const int64_t c = t0 + cidx * CH;
         const int nv = n_valid(c);
@@ -285,36 +316,9 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
             xl[tau] = make_float2(__uint_as_float(lv[0]), __uint_as_float(lv[1]));
         }
     };
-    // Values and beta in C layout for this wave's columns.
-    float pv[2][NCT][4];
-    float pb[2][4];
-    auto load_vb = [&](int64_t cidx, float (&v)[2][NCT][4], float (&b)[2][4]) {
-        const int64_t c = t0 + cidx * CH;
-        const int nv = n_valid(c);
-        const auto rv = make_rsrc((const InT*)p.v + ((size_t)c * H + h) * DK, span_bytes(nv, ES));
-        const auto rb = make_rsrc(p.beta + (size_t)c * H + h, nv <= 0 ? 0 : ((nv - 1) * H + 1) * 4);
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = tb * 16 + g * 4 + r;
-                b[tb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, row * H * 4, 0, 0));
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const int el = row * rowel + col0 + ct * 16 + ln;
-                    if constexpr (F32)
-                        v[tb][ct][r] = __uint_as_float(
-                            __builtin_amdgcn_raw_buffer_load_b32(rv, el * 4, 0, 0));
-                    else
-                        v[tb][ct][r] = __uint_as_float(
-                            (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, el * 2, 0, 0) << 16);
-                }
-            }
-    };
 
-    // ------------------------------------------------------------ decay scan
-    // Writes X, QX, Y (token-major, hi and lo where split), Y^T (channel-
-    // major, buffer `buf`) and the per-channel scalings of buffer `buf`.
+    // Decay scan: writes X, QX (buffer `buf`), Y and the lo parts (single),
+    // Y^T (buffer `buf`) and the per-channel scalings of buffer `buf`.
     auto scan = [&](int buf) {
         float cs0[8], cs1[8];
         float a0 = 0.f, a1 = 0.f;
@@ -334,6 +338,8 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
             *reinterpret_cast<float2*>(&sVec[buf][sb][sc]) =
                 make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
         const int tc = sb * 16 + hf * 8;
+        Op* X = sX[buf];
+        Op* QX = sQX[buf];
         if constexpr (F32) {
             float y0[8], y1[8];
 #pragma unroll
@@ -343,8 +349,8 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                 const float fy0 = __builtin_amdgcn_exp2f(-d0), fy1 = __builtin_amdgcn_exp2f(-d1);
                 const float2 kf = xk[tau], qf = xq[tau];
                 const int row = tc + tau;
-                *reinterpret_cast<float2*>(&sX[row * LDR + sc]) = make_float2(kf.x * fx0, kf.y * fx1);
-                *reinterpret_cast<float2*>(&sQX[row * LDR + sc]) = make_float2(qf.x * fx0, qf.y * fx1);
+                *reinterpret_cast<float2*>(&X[row * LDR + sc]) = make_float2(kf.x * fx0, kf.y * fx1);
+                *reinterpret_cast<float2*>(&QX[row * LDR + sc]) = make_float2(qf.x * fx0, qf.y * fx1);
                 y0[tau] = kf.x * fy0;
                 y1[tau] = kf.y * fy1;
                 *reinterpret_cast<float2*>(&sY[row * LDR + sc]) = make_float2(y0[tau], y1[tau]);
@@ -372,8 +378,8 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                 const float2 qhf = bf2_to_f2(qh), yhf = bf2_to_f2(yh[tau]);
                 yl[tau] = f2_to_bf2(Y0 - yhf.x, Y1 - yhf.y);
                 const int row = tc + tau;
-                *reinterpret_cast<uint32_t*>(&sX[row * LDR + sc]) = f2_to_bf2(X0, X1);
-                *reinterpret_cast<uint32_t*>(&sQX[row * LDR + sc]) = qh;
+                *reinterpret_cast<uint32_t*>(&X[row * LDR + sc]) = f2_to_bf2(X0, X1);
+                *reinterpret_cast<uint32_t*>(&QX[row * LDR + sc]) = qh;
                 *reinterpret_cast<uint32_t*>(&sQXl[row * LDR + sc]) = f2_to_bf2(Q0 - qhf.x, Q1 - qhf.y);
                 *reinterpret_cast<uint32_t*>(&sY[row * LDR + sc]) = yh[tau];
                 *reinterpret_cast<uint32_t*>(&sYl[row * LDR + sc]) = yl[tau];
@@ -422,7 +428,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
         return acc;
     };
     // Store an M block (C layout) at rows r0, columns c0, keeping j <= t if diag.
-    auto store_m = [&](const f32x4& m, int r0, int c0, bool diag) {
+    auto store_m = [&](uint32_t* Mb, const f32x4& m, int r0, int c0, bool diag) {
         uint32_t w[4];
         if constexpr (F32) {
 #pragma unroll
@@ -442,63 +448,31 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
             w[3] = perm2(l23, h23, HI_HALVES);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sM[(r0 + g * 4 + r) * LDM + c0 + ln] = w[r];
+        for (int r = 0; r < 4; ++r) Mb[(r0 + g * 4 + r) * LDM + c0 + ln] = w[r];
     };
 
-    // ------------------------------------------------------------- prologue
-    load_scan(0);
-    load_vb(0, pv, pb);
-    scan(0);
-    load_scan(1);
-    __syncthreads();
-
-    for (int64_t cidx = 0; cidx < nch; ++cidx) {
-        const int buf = (int)(cidx & 1);
-        const int64_t c0 = t0 + cidx * CH;
-        const int nvalid = n_valid(c0);
-
-        // ------------------------ L, M tiles, diagonal inverses and W
-        if (wave == 0) {
-            const f32x4 l00 = block(sX, sX, 0, sY, sY, 0, false);
+    // ------------------------------------------------------------ main loop
+    // Step s: producers prepare chunk s while consumers finish chunk s - 1.
+    // Each role runs its own loop over nch + 1 steps with two workgroup
+    // barriers per step; the role is wave-uniform, so the barrier counts match.
+    if (consumer) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = g * 4 + r;
-                sL[row * LDM + ln] = ln < row ? pb[0][r] * l00[r] : 0.f;
-            }
-            const f32x4 m00 = block(sQX, sQXl, 0, sY, sYl, 0, true);
-            wave_lds_sync();
-            invert16(sL, sT, lane);
-            store_m(m00, 0, 0, true);
-        } else if (wave == 1) {
-            const f32x4 l11 = block(sX, sX, 16, sY, sY, 16, false);
-            f32x4 l10 = block(sX, sX, 16, sY, sY, 0, false);
+        for (int it = 0; it < 8; ++it)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = g * 4 + r;
-                sL[(16 + row) * LDM + 16 + ln] = ln < row ? pb[1][r] * l11[r] : 0.f;
-                l10[r] *= pb[1][r];
-            }
-            wave_lds_sync();
-            invert16(sL + 16 * LDM + 16, sT + 16 * LDM + 16, lane);
-            wave_lds_sync();
-            // W = -T11 L10 (fp32 matrix cores; L10 is already in B layout)
-            f32x4 wacc = {0.f, 0.f, 0.f, 0.f};
-            const float4 t4 = *reinterpret_cast<const float4*>(sT + (16 + ln) * LDM + 16 + g * 4);
-            wacc = mfma4f(t4.x, l10[0], wacc);
-            wacc = mfma4f(t4.y, l10[1], wacc);
-            wacc = mfma4f(t4.z, l10[2], wacc);
-            wacc = mfma4f(t4.w, l10[3], wacc);
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(16 + g * 4 + r) * LDM + ln] = -wacc[r];
-        } else if (wave == 2) {
-            store_m(block(sQX, sQXl, 16, sY, sYl, 0, true), 16, 0, false);
-        } else {
-            store_m(block(sQX, sQXl, 16, sY, sYl, 16, true), 16, 16, true);
-        }
-
-        // -------------------- K+ S -> R and Q+ S -> O with S~ = e^{E0} S
-        f32x4 R[2][NCT], O[2][NCT];
-        {
+                for (int r = 0; r < 4; ++r)
+                    S[it][ct][r] = p.S0 ? p.S0[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 +
+                                               ct * 16 + ln]
+                                        : 0.f;
+        load_v(0, pv);
+        load_beta(0, pb);
+        __syncthreads();   // step 0: nothing to finish yet
+        __syncthreads();
+        for (int64_t cidx = 0; cidx < nch; ++cidx) {
+            // ---------------------------------------------------- phase A
+            const int buf = (int)(cidx & 1);
+            // S~ = e^{E0} S
             const float* e0 = sVec[buf][0];
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
@@ -511,121 +485,116 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                     S[it][ct][3] *= sc4.w;
                 }
             }
-        }
+            // K+ S -> R and Q+ S -> O
+            f32x4 R[2][NCT];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                R[tb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                O[tb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ct = 0; ct < NCT; ++ct) {
+                    R[tb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    O[tb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                Frag<F32> bS[NCT], bSl[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    float f[8];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        f[r] = S[2 * ks][ct][r];
+                        f[4 + r] = S[2 * ks + 1][ct][r];
+                    }
+                    if constexpr (F32) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) bS[ct].v[e] = f[e];
+                    } else {
+                        SplitBF<8> s8 = split8(f);
+                        bS[ct].v = s8.hi;
+                        bSl[ct].v = s8.lo;
+                    }
+                }
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    Frag<F32> aK, aQ;
+                    load_tile(aK, sX[buf] + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
+                    load_tile(aQ, sQX[buf] + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        if constexpr (!F32) {
+                            mma(R[tb][ct], aK, bSl[ct]);
+                            mma(O[tb][ct], aQ, bSl[ct]);
+                        }
+                        mma(R[tb][ct], aK, bS[ct]);
+                        mma(O[tb][ct], aQ, bS[ct]);
+                    }
+                }
             }
+            // R' = B_beta (V - K+ S)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            Frag<F32> bS[NCT], bSl[NCT];
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        R[tb][ct][r] = pb[tb][r] * (pv[tb][ct][r] - R[tb][ct][r]);
+            // next chunk's values and beta (used one step later)
+            load_v(cidx + 1, pv);
+            load_beta(cidx + 1, pb);
+            // U0 = T00 R'0 ; U1 = T11 R'1 + W U0   (W = -T11 L10)
+            {
+                const float* Tb = sT[buf];
+                float t00[4], t11[4], wm[4];
+                float4 a = *reinterpret_cast<const float4*>(Tb + ln * LDM + g * 4);
+                t00[0] = a.x; t00[1] = a.y; t00[2] = a.z; t00[3] = a.w;
+                a = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + 16 + g * 4);
+                t11[0] = a.x; t11[1] = a.y; t11[2] = a.z; t11[3] = a.w;
+                a = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + g * 4);
+                wm[0] = a.x; wm[1] = a.y; wm[2] = a.z; wm[3] = a.w;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    float b[4];
+                    U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) b[r] = R[0][ct][r];
+                    mma_k16<F32, SPLITB>(U0[ct], t00, b);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) b[r] = R[1][ct][r];
+                    mma_k16<F32, SPLITB>(U1[ct], t11, b);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) b[r] = U0[ct][r];
+                    mma_k16<F32, SPLITB>(U1[ct], wm, b);
+                }
+            }
+            // U as the B operand of M U and Y^T U (tile order: U0 rows, U1 rows).
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 float f[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    f[r] = S[2 * ks][ct][r];
-                    f[4 + r] = S[2 * ks + 1][ct][r];
+                    f[r] = U0[ct][r];
+                    f[4 + r] = U1[ct][r];
                 }
                 if constexpr (F32) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bS[ct].v[e] = f[e];
+                    for (int e = 0; e < 8; ++e) bUh[ct].v[e] = f[e];
                 } else {
                     SplitBF<8> s8 = split8(f);
-                    bS[ct].v = s8.hi;
-                    bSl[ct].v = s8.lo;
+                    bUh[ct].v = s8.hi;
+                    bUl[ct].v = s8.lo;
                 }
             }
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                Frag<F32> aK, aQ;
-                load_tile(aK, sX + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
-                load_tile(aQ, sQX + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    if constexpr (!F32) {
-                        mma(R[tb][ct], aK, bSl[ct]);
-                        mma(O[tb][ct], aQ, bSl[ct]);
-                    }
-                    mma(R[tb][ct], aK, bS[ct]);
-                    mma(O[tb][ct], aQ, bS[ct]);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ----------------------------- U, O, the state update; next scan
-        float nv[2][NCT][4];
-        float nb[2][4];
-        load_vb(cidx + 1, nv, nb);
-
-        // R' = B_beta (V - K+ S)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    R[tb][ct][r] = pb[tb][r] * (pv[tb][ct][r] - R[tb][ct][r]);
-
-        // U0 = T00 R'0 ; U1 = T11 R'1 + W U0   (W = -T11 L10)
-        f32x4 U0[NCT], U1[NCT];
-        {
-            float t00[4], t11[4], wm[4];
-            float4 a = *reinterpret_cast<const float4*>(sT + ln * LDM + g * 4);
-            t00[0] = a.x; t00[1] = a.y; t00[2] = a.z; t00[3] = a.w;
-            a = *reinterpret_cast<const float4*>(sT + (16 + ln) * LDM + 16 + g * 4);
-            t11[0] = a.x; t11[1] = a.y; t11[2] = a.z; t11[3] = a.w;
-            a = *reinterpret_cast<const float4*>(sT + (16 + ln) * LDM + g * 4);
-            wm[0] = a.x; wm[1] = a.y; wm[2] = a.z; wm[3] = a.w;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                float b[4];
-                U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) b[r] = R[0][ct][r];
-                mma_k16<F32, SPLITB>(U0[ct], t00, b);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) b[r] = R[1][ct][r];
-                mma_k16<F32, SPLITB>(U1[ct], t11, b);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) b[r] = U0[ct][r];
-                mma_k16<F32, SPLITB>(U1[ct], wm, b);
-            }
-        }
-
-        // U as the B operand of M U and Y^T U (tile order: U0 rows, U1 rows).
-        Frag<F32> bUh[NCT], bUl[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            float f[8];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                f[r] = U0[ct][r];
-                f[4 + r] = U1[ct][r];
-            }
-            if constexpr (F32) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bUh[ct].v[e] = f[e];
-            } else {
-                SplitBF<8> s8 = split8(f);
-                bUh[ct].v = s8.hi;
-                bUl[ct].v = s8.lo;
-            }
-        }
-
-        // O = Q+ S + M U; rows past the sequence end fall outside the store range.
-        {
-            const auto ro = make_rsrc(p.o + ((size_t)c0 * H + h) * DK, span_bytes(nvalid, 4));
+            __syncthreads();
+            // ---------------------------------------------------- phase B
+            const int64_t c0 = t0 + cidx * CH;
+            // O = Q+ S + M U; rows past the sequence end fall outside the store range.
+            const auto ro = make_rsrc(p.o + ((size_t)c0 * H + h) * DK, span_bytes(n_valid(c0), 4));
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
                 Frag<F32> aM, aMl;
                 {
-                    const uint32_t* mr = sM + (tb * 16 + ln) * LDM + g * 4;
+                    const uint32_t* mr = sM[buf] + (tb * 16 + ln) * LDM + g * 4;
                     const uint4 m0 = *reinterpret_cast<const uint4*>(mr);
                     const uint4 m1 = *reinterpret_cast<const uint4*>(mr + 16);
                     if constexpr (F32) {
@@ -658,10 +627,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                     }
                 }
             }
-        }
-
-        // S <- e^{E1 - E0} (S~ + Y^T U)
-        {
+            // S <- e^{E1 - E0} (S~ + Y^T U)
             const float* e1 = sVec[buf][1];
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
@@ -682,34 +648,73 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                     S[it][ct][3] *= sc4.w;
                 }
             }
+            __syncthreads();
         }
-
-        // Decay scan of the next chunk (its tiles are free: all waves passed
-        // the barrier after their last read), then prefetch the one after.
-        scan(buf ^ 1);
-        load_scan(cidx + 2);
+        if (p.S_T) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
+            for (int it = 0; it < 8; ++it)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pb[tb][r] = nb[tb][r];
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) pv[tb][ct][r] = nv[tb][ct][r];
+                    for (int r = 0; r < 4; ++r)
+                        p.S_T[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 + ct * 16 + ln] =
+                            S[it][ct][r];
+        }
+    } else {
+        load_scan(0);
+        for (int64_t s = 0; s < nch; ++s) {
+            // producers: decay scan of chunk s; prefetch chunk s + 1
+            scan((int)(s & 1));
+            load_scan(s + 1);
+            load_beta(s, pbp);
+            __syncthreads();
+            // producers: L, M tiles, diagonal inverses and W of chunk s
+            const int buf = (int)(s & 1);
+            const Op* X = sX[buf];
+            const Op* QX = sQX[buf];
+            float* Tb = sT[buf];
+            uint32_t* Mb = sM[buf];
+            if (role == 0) {
+                const f32x4 l00 = block(X, X, 0, sY, sY, 0, false);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = g * 4 + r;
+                    sL[row * LDM + ln] = ln < row ? pbp[0][r] * l00[r] : 0.f;
+                }
+                const f32x4 m00 = block(QX, sQXl, 0, sY, sYl, 0, true);
+                wave_lds_sync();
+                invert16(sL, Tb, lane);
+                store_m(Mb, m00, 0, 0, true);
+            } else if (role == 1) {
+                const f32x4 l11 = block(X, X, 16, sY, sY, 16, false);
+                f32x4 l10 = block(X, X, 16, sY, sY, 0, false);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = g * 4 + r;
+                    sL[(16 + row) * LDM + 16 + ln] = ln < row ? pbp[1][r] * l11[r] : 0.f;
+                    l10[r] *= pbp[1][r];
+                }
+                wave_lds_sync();
+                invert16(sL + 16 * LDM + 16, Tb + 16 * LDM + 16, lane);
+                wave_lds_sync();
+                // W = -T11 L10 (fp32 matrix cores; L10 is already in B layout)
+                f32x4 wacc = {0.f, 0.f, 0.f, 0.f};
+                const float4 t4 = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + 16 + g * 4);
+                wacc = mfma4f(t4.x, l10[0], wacc);
+                wacc = mfma4f(t4.y, l10[1], wacc);
+                wacc = mfma4f(t4.z, l10[2], wacc);
+                wacc = mfma4f(t4.w, l10[3], wacc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tb[(16 + g * 4 + r) * LDM + ln] = -wacc[r];
+            } else if (role == 2) {
+                store_m(Mb, block(QX, sQXl, 16, sY, sYl, 0, true), 16, 0, false);
+            } else {
+                store_m(Mb, block(QX, sQXl, 16, sY, sYl, 16, true), 16, 16, true);
             }
+            __syncthreads();
         }
+        __syncthreads();   // step nch: consumers finish the last chunk
         __syncthreads();
-    }
-
-    // ------------------------------------------------------------ state out
-    if (p.S_T) {
-#pragma unroll
-        for (int it = 0; it < 8; ++it)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    p.S_T[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 + ct * 16 + ln] =
-                        S[it][ct][r];
     }
 }
 
