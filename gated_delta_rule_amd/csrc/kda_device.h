@@ -40,36 +40,61 @@ struct SplitBF<4> {
     bf16x4 hi, lo;
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed bf16 pair (round to nearest even), and back.  The
+// empty asm emits nothing; it hides the packed value's origin so that the
+// compiler keeps one paired conversion instead of re-deriving each half with
+// a conversion of its own when only that half is inspected (which doubles
+// the conversions of a hi/lo split).  The conversion itself stays an
+// ordinary compiler-generated instruction.
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    bf16x2_t r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    uint32_t u = __builtin_bit_cast(uint32_t, r);
+    asm("" : "+v"(u));
+    return u;
+}
+__device__ __forceinline__ float bf2_first(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf2_second(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
 __device__ __forceinline__ bf16x8 round8(const float (&x)[8]) {
-    bf16x8 r;
+    u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
-    return r;
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf2(x[2 * i], x[2 * i + 1]);
+    return __builtin_bit_cast(bf16x8, w);
 }
 __device__ __forceinline__ bf16x4 round4(const float (&x)[4]) {
-    bf16x4 r;
+    u32x2 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = (__bf16)x[e];
-    return r;
+    for (int i = 0; i < 2; ++i) w[i] = pack_bf2(x[2 * i], x[2 * i + 1]);
+    return __builtin_bit_cast(bf16x4, w);
 }
+// Pairwise: hi = bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ SplitBF<8> split8(const float (&x)[8]) {
-    SplitBF<8> s;
+    u32x4 h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        __bf16 h = (__bf16)x[e];
-        s.hi[e] = h;
-        s.lo[e] = (__bf16)(x[e] - (float)h);
+    for (int i = 0; i < 4; ++i) {
+        h[i] = pack_bf2(x[2 * i], x[2 * i + 1]);
+        l[i] = pack_bf2(x[2 * i] - bf2_first(h[i]), x[2 * i + 1] - bf2_second(h[i]));
     }
+    SplitBF<8> s;
+    s.hi = __builtin_bit_cast(bf16x8, h);
+    s.lo = __builtin_bit_cast(bf16x8, l);
     return s;
 }
 __device__ __forceinline__ SplitBF<4> split4(const float (&x)[4]) {
-    SplitBF<4> s;
+    u32x2 h, l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        __bf16 h = (__bf16)x[e];
-        s.hi[e] = h;
-        s.lo[e] = (__bf16)(x[e] - (float)h);
+    for (int i = 0; i < 2; ++i) {
+        h[i] = pack_bf2(x[2 * i], x[2 * i + 1]);
+        l[i] = pack_bf2(x[2 * i] - bf2_first(h[i]), x[2 * i + 1] - bf2_second(h[i]));
     }
+    SplitBF<4> s;
+    s.hi = __builtin_bit_cast(bf16x4, h);
+    s.lo = __builtin_bit_cast(bf16x4, l);
     return s;
 }
 

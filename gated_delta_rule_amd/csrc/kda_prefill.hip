@@ -116,14 +116,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 __device__ __forceinline__ float2 bf2_to_f2(uint32_t u) {
-    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+    return make_float2(bf2_first(u), bf2_second(u));
 }
-__device__ __forceinline__ uint32_t f2_to_bf2(float a, float b) {
-    bf16x2_t r;
-    r[0] = (__bf16)a;
-    r[1] = (__bf16)b;
-    return __builtin_bit_cast(uint32_t, r);
-}
+__device__ __forceinline__ uint32_t f2_to_bf2(float a, float b) { return pack_bf2(a, b); }
 
 // Pack the low (sel = 0x05040100) or high (0x07060302) bf16 halves of two
 // dwords into one dword: result = {b.half, a.half}.
@@ -292,7 +287,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     typedef typename std::conditional<F32, float2, uint32_t>::type Pair;
     Pair xk[8], xq[8];
     float2 xl[8];
-    float pbp[2][4];   // beta of the chunk being prepared
+    float pbp[2][4];   // beta of the chunk being prepared (loaded one step ahead)
     auto load_scan = [&](int64_t cidx) {
         const int64_t c = t0 + cidx * CH;
         const int nv = n_valid(c);
@@ -661,12 +656,15 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                             S[it][ct][r];
         }
     } else {
+        load_beta(0, pbp);
         load_scan(0);
         for (int64_t s = 0; s < nch; ++s) {
-            // producers: decay scan of chunk s; prefetch chunk s + 1
+            // producers: decay scan of chunk s; prefetch chunk s + 1 (beta
+            // first: phase B waits for it, not for the larger tile loads)
             scan((int)(s & 1));
+            float pbn[2][4];
+            load_beta(s + 1, pbn);
             load_scan(s + 1);
-            load_beta(s, pbp);
             __syncthreads();
             // producers: L, M tiles, diagonal inverses and W of chunk s
             const int buf = (int)(s & 1);
@@ -712,6 +710,10 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                 store_m(Mb, block(QX, sQXl, 16, sY, sYl, 16, true), 16, 16, true);
             }
             __syncthreads();
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pbp[tb][r] = pbn[tb][r];
         }
         __syncthreads();   // step nch: consumers finish the last chunk
         __syncthreads();
