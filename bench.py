@@ -18,7 +18,6 @@ CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -52,24 +51,6 @@ def parse():
     return ap.parse_args()
 
 
-def src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def measured_traffic(kernel_file, profile_json):
-    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
-    on the current kernel source (else None)."""
-    try:
-        with open(profile_json) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256_16") != src_hash(kernel_file):
-        return None
-    return rec.get("hbm_bytes_per_launch")
-
-
 def run_decode_only(args, torch, kda, W, dev):
     wd = W.workload(4)
     S = torch.from_numpy(W.decode_state(wd)).to(dev)
@@ -95,6 +76,7 @@ def main():
     import torch
     import gated_delta_rule_amd as kda
     from gated_delta_rule_amd import workloads as W
+    from gated_delta_rule_amd.traffic import measured as measured_traffic
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -144,8 +126,7 @@ def main():
     pf_flops = B * T * H * PREFILL_FLOPS_PER_TOKEN_HEAD
     pf_gbps = pf_bytes / (pf_kernel_ms * 1e-3) / 1e9
     pf_tflops = pf_flops / (pf_kernel_ms * 1e-3) / 1e12
-    traffic = measured_traffic(os.path.join(ROOT, "gated_delta_rule_amd", "csrc", "kda_prefill.hip"),
-                               os.path.join(ROOT, "profiles", "chunk_fwd_workload1_traffic.json"))
+    traffic = measured_traffic("prefill")
     del d, o, S_T
     torch.cuda.empty_cache()
     if args.only == "prefill":
@@ -189,8 +170,7 @@ def main():
     state_gbps = 2 * n_states * STATE_BYTES / (dec_kernel_ms * 1e-3) / 1e9
     dec_bytes = n_states * (2 * STATE_BYTES + DECODE_INPUT_BYTES_PER_STATE)
     dec_gbps_all = dec_bytes / (dec_kernel_ms * 1e-3) / 1e9
-    dec_traffic = measured_traffic(os.path.join(ROOT, "gated_delta_rule_amd", "csrc", "kda_decode.hip"),
-                                   os.path.join(ROOT, "profiles", "decode_step_workload4_traffic.json"))
+    dec_traffic = measured_traffic("decode")
     del S, ins
     torch.cuda.empty_cache()
 

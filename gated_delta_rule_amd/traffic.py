@@ -1,0 +1,206 @@
+"""HBM traffic of the prefill and decode kernels from rocprofv3 counters.
+
+    python -m gated_delta_rule_amd.traffic collect [--out DIR]
+
+runs, for each target below, two rocprofv3 counter passes (FETCH_SIZE, then
+WRITE_SIZE; one pass per counter, each under its own time limit) as child
+processes, and writes `profiles/<kernel>_<workload>_traffic.json` with the
+bytes per launch.  The counters read KiB per dispatch; they are scaled by
+what the same counters read for a plain elementwise copy (y = 1 * x over
+1 GiB of fp32, so 1 GiB read and 1 GiB written) measured in the same way.
+
+    python -m gated_delta_rule_amd.traffic target {copy,prefill,decode}
+
+is the profiled program: it prepares the resident inputs of one workload
+and launches its kernel a few times.  The orchestrating process never
+touches the GPU itself.
+
+The JSON records a hash of the kernel's sources; the benchmark reports the
+traffic only while that hash matches the sources it runs.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+
+COPY_ELEMS = 1 << 28          # 1 GiB of fp32
+LAUNCHES = {"copy": 6, "prefill": 6, "decode": 8}
+
+# Kernel symbol fragment, profile name, sources the kernel is built from.
+TARGETS = {
+    "prefill": ("chunk_fwd_kernel", "chunk_fwd_workload1",
+                ("kda_prefill.hip", "kda_device.h", "kda_launch.h", "kda_abi.hip")),
+    "decode": ("decode_step_kernel", "decode_step_workload4",
+               ("kda_decode.hip", "kda_device.h", "kda_launch.h", "kda_abi.hip")),
+}
+
+
+def sources_hash(kind):
+    h = hashlib.sha256()
+    for name in TARGETS[kind][2]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def profile_path(kind, profiles_dir=None):
+    return os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), TARGETS[kind][1] + "_traffic.json")
+
+
+def measured(kind):
+    """Bytes per launch from the stored counters, or None when they were taken
+    on other sources (or never)."""
+    try:
+        with open(profile_path(kind)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_sha256_16") != sources_hash(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ targets
+def run_target(kind):
+    import torch
+    import gated_delta_rule_amd as kda
+    from gated_delta_rule_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    n = LAUNCHES[kind]
+    if kind == "copy":
+        x = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(n):
+            torch.mul(x, 1.0, out=y)
+    elif kind == "prefill":
+        w = W.workload(1)
+        a = W.prefill_inputs(w)
+        shp = (w.B, w.T, w.H, 128)
+        d = {k: torch.from_numpy(a[k]).to(dev, torch.bfloat16).view(shp) for k in ("q", "k", "v")}
+        la = torch.from_numpy(a["log_alpha"]).to(dev).view(shp)
+        b = torch.from_numpy(a["beta"]).to(dev).view(w.B, w.T, w.H)
+        o = torch.empty(shp, dtype=torch.float32, device=dev)
+        st = torch.empty((w.B, w.H, 128, 128), dtype=torch.float32, device=dev)
+        for _ in range(n):
+            kda.chunk_fwd(d["q"], d["k"], d["v"], la, b, None, None, o=o, S_T=st)
+    else:
+        w = W.workload(4)
+        S = torch.from_numpy(W.decode_state(w)).to(dev)
+        x = W.decode_inputs(w, 0)
+        e = {k: torch.from_numpy(x[k]).to(dev, torch.bfloat16) for k in ("q", "k", "v")}
+        la = torch.from_numpy(x["log_alpha"]).to(dev)
+        b = torch.from_numpy(x["beta"]).to(dev)
+        o = torch.empty((w.B, w.H, 128), dtype=torch.float32, device=dev)
+        for _ in range(n):
+            kda.decode_step(e["q"], e["k"], e["v"], la, b, S, o=o)
+    torch.cuda.synchronize()
+    print(f"target {kind}: {n} launches done", flush=True)
+
+
+# ------------------------------------------------------------ orchestration
+def counter_pass(kind, counter, out):
+    d = os.path.join(out, f"{kind}_{counter}")
+    cmd = ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", counter, "-d", d, "-o", "run",
+           "--output-format", "csv", "--", sys.executable, "-u", "-m", "gated_delta_rule_amd.traffic",
+           "target", kind]
+    env = dict(os.environ, TMPDIR="/tmp", PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    print("running:", " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, cwd="/tmp", env=env)
+    if r.returncode != 0:
+        raise SystemExit(f"rocprofv3 pass {kind}/{counter} failed with status {r.returncode}")
+    files = []
+    for dp, _, fs in os.walk(d):
+        files += [os.path.join(dp, f) for f in fs if f.endswith("counter_collection.csv")]
+    if not files:
+        raise SystemExit(f"no counter output under {d}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = (row["Dispatch_Id"], row["Kernel_Name"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    return per
+
+
+def kib_per_dispatch(per, fragment):
+    vals = [v for (_, name), v in per.items() if fragment in name]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {fragment!r}")
+    vals = vals[1:] if len(vals) > 2 else vals      # drop the first (cold) launch
+    return sum(vals) / len(vals), len(vals)
+
+
+def collect(out, profiles_dir):
+    os.makedirs(out, exist_ok=True)
+    os.makedirs(profiles_dir, exist_ok=True)
+    copy_bytes = COPY_ELEMS * 4
+    cal = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        per = counter_pass("copy", counter, out)
+        # the copy kernel is the one launched most often in its process
+        names = [name for (_, name) in per]
+        big = max(set(names), key=names.count)
+        kib, n = kib_per_dispatch(per, big)
+        cal[counter] = {"kib_per_dispatch": kib, "dispatches": n, "kernel": big,
+                        "scale": kib * 1024.0 / copy_bytes}
+        print(f"copy {counter}: {kib:.0f} KiB per dispatch, scale {cal[counter]['scale']:.4f}", flush=True)
+    for kind in ("prefill", "decode"):
+        frag = TARGETS[kind][0]
+        rec = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            kib, n = kib_per_dispatch(counter_pass(kind, counter, out), frag)
+            rec[counter] = {"kib_per_dispatch": kib, "dispatches": n,
+                            "bytes_scaled": kib * 1024.0 / cal[counter]["scale"]}
+        total = rec["FETCH_SIZE"]["bytes_scaled"] + rec["WRITE_SIZE"]["bytes_scaled"]
+        doc = {
+            "kernel": frag,
+            "workload": ("prefill B=1 T=8192 H=96 d=128 bf16, S0=0, o and S_T fp32" if kind == "prefill"
+                         else "decode B=256 H=96 d=128 bf16 inputs, fp32 state in place"),
+            "command": "python -m gated_delta_rule_amd.traffic collect (per pass: rocprofv3 --pmc "
+                       "<FETCH_SIZE|WRITE_SIZE> -d <dir> -o run --output-format csv -- python -u -m "
+                       f"gated_delta_rule_amd.traffic target {kind})",
+            "counters": rec,
+            "copy_calibration": {"kernel": "torch elementwise y = 1 * x, 1 GiB fp32 read + 1 GiB written",
+                                 **{k: {kk: vv for kk, vv in v.items() if kk != "kernel"}
+                                    for k, v in cal.items()}},
+            "hbm_bytes_per_launch": total,
+            "kernel_sources_sha256_16": sources_hash(kind),
+        }
+        path = profile_path(kind, profiles_dir)
+        with open(path, "w") as f:
+            json.dump(doc, f, indent=1)
+            f.write("\n")
+        print(f"{kind}: {total / 1e9:.4f} GB per launch -> {path}", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("target")
+    t.add_argument("kind", choices=["copy", "prefill", "decode"])
+    c = sub.add_parser("collect")
+    c.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "traffic"),
+                   help="directory for the raw counter output")
+    c.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"),
+                   help="where the per-kernel JSON summaries go")
+    args = ap.parse_args()
+    if args.cmd == "target":
+        run_target(args.kind)
+    else:
+        collect(os.path.abspath(args.out), os.path.abspath(args.profiles_dir))
+
+
+if __name__ == "__main__":
+    main()
