@@ -138,6 +138,12 @@ __device__ __forceinline__ float quad_bcast(float x, int qc) {
     }
 }
 
+// Value of lane l ^ 32 (one cross-half swap, no LDS round trip).
+__device__ __forceinline__ float lane_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // (I + L)^{-1} of a 16 x 16 strictly lower-triangular L (LDS, row stride
 // LDM, upper part stored as zeros) by forward substitution on one wave:
 // lane 4j + q owns rows q, q+4, q+8, q+12 of column j; at step c the owner
@@ -222,7 +228,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     __shared__ __attribute__((aligned(16))) Op sYtl[2][F32 ? 4 : DK * LDY];    // Y^T lo
     __shared__ __attribute__((aligned(16))) float sVec[2][2][DK];  // e^{E0}, e^{E1 - E0}
     __shared__ __attribute__((aligned(16))) float sL[CH * LDM];    // beta-scaled L blocks 00, 11
-    __shared__ __attribute__((aligned(16))) float sT[2][CH * LDM]; // T00, T11 and W = -T11 L10
+    __shared__ __attribute__((aligned(16))) float sT[2][CH * LDM]; // T00, T11 and -L10 (beta-scaled)
     // M = Tril(Q+ K-^T): bf16 path as packed (hi | lo << 16) pairs, fp32 path as floats.
     __shared__ __attribute__((aligned(16))) uint32_t sM[2][CH * LDM];
 
@@ -288,33 +294,50 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     Pair xk[8], xq[8];
     float2 xl[8];
     float pbp[2][4];   // beta of the chunk being prepared (loaded one step ahead)
-    auto load_scan = [&](int64_t cidx) {
+    // Loads of one chunk's k, q (channel pair) and log alpha, one token at a
+    // time, so that the scan can refill each register right after its last
+    // use and the next chunk's loads overlap this chunk's arithmetic.
+    struct ScanSrc {
+        __amdgpu_buffer_rsrc_t k, q, l;
+    };
+    auto scan_src = [&](int64_t cidx) {
         const int64_t c = t0 + cidx * CH;
         const int nv = n_valid(c);
         const size_t eoff = ((size_t)c * H + h) * DK;
-        const auto rk = make_rsrc((const InT*)p.k + eoff, span_bytes(nv, ES));
-        const auto rq = make_rsrc((const InT*)p.q + eoff, span_bytes(nv, ES));
-        const auto rl = make_rsrc(p.la + eoff, span_bytes(nv, 4));
+        return ScanSrc{make_rsrc((const InT*)p.k + eoff, span_bytes(nv, ES)),
+                       make_rsrc((const InT*)p.q + eoff, span_bytes(nv, ES)),
+                       make_rsrc(p.la + eoff, span_bytes(nv, 4))};
+    };
+    auto load_kq = [&](const ScanSrc& r, int tau) {
+        const int el = (sb * 16 + hf * 8 + tau) * rowel + sc;
+        if constexpr (F32) {
+            auto a = __builtin_amdgcn_raw_buffer_load_b64(r.k, el * 4, 0, 0);
+            auto b = __builtin_amdgcn_raw_buffer_load_b64(r.q, el * 4, 0, 0);
+            xk[tau] = make_float2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+            xq[tau] = make_float2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+        } else {
+            xk[tau] = __builtin_amdgcn_raw_buffer_load_b32(r.k, el * 2, 0, 0);
+            xq[tau] = __builtin_amdgcn_raw_buffer_load_b32(r.q, el * 2, 0, 0);
+        }
+    };
+    auto load_la = [&](const ScanSrc& r, int tau) {
+        const int el = (sb * 16 + hf * 8 + tau) * rowel + sc;
+        auto lv = __builtin_amdgcn_raw_buffer_load_b64(r.l, el * 4, 0, 0);
+        xl[tau] = make_float2(__uint_as_float(lv[0]), __uint_as_float(lv[1]));
+    };
+    auto load_scan = [&](int64_t cidx) {
+        const ScanSrc r = scan_src(cidx);
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) {
-            const int el = (sb * 16 + hf * 8 + tau) * rowel + sc;
-            if constexpr (F32) {
-                auto a = __builtin_amdgcn_raw_buffer_load_b64(rk, el * 4, 0, 0);
-                auto b = __builtin_amdgcn_raw_buffer_load_b64(rq, el * 4, 0, 0);
-                xk[tau] = make_float2(__uint_as_float(a[0]), __uint_as_float(a[1]));
-                xq[tau] = make_float2(__uint_as_float(b[0]), __uint_as_float(b[1]));
-            } else {
-                xk[tau] = __builtin_amdgcn_raw_buffer_load_b32(rk, el * 2, 0, 0);
-                xq[tau] = __builtin_amdgcn_raw_buffer_load_b32(rq, el * 2, 0, 0);
-            }
-            auto lv = __builtin_amdgcn_raw_buffer_load_b64(rl, el * 4, 0, 0);
-            xl[tau] = make_float2(__uint_as_float(lv[0]), __uint_as_float(lv[1]));
+            load_kq(r, tau);
+            load_la(r, tau);
         }
     };
 
     // Decay scan: writes X, QX (buffer `buf`), Y and the lo parts (single),
     // Y^T (buffer `buf`) and the per-channel scalings of buffer `buf`.
-    auto scan = [&](int buf) {
+    auto scan = [&](int buf, int64_t cnext) {
+        const ScanSrc nx = scan_src(cnext);
         float cs0[8], cs1[8];
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -324,8 +347,10 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
             cs0[tau] = a0;
             cs1[tau] = a1;
         }
+#pragma unroll
+        for (int tau = 0; tau < 8; ++tau) load_la(nx, tau);
         // the two halves of the sub-tile live in lanes l and l ^ 32
-        const float o0 = __shfl_xor(a0, 32), o1 = __shfl_xor(a1, 32);
+        const float o0 = lane_xor32(a0), o1 = lane_xor32(a1);
         const float pre0 = hf ? o0 : 0.f, pre1 = hf ? o1 : 0.f;
         const float tot0 = hf ? o0 + a0 : a0 + o0, tot1 = hf ? o1 + a1 : a1 + o1;
         const float ref0 = sb == 0 ? tot0 : 0.f, ref1 = sb == 0 ? tot1 : 0.f;
@@ -343,6 +368,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                 const float fx0 = __builtin_amdgcn_exp2f(d0), fx1 = __builtin_amdgcn_exp2f(d1);
                 const float fy0 = __builtin_amdgcn_exp2f(-d0), fy1 = __builtin_amdgcn_exp2f(-d1);
                 const float2 kf = xk[tau], qf = xq[tau];
+                load_kq(nx, tau);
                 const int row = tc + tau;
                 *reinterpret_cast<float2*>(&X[row * LDR + sc]) = make_float2(kf.x * fx0, kf.y * fx1);
                 *reinterpret_cast<float2*>(&QX[row * LDR + sc]) = make_float2(qf.x * fx0, qf.y * fx1);
@@ -365,6 +391,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                 const float fx0 = __builtin_amdgcn_exp2f(d0), fx1 = __builtin_amdgcn_exp2f(d1);
                 const float fy0 = __builtin_amdgcn_exp2f(-d0), fy1 = __builtin_amdgcn_exp2f(-d1);
                 const float2 kf = bf2_to_f2(xk[tau]), qf = bf2_to_f2(xq[tau]);
+                load_kq(nx, tau);
                 const float X0 = kf.x * fx0, X1 = kf.y * fx1;
                 const float Q0 = qf.x * fx0, Q1 = qf.y * fx1;
                 const float Y0 = kf.x * fy0, Y1 = kf.y * fy1;
@@ -536,16 +563,17 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
             // next chunk's values and beta (used one step later)
             load_v(cidx + 1, pv);
             load_beta(cidx + 1, pb);
-            // U0 = T00 R'0 ; U1 = T11 R'1 + W U0   (W = -T11 L10)
+            // Block forward substitution of (I + L) U = R':
+            //   U0 = T00 R'0,  U1 = T11 (R'1 - L10 U0)
             {
                 const float* Tb = sT[buf];
-                float t00[4], t11[4], wm[4];
+                float t00[4], t11[4], nl10[4];
                 float4 a = *reinterpret_cast<const float4*>(Tb + ln * LDM + g * 4);
                 t00[0] = a.x; t00[1] = a.y; t00[2] = a.z; t00[3] = a.w;
                 a = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + 16 + g * 4);
                 t11[0] = a.x; t11[1] = a.y; t11[2] = a.z; t11[3] = a.w;
                 a = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + g * 4);
-                wm[0] = a.x; wm[1] = a.y; wm[2] = a.z; wm[3] = a.w;
+                nl10[0] = a.x; nl10[1] = a.y; nl10[2] = a.z; nl10[3] = a.w;
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     float b[4];
@@ -554,12 +582,13 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
 #pragma unroll
                     for (int r = 0; r < 4; ++r) b[r] = R[0][ct][r];
                     mma_k16<F32, SPLITB>(U0[ct], t00, b);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) b[r] = R[1][ct][r];
-                    mma_k16<F32, SPLITB>(U1[ct], t11, b);
+                    f32x4 rhs = R[1][ct];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) b[r] = U0[ct][r];
-                    mma_k16<F32, SPLITB>(U1[ct], wm, b);
+                    mma_k16<F32, SPLITB>(rhs, nl10, b);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) b[r] = rhs[r];
+                    mma_k16<F32, SPLITB>(U1[ct], t11, b);
                 }
             }
             // U as the B operand of M U and Y^T U (tile order: U0 rows, U1 rows).
@@ -659,14 +688,13 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
         load_beta(0, pbp);
         load_scan(0);
         for (int64_t s = 0; s < nch; ++s) {
-            // producers: decay scan of chunk s; prefetch chunk s + 1 (beta
-            // first: phase B waits for it, not for the larger tile loads)
-            scan((int)(s & 1));
+            // producers: decay scan of chunk s, which also issues the loads of
+            // chunk s + 1 (beta first: phase B waits for it, not for the tiles)
             float pbn[2][4];
             load_beta(s + 1, pbn);
-            load_scan(s + 1);
+            scan((int)(s & 1), s + 1);
             __syncthreads();
-            // producers: L, M tiles, diagonal inverses and W of chunk s
+            // producers: L, M tiles and the diagonal inverses of chunk s
             const int buf = (int)(s & 1);
             const Op* X = sX[buf];
             const Op* QX = sQX[buf];
@@ -679,35 +707,26 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                     const int row = g * 4 + r;
                     sL[row * LDM + ln] = ln < row ? pbp[0][r] * l00[r] : 0.f;
                 }
-                const f32x4 m00 = block(QX, sQXl, 0, sY, sYl, 0, true);
                 wave_lds_sync();
                 invert16(sL, Tb, lane);
-                store_m(Mb, m00, 0, 0, true);
             } else if (role == 1) {
                 const f32x4 l11 = block(X, X, 16, sY, sY, 16, false);
-                f32x4 l10 = block(X, X, 16, sY, sY, 0, false);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = g * 4 + r;
                     sL[(16 + row) * LDM + 16 + ln] = ln < row ? pbp[1][r] * l11[r] : 0.f;
-                    l10[r] *= pbp[1][r];
                 }
                 wave_lds_sync();
                 invert16(sL + 16 * LDM + 16, Tb + 16 * LDM + 16, lane);
-                wave_lds_sync();
-                // W = -T11 L10 (fp32 matrix cores; L10 is already in B layout)
-                f32x4 wacc = {0.f, 0.f, 0.f, 0.f};
-                const float4 t4 = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + 16 + g * 4);
-                wacc = mfma4f(t4.x, l10[0], wacc);
-                wacc = mfma4f(t4.y, l10[1], wacc);
-                wacc = mfma4f(t4.z, l10[2], wacc);
-                wacc = mfma4f(t4.w, l10[3], wacc);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Tb[(16 + g * 4 + r) * LDM + ln] = -wacc[r];
             } else if (role == 2) {
+                // -L10 (beta-scaled) goes where the consumers read it
+                const f32x4 l10 = block(X, X, 16, sY, sY, 0, false);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tb[(16 + g * 4 + r) * LDM + ln] = -pbp[1][r] * l10[r];
                 store_m(Mb, block(QX, sQXl, 16, sY, sYl, 0, true), 16, 0, false);
             } else {
                 store_m(Mb, block(QX, sQXl, 16, sY, sYl, 16, true), 16, 16, true);
+                store_m(Mb, block(QX, sQXl, 0, sY, sYl, 0, true), 0, 0, true);
             }
             __syncthreads();
 #pragma unroll
