@@ -56,7 +56,6 @@ namespace kda {
 constexpr int CH = 32;          // chunk length (tokens)
 constexpr int DK = 128;         // key / value head dimension
 constexpr int LDM = CH + 4;     // row stride of fp32 [CH][CH] tiles
-constexpr int PF_THREADS = 512;   // 4 consumer + 4 producer waves
 constexpr float LOG2E = 1.4426950408889634f;
 
 template <bool F32>
@@ -138,10 +137,38 @@ __device__ __forceinline__ float quad_bcast(float x, int qc) {
     }
 }
 
-// Value of lane l ^ 32 (one cross-half swap, no LDS round trip).
+// Value of lane l ^ 32, and of lane l ^ 16 (one cross-row swap each, no
+// LDS round trip).
 __device__ __forceinline__ float lane_xor32(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
+// Exclusive prefix `pre` and total `tot` of the per-lane sums `a` over the
+// PARTS lanes l, l + 64/PARTS, ... that hold consecutive token runs of one
+// channel.  The total is formed in one fixed order, so every part gets the
+// same bits.
+template <int PARTS>
+__device__ __forceinline__ void parts_scan(float a, int part, float& pre, float& tot) {
+    if constexpr (PARTS == 2) {
+        const float b = lane_xor32(a);
+        pre = part ? b : 0.f;
+        tot = part ? b + a : a + b;
+    } else {
+        static_assert(PARTS == 4, "two or four parts");
+        const bool odd = part & 1, upper = part & 2;
+        const float b = lane_xor16(a);
+        const float lo = odd ? b : a, hi = odd ? a : b;
+        const float ps = lo + hi;   // sum of the pair of parts
+        const float c = lane_xor32(ps);
+        const float plo = upper ? c : ps, phi = upper ? ps : c;
+        tot = plo + phi;
+        pre = (upper ? plo : 0.f) + (odd ? lo : 0.f);
+    }
 }
 
 // (I + L)^{-1} of a 16 x 16 strictly lower-triangular L (LDS, row stride
@@ -173,8 +200,9 @@ __device__ __forceinline__ void invert16(const float* L, float* T, int lane) {
     for (int k = 0; k < 4; ++k) T[(q + 4 * k) * LDM + j] = x[k];
 }
 
-template <typename InT, int WCOLS>
-__global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) {
+// NPROD producer waves (4 or 8) follow the 4 consumer waves.
+template <typename InT, int WCOLS, int NPROD>
+__global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillParams p) {
     constexpr bool F32 = std::is_same<InT, float>::value;
     constexpr int NCT = WCOLS / 16;   // 16-column tiles per consumer wave
     constexpr int DVW = 4 * WCOLS;    // value columns per workgroup
@@ -211,7 +239,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const bool consumer = wave < 4;
-    const int role = wave & 3;   // consumer column block / producer role
+    const int role = consumer ? wave : wave - 4;   // consumer column block / producer role
     const int g = lane >> 4;     // lane group
     const int ln = lane & 15;    // row / column within a 16-wide tile
     const int col0 = slice * DVW + role * WCOLS;   // first value column (consumers)
@@ -233,8 +261,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     __shared__ __attribute__((aligned(16))) uint32_t sM[2][CH * LDM];
 
     // M's upper-right 16 x 16 block is identically zero; never rewritten.
-    if (tid < 256) sM[0][(tid >> 4) * LDM + 16 + (tid & 15)] = 0u;
-    else sM[1][((tid - 256) >> 4) * LDM + 16 + (tid & 15)] = 0u;
+    if (tid < 512) sM[tid >> 8][((tid & 255) >> 4) * LDM + 16 + (tid & 15)] = 0u;
 
     auto n_valid = [&](int64_t c) -> int {
         const int64_t nv = t1 - c;
@@ -284,15 +311,20 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     Frag<F32> bUh[NCT], bUl[NCT];
 
     // ======================================================== producer state
-    // Scan role: sub-tile sb, channel pair (2 cp, 2 cp + 1), half hf of the
-    // sub-tile (tokens 16 sb + 8 hf + tau, tau < 8).
-    const int sb = role >> 1;
-    const int cp = (role & 1) * 32 + (lane & 31);
-    const int hf = lane >> 5;
+    // Scan role: a lane handles TPL consecutive tokens of the channel pair
+    // (2 cp, 2 cp + 1); the PARTS lanes holding one pair (lane stride LPP)
+    // cover the 16-token sub-tile sb.
+    constexpr int TPL = 32 / NPROD;     // tokens per lane
+    constexpr int PARTS = 16 / TPL;     // lanes per channel pair and sub-tile
+    constexpr int LPP = 64 / PARTS;     // channel pairs per wave
+    constexpr int WPS = NPROD / 2;      // waves per sub-tile
+    const int sb = role / WPS;
+    const int cp = (role % WPS) * LPP + lane % LPP;
+    const int part = lane / LPP;
     const int sc = 2 * cp;
     typedef typename std::conditional<F32, float2, uint32_t>::type Pair;
-    Pair xk[8], xq[8];
-    float2 xl[8];
+    Pair xk[TPL], xq[TPL];
+    float2 xl[TPL];
     float pbp[2][4];   // beta of the chunk being prepared (loaded one step ahead)
     // Loads of one chunk's k, q (channel pair) and log alpha, one token at a
     // time, so that the scan can refill each register right after its last
@@ -309,7 +341,7 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                        make_rsrc(p.la + eoff, span_bytes(nv, 4))};
     };
     auto load_kq = [&](const ScanSrc& r, int tau) {
-        const int el = (sb * 16 + hf * 8 + tau) * rowel + sc;
+        const int el = (sb * 16 + part * TPL + tau) * rowel + sc;
         if constexpr (F32) {
             auto a = __builtin_amdgcn_raw_buffer_load_b64(r.k, el * 4, 0, 0);
             auto b = __builtin_amdgcn_raw_buffer_load_b64(r.q, el * 4, 0, 0);
@@ -321,14 +353,14 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
         }
     };
     auto load_la = [&](const ScanSrc& r, int tau) {
-        const int el = (sb * 16 + hf * 8 + tau) * rowel + sc;
+        const int el = (sb * 16 + part * TPL + tau) * rowel + sc;
         auto lv = __builtin_amdgcn_raw_buffer_load_b64(r.l, el * 4, 0, 0);
         xl[tau] = make_float2(__uint_as_float(lv[0]), __uint_as_float(lv[1]));
     };
     auto load_scan = [&](int64_t cidx) {
         const ScanSrc r = scan_src(cidx);
 #pragma unroll
-        for (int tau = 0; tau < 8; ++tau) {
+        for (int tau = 0; tau < TPL; ++tau) {
             load_kq(r, tau);
             load_la(r, tau);
         }
@@ -338,32 +370,31 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
     // Y^T (buffer `buf`) and the per-channel scalings of buffer `buf`.
     auto scan = [&](int buf, int64_t cnext) {
         const ScanSrc nx = scan_src(cnext);
-        float cs0[8], cs1[8];
+        float cs0[TPL], cs1[TPL];
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int tau = 0; tau < 8; ++tau) {
+        for (int tau = 0; tau < TPL; ++tau) {
             a0 += xl[tau].x * LOG2E;
             a1 += xl[tau].y * LOG2E;
             cs0[tau] = a0;
             cs1[tau] = a1;
         }
 #pragma unroll
-        for (int tau = 0; tau < 8; ++tau) load_la(nx, tau);
-        // the two halves of the sub-tile live in lanes l and l ^ 32
-        const float o0 = lane_xor32(a0), o1 = lane_xor32(a1);
-        const float pre0 = hf ? o0 : 0.f, pre1 = hf ? o1 : 0.f;
-        const float tot0 = hf ? o0 + a0 : a0 + o0, tot1 = hf ? o1 + a1 : a1 + o1;
+        for (int tau = 0; tau < TPL; ++tau) load_la(nx, tau);
+        float pre0, pre1, tot0, tot1;
+        parts_scan<PARTS>(a0, part, pre0, tot0);
+        parts_scan<PARTS>(a1, part, pre1, tot1);
         const float ref0 = sb == 0 ? tot0 : 0.f, ref1 = sb == 0 ? tot1 : 0.f;
-        if (hf == 0)
+        if (part == 0)
             *reinterpret_cast<float2*>(&sVec[buf][sb][sc]) =
                 make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
-        const int tc = sb * 16 + hf * 8;
+        const int tc = sb * 16 + part * TPL;
         Op* X = sX[buf];
         Op* QX = sQX[buf];
         if constexpr (F32) {
-            float y0[8], y1[8];
+            float y0[TPL], y1[TPL];
 #pragma unroll
-            for (int tau = 0; tau < 8; ++tau) {
+            for (int tau = 0; tau < TPL; ++tau) {
                 const float d0 = cs0[tau] + pre0 - ref0, d1 = cs1[tau] + pre1 - ref1;
                 const float fx0 = __builtin_amdgcn_exp2f(d0), fx1 = __builtin_amdgcn_exp2f(d1);
                 const float fy0 = __builtin_amdgcn_exp2f(-d0), fy1 = __builtin_amdgcn_exp2f(-d1);
@@ -377,16 +408,16 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                 *reinterpret_cast<float2*>(&sY[row * LDR + sc]) = make_float2(y0[tau], y1[tau]);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < TPL / 4; ++i) {
                 *reinterpret_cast<float4*>(&sYt[buf][sc * LDY + tc + 4 * i]) =
                     make_float4(y0[4 * i], y0[4 * i + 1], y0[4 * i + 2], y0[4 * i + 3]);
                 *reinterpret_cast<float4*>(&sYt[buf][(sc + 1) * LDY + tc + 4 * i]) =
                     make_float4(y1[4 * i], y1[4 * i + 1], y1[4 * i + 2], y1[4 * i + 3]);
             }
         } else {
-            uint32_t yh[8], yl[8];
+            uint32_t yh[TPL], yl[TPL];
 #pragma unroll
-            for (int tau = 0; tau < 8; ++tau) {
+            for (int tau = 0; tau < TPL; ++tau) {
                 const float d0 = cs0[tau] + pre0 - ref0, d1 = cs1[tau] + pre1 - ref1;
                 const float fx0 = __builtin_amdgcn_exp2f(d0), fx1 = __builtin_amdgcn_exp2f(d1);
                 const float fy0 = __builtin_amdgcn_exp2f(-d0), fy1 = __builtin_amdgcn_exp2f(-d1);
@@ -407,20 +438,26 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                 *reinterpret_cast<uint32_t*>(&sYl[row * LDR + sc]) = yl[tau];
             }
             // Y^T rows sc and sc + 1: regroup the channel pairs into runs of
-            // 8 tokens per channel.
-            uint4 h0, h1, l0, l1;
-            h0.x = perm2(yh[1], yh[0], LO_HALVES); h0.y = perm2(yh[3], yh[2], LO_HALVES);
-            h0.z = perm2(yh[5], yh[4], LO_HALVES); h0.w = perm2(yh[7], yh[6], LO_HALVES);
-            h1.x = perm2(yh[1], yh[0], HI_HALVES); h1.y = perm2(yh[3], yh[2], HI_HALVES);
-            h1.z = perm2(yh[5], yh[4], HI_HALVES); h1.w = perm2(yh[7], yh[6], HI_HALVES);
-            l0.x = perm2(yl[1], yl[0], LO_HALVES); l0.y = perm2(yl[3], yl[2], LO_HALVES);
-            l0.z = perm2(yl[5], yl[4], LO_HALVES); l0.w = perm2(yl[7], yl[6], LO_HALVES);
-            l1.x = perm2(yl[1], yl[0], HI_HALVES); l1.y = perm2(yl[3], yl[2], HI_HALVES);
-            l1.z = perm2(yl[5], yl[4], HI_HALVES); l1.w = perm2(yl[7], yl[6], HI_HALVES);
-            *reinterpret_cast<uint4*>(&sYt[buf][sc * LDY + tc]) = h0;
-            *reinterpret_cast<uint4*>(&sYt[buf][(sc + 1) * LDY + tc]) = h1;
-            *reinterpret_cast<uint4*>(&sYtl[buf][sc * LDY + tc]) = l0;
-            *reinterpret_cast<uint4*>(&sYtl[buf][(sc + 1) * LDY + tc]) = l1;
+            // TPL tokens per channel.
+            uint32_t h0[TPL / 2], h1[TPL / 2], l0[TPL / 2], l1[TPL / 2];
+#pragma unroll
+            for (int i = 0; i < TPL / 2; ++i) {
+                h0[i] = perm2(yh[2 * i + 1], yh[2 * i], LO_HALVES);
+                h1[i] = perm2(yh[2 * i + 1], yh[2 * i], HI_HALVES);
+                l0[i] = perm2(yl[2 * i + 1], yl[2 * i], LO_HALVES);
+                l1[i] = perm2(yl[2 * i + 1], yl[2 * i], HI_HALVES);
+            }
+            if constexpr (TPL == 8) {
+                *reinterpret_cast<uint4*>(&sYt[buf][sc * LDY + tc]) = make_uint4(h0[0], h0[1], h0[2], h0[3]);
+                *reinterpret_cast<uint4*>(&sYt[buf][(sc + 1) * LDY + tc]) = make_uint4(h1[0], h1[1], h1[2], h1[3]);
+                *reinterpret_cast<uint4*>(&sYtl[buf][sc * LDY + tc]) = make_uint4(l0[0], l0[1], l0[2], l0[3]);
+                *reinterpret_cast<uint4*>(&sYtl[buf][(sc + 1) * LDY + tc]) = make_uint4(l1[0], l1[1], l1[2], l1[3]);
+            } else {
+                *reinterpret_cast<uint2*>(&sYt[buf][sc * LDY + tc]) = make_uint2(h0[0], h0[1]);
+                *reinterpret_cast<uint2*>(&sYt[buf][(sc + 1) * LDY + tc]) = make_uint2(h1[0], h1[1]);
+                *reinterpret_cast<uint2*>(&sYtl[buf][sc * LDY + tc]) = make_uint2(l0[0], l0[1]);
+                *reinterpret_cast<uint2*>(&sYtl[buf][(sc + 1) * LDY + tc]) = make_uint2(l1[0], l1[1]);
+            }
         }
     };
 
@@ -718,15 +755,30 @@ __global__ __launch_bounds__(PF_THREADS) void chunk_fwd_kernel(PrefillParams p) 
                 }
                 wave_lds_sync();
                 invert16(sL + 16 * LDM + 16, Tb + 16 * LDM + 16, lane);
-            } else if (role == 2) {
-                // -L10 (beta-scaled) goes where the consumers read it
-                const f32x4 l10 = block(X, X, 16, sY, sY, 0, false);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Tb[(16 + g * 4 + r) * LDM + ln] = -pbp[1][r] * l10[r];
-                store_m(Mb, block(QX, sQXl, 16, sY, sYl, 0, true), 16, 0, false);
             } else {
-                store_m(Mb, block(QX, sQXl, 16, sY, sYl, 16, true), 16, 16, true);
-                store_m(Mb, block(QX, sQXl, 0, sY, sYl, 0, true), 0, 0, true);
+                // -L10 (beta-scaled) goes where the consumers read it
+                auto l10 = [&]() {
+                    const f32x4 v = block(X, X, 16, sY, sY, 0, false);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Tb[(16 + g * 4 + r) * LDM + ln] = -pbp[1][r] * v[r];
+                };
+                auto m10 = [&]() { store_m(Mb, block(QX, sQXl, 16, sY, sYl, 0, true), 16, 0, false); };
+                auto m11 = [&]() { store_m(Mb, block(QX, sQXl, 16, sY, sYl, 16, true), 16, 16, true); };
+                auto m00 = [&]() { store_m(Mb, block(QX, sQXl, 0, sY, sYl, 0, true), 0, 0, true); };
+                if constexpr (NPROD == 8) {
+                    if (role == 2) l10();
+                    else if (role == 3) m10();
+                    else if (role == 4) m11();
+                    else if (role == 5) m00();
+                } else {
+                    if (role == 2) {
+                        l10();
+                        m10();
+                    } else {
+                        m11();
+                        m00();
+                    }
+                }
             }
             __syncthreads();
 #pragma unroll
@@ -772,17 +824,19 @@ hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, b
         p.order = nullptr;
     }
     const int64_t groups = ((int64_t)p.n_units + 7) / 8;
-    dim3 grid((unsigned)(groups * 8 * p.n_slices)), block(PF_THREADS);
+    // 16 columns per consumer wave (two slices per head) pairs with eight
+    // producer waves, 32 columns (one slice) with four.
+    dim3 grid((unsigned)(groups * 8 * p.n_slices));
     if (bf16_in) {
         if (wcols == 32)
-            hipLaunchKernelGGL((chunk_fwd_kernel<__bf16, 32>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((chunk_fwd_kernel<__bf16, 32, 4>), grid, dim3(512), 0, stream, p);
         else
-            hipLaunchKernelGGL((chunk_fwd_kernel<__bf16, 16>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((chunk_fwd_kernel<__bf16, 16, 8>), grid, dim3(768), 0, stream, p);
     } else {
         if (wcols == 32)
-            hipLaunchKernelGGL((chunk_fwd_kernel<float, 32>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((chunk_fwd_kernel<float, 32, 4>), grid, dim3(512), 0, stream, p);
         else
-            hipLaunchKernelGGL((chunk_fwd_kernel<float, 16>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((chunk_fwd_kernel<float, 16, 8>), grid, dim3(768), 0, stream, p);
     }
     return hipGetLastError();
 }
