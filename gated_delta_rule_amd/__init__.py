@@ -98,7 +98,8 @@ def chunk_fwd_workspace_bytes(n_seqs: int, T: int, H: int, varlen: bool) -> int:
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
-              output_final_state: bool = True, o=None, S_T=None, workspace=None):
+              output_final_state: bool = True, o=None, S_T=None, workspace=None,
+              sequence_parallel: bool = True):
     """Chunkwise KDA prefill (see kda_chunk_fwd in include/kda.h).
 
     Equal-length batch: q, k, log_alpha [B, T, H, 128]; v [B, T, H, 128];
@@ -106,6 +107,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
     [T_total, H, ...] (a leading axis of 1 is allowed) and cu_seqlens int32
     [N+1] on the device.  S0: [N, H, 128, 128] float32 or None.
     Returns (o float32 like v, S_T [N, H, 128, 128] float32 or None).
+    sequence_parallel=False keeps equal-length batches on the sequential
+    path (no workspace is passed).
     """
     import torch
     lib = load_library()
@@ -144,6 +147,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
         _check(S_T, "S_T", torch.float32, dev)
     ws_bytes = int(lib.kda_chunk_fwd_workspace_bytes(n_seqs, T, H, dk, dv,
                                                      int(cu_seqlens is not None)))
+    if cu_seqlens is None and not sequence_parallel:
+        ws_bytes, workspace = 0, None
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream

@@ -13,6 +13,35 @@ namespace {
 constexpr int64_t kHeadDim = 128;
 constexpr int32_t kOrderMax = 4096;       // sequences sorted longest-first up to this count
 constexpr int64_t kMaxGrid = 0x7fffffffLL;
+constexpr int64_t kChunk = 32;             // tokens per chunk inside the kernel
+constexpr int64_t kMinSegTokens = 2048;    // shortest segment worth a separate chain
+constexpr int64_t kStateBytes = kHeadDim * kHeadDim * 4;
+constexpr int64_t kFillUnits = 256;        // compute units to cover
+
+// Sequence-parallel split of an equal-length batch: segments per sequence
+// (1 = none) and tokens per segment (a multiple of the chunk).  Used when
+// the (sequence, head) chains, at two workgroups each, cover at most half
+// the compute units.
+struct Split {
+    int32_t P;
+    int64_t L;
+};
+
+Split split_for(int64_t n_seqs, int64_t T, int64_t H) {
+    Split sp{1, T};
+    const int64_t units = n_seqs * H;
+    if (units <= 0 || T <= 0 || units * 4 > kFillUnits) return sp;
+    int64_t P = kFillUnits / (units * 2);
+    const int64_t by_len = T / kMinSegTokens;
+    if (P > by_len) P = by_len;
+    if (P < 2) return sp;
+    int64_t L = (T + P - 1) / P;
+    L = (L + kChunk - 1) / kChunk * kChunk;
+    sp.P = (int32_t)((T + L - 1) / L);
+    sp.L = L;
+    if (sp.P < 2) sp = Split{1, T};
+    return sp;
+}
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -62,11 +91,12 @@ const char* kda_status_str(int status) {
 
 size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H, int32_t dk,
                                      int32_t dv, int varlen) {
-    (void)T;
-    (void)H;
-    if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim) return 0;
-    if (!varlen || n_seqs > kOrderMax) return 0;
-    return (size_t)n_seqs * sizeof(int32_t);
+    if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim || H < 1 || T < 0) return 0;
+    if (varlen) return n_seqs > kOrderMax ? 0 : (size_t)n_seqs * sizeof(int32_t);
+    const Split sp = split_for(n_seqs, T, H);
+    if (sp.P < 2) return 0;
+    // transitions, local final states and incoming states of every segment
+    return (size_t)3 * n_seqs * sp.P * H * kStateBytes;
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
@@ -122,10 +152,19 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
         if (overlaps(rst, r)) return KDA_ERR_ALIASING;
     if (S0 && S_T && S0 != (const float*)S_T && overlaps(rs0, rst)) return KDA_ERR_ALIASING;
 
+    // Packed batches need the order workspace; equal-length batches use the
+    // sequence-parallel path only when the caller provides its workspace.
     const size_t need = kda_chunk_fwd_workspace_bytes(n_seqs, T, H, dk, dv, varlen ? 1 : 0);
-    if (need > 0) {
+    bool use_ws = false;
+    if (varlen && need > 0) {
         if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
-        if (!aligned(workspace, 4)) return KDA_ERR_MISALIGNED;
+        if (!aligned(workspace, 16)) return KDA_ERR_MISALIGNED;
+        use_ws = true;
+    } else if (!varlen && need > 0 && workspace && workspace_bytes >= need) {
+        if (!aligned(workspace, 16)) return KDA_ERR_MISALIGNED;
+        use_ws = true;
+    }
+    if (use_ws) {
         const Range rw = span(workspace, (int64_t)need);
         const Range all[] = {rq, rk, rv, rla, rb, rs0, rcu, ro, rst};
         for (const Range& r : all)
@@ -140,6 +179,9 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     if (grid > kMaxGrid) return KDA_ERR_TOO_LARGE;
 
     kda::PrefillParams p;
+    p.seg_len = T;
+    p.seg_per_seq = 1;
+    p.s0_identity = 0;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -147,7 +189,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     p.beta = beta;
     p.S0 = S0;
     p.cu = cu_seqlens;
-    p.order = need > 0 ? (const int32_t*)workspace : nullptr;
+    p.order = varlen && use_ws ? (const int32_t*)workspace : nullptr;
     p.o = o;
     p.S_T = S_T;
     p.T = T;
@@ -155,7 +197,50 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     p.H = H;
     p.n_slices = n_slices;
     p.n_units = (int32_t)units;
-    hipError_t e = kda::launch_chunk_fwd(p, in_dtype == KDA_BF16, wcols, need > 0, stream);
+    const bool bf16_in = in_dtype == KDA_BF16;
+    if (varlen || !use_ws) {
+        hipError_t e = kda::launch_chunk_fwd(p, bf16_in, wcols, varlen && use_ws, stream);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+
+    // Sequence-parallel path (equal lengths, few chains): every sequence is
+    // cut into P segments.  Pass 1 runs each segment from a zero state (its
+    // local final state) and from the identity with v = 0 (its transition);
+    // the merge chains them into each segment's incoming state and the
+    // final states; pass 2 reruns each segment from its incoming state and
+    // writes o.
+    const Split sp = split_for(n_seqs, T, H);
+    const int64_t chains = (int64_t)n_seqs * sp.P;
+    const int64_t cunits = chains * H;
+    float* wF = (float*)workspace;
+    float* wSl = wF + cunits * (kHeadDim * kHeadDim);
+    float* wSin = wSl + cunits * (kHeadDim * kHeadDim);
+    kda::PrefillParams ps = p;
+    ps.n_seqs = (int32_t)chains;
+    ps.n_units = (int32_t)cunits;
+    ps.n_slices = cunits < 256 ? 2 : 1;
+    ps.seg_len = sp.L;
+    ps.seg_per_seq = sp.P;
+    const int swcols = 128 / (4 * ps.n_slices);
+    if (((cunits + 7) / 8) * 8 * ps.n_slices > kMaxGrid) return KDA_ERR_TOO_LARGE;
+
+    kda::PrefillParams pa = ps;   // local final states
+    pa.S0 = nullptr;
+    pa.o = nullptr;
+    pa.S_T = wSl;
+    kda::PrefillParams pb = ps;   // transitions
+    pb.S0 = nullptr;
+    pb.o = nullptr;
+    pb.S_T = wF;
+    pb.s0_identity = 1;
+    kda::PrefillParams pc = ps;   // outputs from the true incoming states
+    pc.S0 = wSin;
+    pc.S_T = nullptr;
+    hipError_t e = kda::launch_chunk_fwd(pa, bf16_in, swcols, false, stream);
+    if (e == hipSuccess) e = kda::launch_chunk_fwd(pb, bf16_in, swcols, false, stream);
+    if (e == hipSuccess)
+        e = kda::launch_segment_merge(wF, wSl, S0, wSin, S_T, n_seqs, sp.P, H, stream);
+    if (e == hipSuccess) e = kda::launch_chunk_fwd(pc, bf16_in, swcols, false, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

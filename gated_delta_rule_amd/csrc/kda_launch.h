@@ -18,12 +18,26 @@ struct PrefillParams {
     float* o;
     float* S_T;
     int64_t T;              // tokens per sequence (equal lengths) or total (packed)
-    int32_t n_seqs, H, n_slices, n_units;
+    // Equal lengths only: each sequence is cut into seg_per_seq segments of
+    // seg_len tokens (the last one shorter), run as independent chains
+    // numbered b * seg_per_seq + r.  seg_per_seq = 1, seg_len = T: no split.
+    int64_t seg_len;
+    int32_t seg_per_seq;
+    // Transition pass: every chain starts from the identity state and reads
+    // v as zero, so its final state is the chain's linear map S_in -> S_out.
+    int32_t s0_identity;
+    int32_t n_seqs, H, n_slices, n_units;   // n_seqs counts chains (segments)
 };
 
 // Enqueue the prefill (and, when `sort`, the sequence-order pass first).
 hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, bool sort,
                             hipStream_t stream);
+
+// S_in[b, r] and S_T[b] of the segmented prefill: S_in[b, 0] = S0[b] (or 0),
+// S_in[b, r + 1] = F[b, r] S_in[b, r] + Sl[b, r]; S_T[b] = the state after
+// the last segment (skipped when S_T is null).  Arrays [B * P, H, 128, 128].
+hipError_t launch_segment_merge(const float* F, const float* Sl, const float* S0, float* S_in,
+                                float* S_T, int32_t B, int32_t P, int32_t H, hipStream_t stream);
 
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16_in,
                               const float* log_alpha, const float* beta, float* S,

@@ -228,8 +228,11 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
         t0 = a < 0 ? 0 : (a > Tt ? Tt : a);
         t1 = b < t0 ? t0 : (b > Tt ? Tt : b);
     } else {
-        t0 = (int64_t)n * Tt;
-        t1 = t0 + Tt;
+        const int64_t b = n / p.seg_per_seq, r = n - b * p.seg_per_seq;
+        const int64_t e = (b + 1) * Tt;
+        t0 = b * Tt + r * p.seg_len;
+        t0 = t0 < e ? t0 : e;
+        t1 = e - t0 > p.seg_len ? t0 + p.seg_len : e;
     }
     const int64_t nch = (t1 - t0 + CH - 1) / CH;
     const int H = p.H;
@@ -290,7 +293,8 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
     auto load_v = [&](int64_t cidx, float (&v)[2][NCT][4]) {
         const int64_t c = t0 + cidx * CH;
         const int nv = n_valid(c);
-        const auto rv = make_rsrc((const InT*)p.v + ((size_t)c * H + h) * DK, span_bytes(nv, ES));
+        const auto rv = make_rsrc((const InT*)p.v + ((size_t)c * H + h) * DK,
+                                  p.s0_identity ? 0 : span_bytes(nv, ES));
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -521,9 +525,11 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    S[it][ct][r] = p.S0 ? p.S0[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 +
-                                               ct * 16 + ln]
-                                        : 0.f;
+                    S[it][ct][r] = p.s0_identity
+                                       ? (it * 16 + g * 4 + r == col0 + ct * 16 + ln ? 1.f : 0.f)
+                                   : p.S0 ? p.S0[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 +
+                                                 ct * 16 + ln]
+                                          : 0.f;
         load_v(0, pv);
         load_beta(0, pb);
         __syncthreads();   // step 0: nothing to finish yet
@@ -649,42 +655,45 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
             __syncthreads();
             // ---------------------------------------------------- phase B
             const int64_t c0 = t0 + cidx * CH;
-            // O = Q+ S + M U; rows past the sequence end fall outside the store range.
-            const auto ro = make_rsrc(p.o + ((size_t)c0 * H + h) * DK, span_bytes(n_valid(c0), 4));
+            // O = Q+ S + M U (skipped when o is not wanted); rows past the
+            // sequence end fall outside the store range.
+            if (p.o) {
+                const auto ro = make_rsrc(p.o + ((size_t)c0 * H + h) * DK, span_bytes(n_valid(c0), 4));
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                Frag<F32> aM, aMl;
-                {
-                    const uint32_t* mr = sM[buf] + (tb * 16 + ln) * LDM + g * 4;
-                    const uint4 m0 = *reinterpret_cast<const uint4*>(mr);
-                    const uint4 m1 = *reinterpret_cast<const uint4*>(mr + 16);
-                    if constexpr (F32) {
-                        aM.v[0] = __uint_as_float(m0.x); aM.v[1] = __uint_as_float(m0.y);
-                        aM.v[2] = __uint_as_float(m0.z); aM.v[3] = __uint_as_float(m0.w);
-                        aM.v[4] = __uint_as_float(m1.x); aM.v[5] = __uint_as_float(m1.y);
-                        aM.v[6] = __uint_as_float(m1.z); aM.v[7] = __uint_as_float(m1.w);
-                    } else {
-                        uint4 hv, lv;
-                        hv.x = perm2(m0.y, m0.x, LO_HALVES); hv.y = perm2(m0.w, m0.z, LO_HALVES);
-                        hv.z = perm2(m1.y, m1.x, LO_HALVES); hv.w = perm2(m1.w, m1.z, LO_HALVES);
-                        lv.x = perm2(m0.y, m0.x, HI_HALVES); lv.y = perm2(m0.w, m0.z, HI_HALVES);
-                        lv.z = perm2(m1.y, m1.x, HI_HALVES); lv.w = perm2(m1.w, m1.z, HI_HALVES);
-                        aM.v = __builtin_bit_cast(bf16x8, hv);
-                        aMl.v = __builtin_bit_cast(bf16x8, lv);
+                for (int tb = 0; tb < 2; ++tb) {
+                    Frag<F32> aM, aMl;
+                    {
+                        const uint32_t* mr = sM[buf] + (tb * 16 + ln) * LDM + g * 4;
+                        const uint4 m0 = *reinterpret_cast<const uint4*>(mr);
+                        const uint4 m1 = *reinterpret_cast<const uint4*>(mr + 16);
+                        if constexpr (F32) {
+                            aM.v[0] = __uint_as_float(m0.x); aM.v[1] = __uint_as_float(m0.y);
+                            aM.v[2] = __uint_as_float(m0.z); aM.v[3] = __uint_as_float(m0.w);
+                            aM.v[4] = __uint_as_float(m1.x); aM.v[5] = __uint_as_float(m1.y);
+                            aM.v[6] = __uint_as_float(m1.z); aM.v[7] = __uint_as_float(m1.w);
+                        } else {
+                            uint4 hv, lv;
+                            hv.x = perm2(m0.y, m0.x, LO_HALVES); hv.y = perm2(m0.w, m0.z, LO_HALVES);
+                            hv.z = perm2(m1.y, m1.x, LO_HALVES); hv.w = perm2(m1.w, m1.z, LO_HALVES);
+                            lv.x = perm2(m0.y, m0.x, HI_HALVES); lv.y = perm2(m0.w, m0.z, HI_HALVES);
+                            lv.z = perm2(m1.y, m1.x, HI_HALVES); lv.w = perm2(m1.w, m1.z, HI_HALVES);
+                            aM.v = __builtin_bit_cast(bf16x8, hv);
+                            aMl.v = __builtin_bit_cast(bf16x8, lv);
+                        }
                     }
-                }
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    if constexpr (!F32) {
-                        mma(O[tb][ct], aMl, bUh[ct]);
-                        mma(O[tb][ct], aM, bUl[ct]);
-                    }
-                    mma(O[tb][ct], aM, bUh[ct]);
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        if constexpr (!F32) {
+                            mma(O[tb][ct], aMl, bUh[ct]);
+                            mma(O[tb][ct], aM, bUl[ct]);
+                        }
+                        mma(O[tb][ct], aM, bUh[ct]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int el = (tb * 16 + g * 4 + r) * rowel + col0 + ct * 16 + ln;
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[tb][ct][r]), ro,
-                                                              el * 4, 0, 0);
+                        for (int r = 0; r < 4; ++r) {
+                            const int el = (tb * 16 + g * 4 + r) * rowel + col0 + ct * 16 + ln;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[tb][ct][r]), ro,
+                                                                  el * 4, 0, 0);
+                        }
                     }
                 }
             }

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -74,18 +74,30 @@ int kda_abi_version(void);
 const char* kda_status_str(int status);
 
 /*
- * Workspace size in bytes that kda_chunk_fwd needs for these sizes (0 when
- * none is needed).  `varlen` != 0 when cu_seqlens will be passed.  The
- * varlen path keeps a longest-first order of the sequences in the workspace
- * (n_seqs int32).  Returns 0 for invalid sizes as well; kda_chunk_fwd then
- * reports the real error.
+ * Workspace size in bytes for kda_chunk_fwd with these sizes (0 when none
+ * is used).  `varlen` != 0 when cu_seqlens will be passed.
+ *   varlen: a longest-first order of the sequences (n_seqs int32); the
+ *       workspace is then required.
+ *   equal lengths: when n_seqs * H is small (at most 64 (sequence, head)
+ *       pairs) and T is long, the sequence-parallel path cuts every
+ *       sequence into P segments and needs 3 * n_seqs * P * H * 64 KiB
+ *       (each segment's transition, local final state and incoming state).
+ *       That workspace is optional: without it (NULL or smaller), the
+ *       sequential path runs instead, with the same result up to rounding.
+ * Returns 0 for invalid sizes as well; kda_chunk_fwd then reports the real
+ * error.
  */
 size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
                                      int32_t dk, int32_t dv, int varlen);
 
 /*
  * Chunkwise prefill: runs the recurrence over whole sequences and returns
- * every o_t and, optionally, each sequence's final state.  The chunkwise
+ * every o_t and, optionally, each sequence's final state.  With equal-length
+ * sequences and few (sequence, head) pairs, the sequence-parallel path
+ * (when its workspace is given) runs the segments of each sequence as
+ * independent chains, merges them through each segment's transition
+ * d_k x d_k matrix and reruns every segment from its true incoming state;
+ * "Kimi K3 技术报告解读" section 7.3 describes this within-GPU split.  The chunkwise
  * evaluation (cumulative in-chunk log-decay, k+ = k e^{g}, k- = k e^{-g},
  * the strictly lower-triangular A_tj = beta_t k+_t . k-_j solved by forward
  * substitution, O = Q+ S + Tril(Q+ K-^T) U and the state hand-off
@@ -108,9 +120,10 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  *         may be the same pointer as S0 (in-place carry); any other overlap
  *         with an input is rejected.
  *   o   : must not overlap any input or S_T.
- *   workspace: at least kda_chunk_fwd_workspace_bytes(...) bytes of device
- *         memory (may be NULL when that is 0); contents need no
- *         initialisation and are clobbered.
+ *   workspace: kda_chunk_fwd_workspace_bytes(...) bytes of device memory,
+ *         16-byte aligned, overlapping no other argument (required for
+ *         packed batches when that size is not 0, optional otherwise; see
+ *         above); contents need no initialisation and are clobbered.
  * Numerics: fp32 accumulation throughout; with KDA_BF16 inputs the matrix
  * products run on bf16 matrix cores with split (hi + lo) bf16 operands
  * where a single rounding would exceed 2e-3 relative error; with KDA_F32

@@ -61,6 +61,13 @@ def test_workspace_query(lib):
     assert ws(5000, 10 ** 6, 16, 128, 128, 1) == 0        # beyond the sorted-order limit
     assert ws(32, 1000, 96, 64, 128, 1) == 0              # invalid head size
     assert ws(-1, 1000, 96, 128, 128, 1) == 0
+    # equal lengths, few (sequence, head) pairs, long T: sequence-parallel
+    # path with P segments, 3 state-sized arrays per segment and head
+    assert ws(1, 1 << 20, 16, 128, 128, 0) == 3 * 8 * 16 * 65536      # P = 256 / (2 * 16)
+    assert ws(2, 6000, 3, 128, 128, 0) == 3 * 2 * 2 * 3 * 65536       # P limited by T / 2048
+    assert ws(1, 8192, 16, 128, 128, 0) == 3 * 4 * 16 * 65536        # P = 8192 / 2048
+    assert ws(1, 4095, 16, 128, 128, 0) == 0                           # too short to split
+    assert ws(1, 1 << 20, 65, 128, 128, 0) == 0                        # enough pairs already
 
 
 # Fake, never-dereferenced device addresses for validation-only calls.
@@ -106,6 +113,10 @@ def test_chunk_fwd_validation(lib):
     assert chunk(lib, cu=P["cu"], ws=None) == WS       # packed batch needs the order workspace
     assert chunk(lib, cu=P["cu"], ws=P["ws"], wsb=4) == WS
     assert chunk(lib, n=2 ** 31 - 1, T=2 ** 40) == LARGE
+    # equal lengths with a sequence-parallel workspace: checked like any other
+    seg = dict(n=1, T=8192, H=16, wsb=3 * 4 * 16 * 65536)
+    assert chunk(lib, ws=P["ws"] + 4, **seg) == ALIGN
+    assert chunk(lib, ws=P["o"] + 4096, **seg) == ALIAS
     assert chunk(lib, n=0) == OK                        # empty batch: nothing to do
     assert chunk(lib, n=3, T=0, q=None, k=None, v=None, la=None, b=None, o=None,
                  st=P["st"] + 2) == ALIGN               # state pointers still checked

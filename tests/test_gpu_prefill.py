@@ -160,6 +160,38 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+# ------------------------------------------------ sequence-parallel path
+# Equal-length batches with few (sequence, head) pairs and long sequences run
+# as independent segments merged through their transitions (the workspace
+# query reports the path: nonzero for equal lengths means it is taken).
+
+@pytest.mark.parametrize("T,H,B,s0,dtype", [(6000, 3, 2, 0.02, "bf16"),   # 2 segments, ragged
+                                            (8192, 4, 1, 0.0, "bf16"),    # 4 segments
+                                            (5000, 2, 1, 0.02, "f32")])   # fp32 inputs
+def test_sequence_parallel_matches_oracle(T, H, B, s0, dtype):
+    assert kda.chunk_fwd_workspace_bytes(B, T, H, varlen=False) > 0
+    w, arrs = small(T, H, B, s0, dtype=dtype, wid=0 if dtype == "f32" else 1)
+    check_full(w, arrs, tol=TOL_F32 if dtype == "f32" else TOL_BF16,
+               label=f"sequence-parallel {dtype} T={T} H={H} B={B} s0={s0}")
+
+
+def test_sequence_parallel_agrees_with_sequential_and_in_place():
+    w, arrs = small(6000, 3, 2, 0.02)
+    d = to_dev(arrs, w)
+    say("[prefill] sequence-parallel vs sequential")
+    o_p, s_p = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    o_s, s_s = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                             sequence_parallel=False)
+    S = d["S0"].clone()
+    o_i, _ = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S, S_T=S)
+    torch.cuda.synchronize()
+    eo = rel_err(o_p.cpu().numpy(), o_s.cpu().numpy())
+    es = rel_err(s_p.cpu().numpy(), s_s.cpu().numpy())
+    say(f"[prefill] parallel vs sequential: o {eo:.3e}  S_T {es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert torch.equal(o_i, o_p) and torch.equal(S, s_p)   # S_T may be S0
+
+
 def _sampled_check(w, heads, label, seqs=None, cols=None):
     say(f"[prefill] {label}: generating inputs on the device")
     d, cu = device_prefill_inputs(w)
@@ -209,5 +241,6 @@ def test_workload2_full_size_sampled_units():
 
 @pytest.mark.timeout(900)
 def test_workload3_full_size_sampled_columns():
-    """T=1,048,576, H=16: eight value columns of two heads, every token."""
+    """T=1,048,576, H=16: eight value columns of two heads, every token (the
+    sequence-parallel path: 8 segments per head)."""
     _sampled_check(W.workload(3), [0, 9], "workload 3 (T=1M H=16)", cols=(40, 48))
