@@ -8,14 +8,16 @@ calls raise; there is no fallback.
 
     o, S_T = chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None)
     o = decode_step(q, k, v, log_alpha, beta, S)       # S updated in place
+    o = recurrent_fwd(q, k, v, log_alpha, beta, S, replay=None, n_replay=None,
+                      commit=True)                     # up to 64 tokens per request
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "decode_step", "chunk_fwd_workspace_bytes", "library_path",
-           "load_library", "KDAError", "KDA_BF16", "KDA_F32", "HEAD_DIM"]
+__all__ = ["chunk_fwd", "decode_step", "recurrent_fwd", "chunk_fwd_workspace_bytes",
+           "library_path", "load_library", "KDAError", "KDA_BF16", "KDA_F32", "HEAD_DIM"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -55,6 +57,9 @@ def load_library():
     lib.kda_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, i32, i32, i32, i32,
                                     fp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, vp, vp, vp, fp, fp, ip,
+                                      fp, i32, i32, i32, i32, i32, i32, ctypes.c_int, fp, vp]
+    lib.kda_recurrent_fwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -191,4 +196,61 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None):
     rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(log_alpha), _ptr(beta),
                              _ptr(S), B, H, dk, dv, _ptr(o), ctypes.c_void_p(stream))
     _status(rc, "kda_decode_step")
+    return o
+
+
+def recurrent_fwd(q, k, v, log_alpha, beta, S, *, replay=None, n_replay=None, commit=True,
+                  o=None):
+    """Multi-token recurrent decode (see kda_recurrent_fwd in include/kda.h).
+
+    q, k, log_alpha [B, T, H, 128]; v [B, T, H, 128]; beta [B, T, H] (T <= 64);
+    S [B, H, 128, 128] float32, updated in place.  `replay` = (q, k, v,
+    log_alpha, beta) of Tr <= 64 tokens per request applied first without
+    outputs, `n_replay` int32 [B] (device) how many of them to apply (None:
+    all).  commit=False stores the state right after the replay.  Returns
+    o [B, T, H, 128] float32.
+    """
+    import torch
+    lib = load_library()
+    dev = S.device
+    _check(S, "S", torch.float32, dev)
+    if S.dim() != 4:
+        raise KDAError("S must be [B, H, 128, 128]")
+    B, H, dk, dv = S.shape
+
+    def tokens(group, label):
+        tq, tk, tv, tla, tb = group
+        for name, t in (("q", tq), ("k", tk), ("v", tv)):
+            _check(t, f"{label} {name}", tq.dtype, dev)
+        _check(tla, f"{label} log_alpha", torch.float32, dev)
+        _check(tb, f"{label} beta", torch.float32, dev)
+        if tq.dim() != 4 or tq.shape[0] != B or tq.shape[2] != H or tq.shape[3] != dk:
+            raise KDAError(f"{label} q must be [B, T, H, 128] matching S")
+        if tk.shape != tq.shape or tla.shape != tq.shape or tv.shape[:-1] != tq.shape[:-1] \
+                or tb.shape != tq.shape[:-1]:
+            raise KDAError(f"{label} q/k/v/log_alpha/beta shapes disagree")
+        return tq.shape[1]
+
+    T = tokens((q, k, v, log_alpha, beta), "new")
+    dt = _in_dtype(q)
+    Tr, rq, rk, rv, rla, rb = 0, None, None, None, None, None
+    if replay is not None:
+        rq, rk, rv, rla, rb = replay
+        Tr = tokens(replay, "replay")
+        if rq.dtype != q.dtype:
+            raise KDAError("replay and new tokens must share a dtype")
+    if n_replay is not None:
+        _check(n_replay, "n_replay", torch.int32, dev)
+        if n_replay.numel() != B:
+            raise KDAError("n_replay must have one entry per request")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(o, "o", torch.float32, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(log_alpha), _ptr(beta),
+                               _ptr(rq), _ptr(rk), _ptr(rv), _ptr(rla), _ptr(rb),
+                               _ptr(n_replay), _ptr(S), B, T, Tr, H, dk, dv, int(bool(commit)),
+                               _ptr(o), ctypes.c_void_p(stream))
+    _status(rc, "kda_recurrent_fwd")
     return o

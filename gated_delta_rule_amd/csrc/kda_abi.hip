@@ -17,6 +17,7 @@ constexpr int64_t kChunk = 32;             // tokens per chunk inside the kernel
 constexpr int64_t kMinSegTokens = 2048;    // shortest segment worth a separate chain
 constexpr int64_t kStateBytes = kHeadDim * kHeadDim * 4;
 constexpr int64_t kFillUnits = 256;        // compute units to cover
+constexpr int32_t kMaxRecurrent = 64;      // tokens per request on the recurrent path
 
 // Sequence-parallel split of an equal-length batch: segments per sequence
 // (1 = none) and tokens per segment (a multiple of the chunk).  Used when
@@ -267,6 +268,51 @@ int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,
     if (overlaps(ro, rs)) return KDA_ERR_ALIASING;
     hipError_t e = kda::launch_decode_step(q, k, v, in_dtype == KDA_BF16, log_alpha, beta, S,
                                            states, o, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                      const float* log_alpha, const float* beta, const void* rq,
+                      const void* rk, const void* rv, const float* rlog_alpha,
+                      const float* rbeta, const int32_t* n_replay, float* S, int32_t B,
+                      int32_t T, int32_t Tr, int32_t H, int32_t dk, int32_t dv, int commit,
+                      float* o, hipStream_t stream) {
+    if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
+    if (dk != kHeadDim || dv != kHeadDim || H < 1 || B < 0 || T < 0 || T > kMaxRecurrent ||
+        Tr < 0 || Tr > kMaxRecurrent)
+        return KDA_ERR_BAD_SHAPE;
+    if (B == 0) return KDA_OK;
+    const int64_t states = (int64_t)B * H;
+    if (states > kMaxGrid) return KDA_ERR_TOO_LARGE;
+    if (!S) return KDA_ERR_NULL_POINTER;
+    if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    if (Tr > 0 && (!rq || !rk || !rv || !rlog_alpha || !rbeta)) return KDA_ERR_NULL_POINTER;
+    if (!aligned(S, 16)) return KDA_ERR_MISALIGNED;
+    if (T > 0 && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+                  !aligned(log_alpha, 16) || !aligned(o, 16) || !aligned(beta, 4)))
+        return KDA_ERR_MISALIGNED;
+    if (Tr > 0 && (!aligned(rq, 16) || !aligned(rk, 16) || !aligned(rv, 16) ||
+                   !aligned(rlog_alpha, 16) || !aligned(rbeta, 4)))
+        return KDA_ERR_MISALIGNED;
+    if (n_replay && !aligned(n_replay, 4)) return KDA_ERR_MISALIGNED;
+    const int64_t es = elem_size(in_dtype);
+    const int64_t e_new = states * T * kHeadDim, e_rep = states * Tr * kHeadDim;
+    const Range rs = span(S, states * kHeadDim * kHeadDim * 4);
+    const Range ro = span(o, T > 0 ? e_new * 4 : 0);
+    const Range ins[] = {span(q, T > 0 ? e_new * es : 0), span(k, T > 0 ? e_new * es : 0),
+                         span(v, T > 0 ? e_new * es : 0), span(log_alpha, T > 0 ? e_new * 4 : 0),
+                         span(beta, T > 0 ? states * T * 4 : 0),
+                         span(rq, Tr > 0 ? e_rep * es : 0), span(rk, Tr > 0 ? e_rep * es : 0),
+                         span(rv, Tr > 0 ? e_rep * es : 0),
+                         span(rlog_alpha, Tr > 0 ? e_rep * 4 : 0),
+                         span(rbeta, Tr > 0 ? states * Tr * 4 : 0),
+                         span(n_replay, Tr > 0 && n_replay ? (int64_t)B * 4 : 0)};
+    for (const Range& r : ins)
+        if (overlaps(ro, r) || overlaps(rs, r)) return KDA_ERR_ALIASING;
+    if (overlaps(ro, rs)) return KDA_ERR_ALIASING;
+    hipError_t e = kda::launch_recurrent(q, k, v, in_dtype == KDA_BF16, log_alpha, beta, rq, rk,
+                                         rv, rlog_alpha, rbeta, Tr > 0 ? n_replay : nullptr, S,
+                                         states, H, T, Tr, commit ? 1 : 0, o, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -39,6 +39,16 @@ hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, b
 hipError_t launch_segment_merge(const float* F, const float* Sl, const float* S0, float* S_in,
                                 float* S_T, int32_t B, int32_t P, int32_t H, hipStream_t stream);
 
+// Multi-token recurrent decode: per state, apply the first n_replay[b]
+// (NULL: all Tr) replay tokens, then T tokens with outputs; the state is
+// stored after the replay (commit = 0) or after everything (commit = 1).
+hipError_t launch_recurrent(const void* q, const void* k, const void* v, bool bf16_in,
+                            const float* log_alpha, const float* beta, const void* rq,
+                            const void* rk, const void* rv, const float* rlog_alpha,
+                            const float* rbeta, const int32_t* n_replay, float* S,
+                            int64_t n_states, int32_t H, int32_t T, int32_t Tr, int32_t commit,
+                            float* o, hipStream_t stream);
+
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16_in,
                               const float* log_alpha, const float* beta, float* S,
                               int64_t n_states, float* o, hipStream_t stream);

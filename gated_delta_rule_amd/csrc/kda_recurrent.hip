@@ -1,0 +1,210 @@
+// Multi-token recurrent decode with on-chip replay (gfx950).
+//
+// Decode with a few tokens per request runs the recurrence token by token
+// ("把注意力换成一块「会遗忘的内存」" section "层的实现:低秩门控与两条执行路径":
+// sequences of up to 64 tokens take the fused recurrent path, where the
+// fixed-size state makes the token loop the fastest form).  For speculative
+// decoding, "Kimi K3 技术报告解读" section 9 keeps only the draft tokens'
+// inputs and rebuilds the accepted tokens' state on chip, with verification
+// and write-back in one kernel.  Both are this kernel: per (request, head)
+// the state is loaded once, the first n_replay[b] replay tokens are applied
+// (state only), then T tokens are applied with their outputs, and the state
+// is stored either after the replay (commit = 0: the T drafts are verified
+// but not committed) or after all tokens (commit = 1).
+//
+// Each token is the three-step update of "Kimi K3 核心算子拆解" section 2.3
+// read after the update, in the single-pass form
+//   u = beta (v - x),  x = k^T Diag(a) S,  o = y + (q . k) u,  y = q^T Diag(a) S,
+//   S <- Diag(a) S + k u^T.
+//
+// Work decomposition: one 1024-thread workgroup per state; wave w owns value
+// columns 8w..8w+7 for all 128 key rows, lane l holding column 8w + (l & 7)
+// of rows (l >> 3) + 8i, i < 16.  The sums over key rows then stay inside
+// the wave (three cross-lane butterflies, no LDS and no barrier per token);
+// waves only share the token data, staged in LDS 16 tokens at a time.  The
+// state moves between HBM and registers through LDS so that both transfers
+// are 1 KB-contiguous per wave instruction.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+constexpr int RC_THREADS = 1024;
+constexpr int RC_TOK = 16;       // tokens staged per pass
+constexpr int RC_LDS = 136;      // LDS row stride of the staged state (floats)
+
+// x + (value of lane l ^ 8), within each 16-lane row (rotation by 8).
+__device__ __forceinline__ float add_xor8(float x) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return x + __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return x + __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+struct TokSrc {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* la;
+    const float* beta;
+    int32_t T;   // tokens per request in this stream
+};
+
+template <typename InT>
+__global__ __launch_bounds__(RC_THREADS) void recurrent_kernel(TokSrc rep, const int32_t* n_replay,
+                                                               TokSrc out, float* S, float* o,
+                                                               int32_t H, int32_t commit) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = lane & 7, rg = lane >> 3;
+    const int col = wave * 8 + c;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = (int)(bh - b * H);
+
+    // One LDS area: the staged state while it moves to or from HBM, the token
+    // data in between (barriers separate the two uses).  Token data: k, q and
+    // the decay factors permuted so that lane group rg reads its rows
+    // rg + 8i as 16 consecutive floats.
+    __shared__ __attribute__((aligned(16))) float smem[128 * RC_LDS];
+    float* sS = smem;
+    float (*sK)[128] = reinterpret_cast<float (*)[128]>(smem);
+    float (*sQ)[128] = reinterpret_cast<float (*)[128]>(smem + RC_TOK * 128);
+    float (*sA)[128] = reinterpret_cast<float (*)[128]>(smem + 2 * RC_TOK * 128);
+    float (*sV)[128] = reinterpret_cast<float (*)[128]>(smem + 3 * RC_TOK * 128);
+    float* sB = smem + 4 * RC_TOK * 128;
+    float* sQK = sB + RC_TOK;
+
+    float4* Sg = reinterpret_cast<float4*>(S + bh * (128 * 128));
+    // state: HBM -> LDS (1 KB per wave instruction) -> registers
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + RC_THREADS * j;
+        const float4 x = Sg[e];
+        *reinterpret_cast<float4*>(&sS[(e >> 5) * RC_LDS + 4 * (e & 31)]) = x;
+    }
+    __syncthreads();
+    float s[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = sS[(rg + 8 * i) * RC_LDS + col];
+
+    auto store_state = [&]() {
+        __syncthreads();   // every lane is done reading sS
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sS[(rg + 8 * i) * RC_LDS + col] = s[i];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = tid + RC_THREADS * j;
+            Sg[e] = *reinterpret_cast<const float4*>(&sS[(e >> 5) * RC_LDS + 4 * (e & 31)]);
+        }
+    };
+
+    // Run n tokens of one stream; outputs when `emit`.
+    auto run = [&](const TokSrc& src, int n, bool emit) {
+        for (int t0 = 0; t0 < n; t0 += RC_TOK) {
+            const int nt = n - t0 < RC_TOK ? n - t0 : RC_TOK;
+            __syncthreads();   // previous tokens consumed
+            // stage nt tokens: thread (token tt = tid >> 6, channel pair) -- one wave per token
+            if (wave < nt) {
+                const size_t row = ((size_t)b * src.T + t0 + wave) * H + h;
+                const InT* kp = (const InT*)src.k + row * 128;
+                const InT* qp = (const InT*)src.q + row * 128;
+                const InT* vp = (const InT*)src.v + row * 128;
+                const float* lp = src.la + row * 128;
+                float qk = 0.f;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int ch = lane + 64 * half;
+                    const float kk = to_f32(kp[ch]), qq = to_f32(qp[ch]);
+                    const int slot = (ch & 7) * 16 + (ch >> 3);   // row ch = rg + 8 i
+                    sK[wave][slot] = kk;
+                    sQ[wave][slot] = qq;
+                    sA[wave][slot] = __expf(lp[ch]);
+                    sV[wave][ch] = to_f32(vp[ch]);
+                    qk += qq * kk;
+                }
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) qk += __shfl_xor(qk, off);
+                if (lane == 0) {
+                    sQK[wave] = qk;
+                    sB[wave] = src.beta[row];
+                }
+            }
+            __syncthreads();
+            for (int tt = 0; tt < nt; ++tt) {
+                const float4* k4 = reinterpret_cast<const float4*>(&sK[tt][rg * 16]);
+                const float4* q4 = reinterpret_cast<const float4*>(&sQ[tt][rg * 16]);
+                const float4* a4 = reinterpret_cast<const float4*>(&sA[tt][rg * 16]);
+                float x = 0.f, y = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 kk = k4[i], qq = q4[i], aa = a4[i];
+                    s[4 * i] *= aa.x;
+                    s[4 * i + 1] *= aa.y;
+                    s[4 * i + 2] *= aa.z;
+                    s[4 * i + 3] *= aa.w;
+                    x = fmaf(kk.x, s[4 * i], x);
+                    x = fmaf(kk.y, s[4 * i + 1], x);
+                    x = fmaf(kk.z, s[4 * i + 2], x);
+                    x = fmaf(kk.w, s[4 * i + 3], x);
+                    y = fmaf(qq.x, s[4 * i], y);
+                    y = fmaf(qq.y, s[4 * i + 1], y);
+                    y = fmaf(qq.z, s[4 * i + 2], y);
+                    y = fmaf(qq.w, s[4 * i + 3], y);
+                }
+                x = add_xor32(add_xor16(add_xor8(x)));
+                y = add_xor32(add_xor16(add_xor8(y)));
+                const float u = sB[tt] * (sV[tt][col] - x);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 kk = k4[i];
+                    s[4 * i] = fmaf(kk.x, u, s[4 * i]);
+                    s[4 * i + 1] = fmaf(kk.y, u, s[4 * i + 1]);
+                    s[4 * i + 2] = fmaf(kk.z, u, s[4 * i + 2]);
+                    s[4 * i + 3] = fmaf(kk.w, u, s[4 * i + 3]);
+                }
+                if (emit && rg == 0) {
+                    const size_t row = ((size_t)b * src.T + t0 + tt) * H + h;
+                    o[row * 128 + col] = fmaf(sQK[tt], u, y);
+                }
+            }
+        }
+    };
+
+    int nr = 0;
+    if (rep.T > 0) {
+        nr = n_replay ? n_replay[b] : rep.T;
+        nr = nr < 0 ? 0 : (nr > rep.T ? rep.T : nr);
+        run(rep, nr, false);
+    }
+    if (!commit && nr > 0) store_state();
+    run(out, out.T, true);
+    if (commit) store_state();
+}
+
+hipError_t launch_recurrent(const void* q, const void* k, const void* v, bool bf16_in,
+                            const float* log_alpha, const float* beta, const void* rq,
+                            const void* rk, const void* rv, const float* rlog_alpha,
+                            const float* rbeta, const int32_t* n_replay, float* S,
+                            int64_t n_states, int32_t H, int32_t T, int32_t Tr, int32_t commit,
+                            float* o, hipStream_t stream) {
+    const TokSrc out{q, k, v, log_alpha, beta, T};
+    const TokSrc rep{rq, rk, rv, rlog_alpha, rbeta, Tr};
+    dim3 grid((unsigned)n_states), block(RC_THREADS);
+    if (bf16_in)
+        hipLaunchKernelGGL(recurrent_kernel<__bf16>, grid, block, 0, stream, rep, n_replay, out, S,
+                           o, H, commit);
+    else
+        hipLaunchKernelGGL(recurrent_kernel<float>, grid, block, 0, stream, rep, n_replay, out, S,
+                           o, H, commit);
+    return hipGetLastError();
+}
+
+}  // namespace kda

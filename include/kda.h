@@ -153,6 +153,38 @@ int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,
                     int32_t B, int32_t H, int32_t dk, int32_t dv, float* o,
                     hipStream_t stream);
 
+/*
+ * Multi-token recurrent decode with on-chip replay.  For each (request,
+ * head) the state S is loaded once; the first n_replay[b] of the Tr replay
+ * tokens are applied (state only, no outputs); then the T tokens are applied
+ * one by one, each emitting o_t = S_t^T q_t (read after its update); finally
+ * the state is written back either after the replay (commit == 0) or after
+ * all tokens (commit != 0).  Each token is the same step as kda_decode_step.
+ *   - decode of up to 64 tokens per request: Tr = 0, commit = 1 (the fused
+ *     recurrent path of "把注意力换成一块「会遗忘的内存」", section
+ *     "层的实现:低秩门控与两条执行路径");
+ *   - speculative decoding: the replay tokens are the previous step's drafts
+ *     with n_replay the accepted counts, the T tokens are the new drafts and
+ *     commit = 0, so the state holds exactly the accepted tokens and only the
+ *     drafts' inputs are kept between steps ("Kimi K3 技术报告解读"
+ *     section 9).
+ *
+ * Layout: q, k, log_alpha [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
+ *         rq, rk, rlog_alpha [B, Tr, H, dk]; rv [B, Tr, H, dv];
+ *         rbeta [B, Tr, H] (all may be NULL when Tr == 0);
+ *         n_replay int32 [B] on the device, each clamped into [0, Tr], or
+ *         NULL for all Tr;
+ *         S [B, H, dk, dv] float32, read and overwritten in place;
+ *         o [B, T, H, dv] float32 (must not overlap any input or S).
+ * Sizes: 0 <= T <= 64, 0 <= Tr <= 64.  Replay and new tokens share in_dtype.
+ */
+int kda_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                      const float* log_alpha, const float* beta, const void* rq,
+                      const void* rk, const void* rv, const float* rlog_alpha,
+                      const float* rbeta, const int32_t* n_replay, float* S, int32_t B,
+                      int32_t T, int32_t Tr, int32_t H, int32_t dk, int32_t dv, int commit,
+                      float* o, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,7 @@ def header_status_codes():
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert names == sorted(["kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_bytes",
-                            "kda_chunk_fwd", "kda_decode_step"])
+                            "kda_chunk_fwd", "kda_decode_step", "kda_recurrent_fwd"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -132,6 +132,38 @@ def test_decode_validation(lib):
     assert decode(lib, o=P["S"] if "S" in P else P["st"]) == ALIAS
     assert decode(lib, S=P["k"]) == ALIAS
     assert decode(lib, B=0) == OK
+
+
+def recurrent(lib, **kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], dtype=0, la=P["la"], b=P["b"], rq=None, rk=None,
+             rv=None, rla=None, rb=None, nr=None, S=P["st"], B=8, T=4, Tr=0, H=4, dk=128, dv=128,
+             commit=1, o=P["o"])
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.kda_recurrent_fwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), a["dtype"], vp(a["la"]),
+                                 vp(a["b"]), vp(a["rq"]), vp(a["rk"]), vp(a["rv"]), vp(a["rla"]),
+                                 vp(a["rb"]), vp(a["nr"]), vp(a["S"]), a["B"], a["T"], a["Tr"],
+                                 a["H"], a["dk"], a["dv"], a["commit"], vp(a["o"]), None)
+
+
+def test_recurrent_validation(lib):
+    assert recurrent(lib, dtype=3) == DTYPE
+    assert recurrent(lib, T=65) == SHAPE                 # at most 64 tokens per request
+    assert recurrent(lib, Tr=65) == SHAPE
+    assert recurrent(lib, T=-1) == SHAPE
+    assert recurrent(lib, dv=64) == SHAPE
+    assert recurrent(lib, S=None) == NULLP
+    assert recurrent(lib, o=None) == NULLP
+    assert recurrent(lib, Tr=3) == NULLP                 # replay tokens without their tensors
+    rep = dict(Tr=3, rq=P["cu"], rk=P["cu"] + 2 ** 26, rv=P["cu"] + 2 ** 27, rla=P["ws"],
+               rb=P["ws"] + 2 ** 27)
+    assert recurrent(lib, nr=P["s0"] + 2, **rep) == ALIGN
+    assert recurrent(lib, rq=P["cu"] + 8, **{k: v for k, v in rep.items() if k != "rq"}) == ALIGN
+    assert recurrent(lib, o=P["cu"], **rep) == ALIAS     # o on top of the replay q
+    assert recurrent(lib, S=P["k"]) == ALIAS
+    assert recurrent(lib, B=0) == OK
+    assert recurrent(lib, T=0, o=None, q=None, k=None, v=None, la=None, b=None,
+                     S=P["st"] + 8) == ALIGN             # state still checked with no tokens
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
