@@ -48,7 +48,105 @@ def parse():
                     help="run one path only (for profiler runs); prints no JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the repeated oracle runs")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the informational 1M-token prefill and multi-token decode runs")
     return ap.parse_args()
+
+
+def long_context(torch, kda, W, dev, reps=3):
+    """The T=1,048,576, H=16 prefill (for information): few (sequence, head)
+    pairs, so kda_chunk_fwd takes its sequence-parallel path.  Inputs are drawn
+    on the device with torch's seeded generator in the workload's
+    distributions (generating 1M tokens x 16 heads on the host would dominate
+    the run)."""
+    w = W.workload(3)
+    T, H = w.T, w.H
+    g = torch.Generator(device=dev).manual_seed(2026)
+    shp = (1, T, H, 128)
+    nrm = torch.nn.functional.normalize
+    q = nrm(torch.randn(shp, device=dev, generator=g), dim=-1).to(torch.bfloat16)
+    k = nrm(torch.randn(shp, device=dev, generator=g), dim=-1).to(torch.bfloat16)
+    v = torch.randn(shp, device=dev, generator=g).to(torch.bfloat16)
+    la = -5.0 * torch.sigmoid(torch.randn(shp, device=dev, generator=g))
+    b = torch.sigmoid(torch.randn((1, T, H), device=dev, generator=g))
+    o = torch.empty(shp, dtype=torch.float32, device=dev)
+    st = torch.empty((1, H, 128, 128), dtype=torch.float32, device=dev)
+    ws_bytes = kda.chunk_fwd_workspace_bytes(1, T, H, varlen=False)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, sp in (("sequence_parallel", True), ("sequential", False)):
+        n = reps if sp else 1
+        kda.chunk_fwd(q, k, v, la, b, None, None, o=o, S_T=st, workspace=ws if sp else None,
+                      sequence_parallel=sp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            kda.chunk_fwd(q, k, v, la, b, None, None, o=o, S_T=st, workspace=ws if sp else None,
+                          sequence_parallel=sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / n
+    del q, k, v, la, b, o, st, ws
+    torch.cuda.empty_cache()
+    ms = out["sequence_parallel"]
+    return {"workload": f"KDA prefill B=1 T={T} H={H} d=128 bf16, S0=0 (device-drawn inputs)",
+            "tokens_per_s": T / (ms * 1e-3), "ms": ms,
+            "sequential_path_ms": out["sequential"],
+            "path": "sequence-parallel: segments from zero and from the identity, merge, rerun",
+            "workspace_bytes": ws_bytes}
+
+
+def multi_token_decode(torch, kda, W, dev, T=8, reps=5):
+    """Recurrent decode of T tokens per request on the decode workload's state
+    (B=256, H=96; for information), and one speculative step: replay of the
+    accepted prefix of 4 earlier drafts, then 4 new drafts without commit.
+    Inputs are drawn on the device (torch's seeded generator, the workload's
+    distributions)."""
+    wd = W.workload(4)
+    B, H = wd.B, wd.H
+    g = torch.Generator(device=dev).manual_seed(7)
+    S = torch.from_numpy(W.decode_state(wd)).to(dev)
+    nrm = torch.nn.functional.normalize
+
+    def toks(n):
+        shp = (B, n, H, 128)
+        return (nrm(torch.randn(shp, device=dev, generator=g), dim=-1).to(torch.bfloat16),
+                nrm(torch.randn(shp, device=dev, generator=g), dim=-1).to(torch.bfloat16),
+                torch.randn(shp, device=dev, generator=g).to(torch.bfloat16),
+                -5.0 * torch.sigmoid(torch.randn(shp, device=dev, generator=g)),
+                torch.sigmoid(torch.randn((B, n, H), device=dev, generator=g)))
+
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    new = toks(T)
+    o = torch.empty((B, T, H, 128), dtype=torch.float32, device=dev)
+    ms = timed(lambda: kda.recurrent_fwd(*new, S, o=o))
+    rep, drafts = toks(4), toks(4)
+    n_acc = torch.randint(0, 5, (B,), device=dev, generator=g, dtype=torch.int32)
+    o4 = torch.empty((B, 4, H, 128), dtype=torch.float32, device=dev)
+    ms_spec = timed(lambda: kda.recurrent_fwd(*drafts, S, replay=rep, n_replay=n_acc,
+                                              commit=False, o=o4))
+    del S, new, rep, drafts, o, o4
+    torch.cuda.empty_cache()
+    return {"workload": f"KDA recurrent decode B={B} H={H} d=128, {T} tokens per request, "
+                        "fp32 state in place (device-drawn inputs)",
+            "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "ms_per_token": ms / T,
+            "speculative_step_ms": ms_spec,
+            "speculative_step": "replay of up to 4 accepted drafts + 4 new drafts, commit after replay"}
 
 
 def run_decode_only(args, torch, kda, W, dev):
@@ -175,6 +273,9 @@ def main():
     torch.cuda.empty_cache()
 
     # ------------------------------------------------- CPU oracle baseline
+    long_ctx = None if args.no_long else long_context(torch, kda, W, dev)
+    multi_tok = None if args.no_long else multi_token_decode(torch, kda, W, dev)
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -232,6 +333,8 @@ def main():
                          "algorithmic_flops": n_states * DECODE_FLOPS_PER_STATE},
         },
         "cpu_baseline": cpu,
+        "long_context_prefill": long_ctx,
+        "multi_token_decode": multi_tok,
         "wall_s_timed_prefill": t_wall,
     }
     print(json.dumps(out), flush=True)
