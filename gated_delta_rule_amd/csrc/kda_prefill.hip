@@ -537,17 +537,19 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
         for (int64_t cidx = 0; cidx < nch; ++cidx) {
             // ---------------------------------------------------- phase A
             const int buf = (int)(cidx & 1);
-            // S~ = e^{E0} S
-            const float* e0 = sVec[buf][0];
+            // S~ = e^{E0} S (for later chunks the previous update applied it)
+            if (cidx == 0) {
+                const float* e0 = sVec[buf][0];
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const float4 sc4 = *reinterpret_cast<const float4*>(e0 + it * 16 + g * 4);
+                for (int it = 0; it < 8; ++it) {
+                    const float4 sc4 = *reinterpret_cast<const float4*>(e0 + it * 16 + g * 4);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    S[it][ct][0] *= sc4.x;
-                    S[it][ct][1] *= sc4.y;
-                    S[it][ct][2] *= sc4.z;
-                    S[it][ct][3] *= sc4.w;
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        S[it][ct][0] *= sc4.x;
+                        S[it][ct][1] *= sc4.y;
+                        S[it][ct][2] *= sc4.z;
+                        S[it][ct][3] *= sc4.w;
+                    }
                 }
             }
             // K+ S -> R and Q+ S -> O
@@ -697,8 +699,12 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     }
                 }
             }
-            // S <- e^{E1 - E0} (S~ + Y^T U)
+            // S <- e^{E1 - E0} (S~ + Y^T U), and, when another chunk follows,
+            // already that chunk's S~ (its scan ran in this step's phase A):
+            // this phase has slack, the next one does not.
             const float* e1 = sVec[buf][1];
+            const bool more = cidx + 1 < nch;
+            const float* e0n = sVec[buf ^ 1][0];
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
                 Frag<F32> aY, aYl;
@@ -716,6 +722,21 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     S[it][ct][1] *= sc4.y;
                     S[it][ct][2] *= sc4.z;
                     S[it][ct][3] *= sc4.w;
+                }
+                // two separate scalings: their product alone can underflow
+                // (e^{-80} e^{-80}) where the scaled state does not; a select,
+                // not a branch, so the matrix-core chains stay interleaved
+                float4 n4 = *reinterpret_cast<const float4*>(e0n + it * 16 + g * 4);
+                n4.x = more ? n4.x : 1.f;
+                n4.y = more ? n4.y : 1.f;
+                n4.z = more ? n4.z : 1.f;
+                n4.w = more ? n4.w : 1.f;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    S[it][ct][0] *= n4.x;
+                    S[it][ct][1] *= n4.y;
+                    S[it][ct][2] *= n4.z;
+                    S[it][ct][3] *= n4.w;
                 }
             }
             __syncthreads();
