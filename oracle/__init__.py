@@ -9,7 +9,9 @@ written in ``kda_oracle.c``; this module builds it with gcc, loads it with
 ctypes and wraps it for numpy arrays.  ``reference.py`` holds small numpy
 restatements of the special cases the pages name (DeltaNet, gated DeltaNet,
 linear attention, the naive DPLR product, the unrolled product) that pin the
-oracle, and ``chunkwise.py`` holds the CPU chunkwise derivation.
+oracle, ``chunkwise.py`` holds the CPU chunkwise derivation, and ``layer.py``
+the steps on either side of the recurrence in a layer (short convolution with
+its cache, activations, norms, gates).
 """
 from __future__ import annotations
 
