@@ -10,13 +10,16 @@ calls raise; there is no fallback.
     o = decode_step(q, k, v, log_alpha, beta, S)       # S updated in place
     o = recurrent_fwd(q, k, v, log_alpha, beta, S, replay=None, n_replay=None,
                       commit=True)                     # up to 64 tokens per request
+    q, k, v, log_alpha, beta = prologue(q_raw, k_raw, v_raw, conv_w, a, b, conv_cache)
+    out = epilogue(o, g, w)                            # gated RMSNorm of the output
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "decode_step", "recurrent_fwd", "chunk_fwd_workspace_bytes",
+__all__ = ["chunk_fwd", "decode_step", "recurrent_fwd", "prologue", "epilogue",
+           "chunk_fwd_workspace_bytes",
            "library_path", "load_library", "KDAError", "KDA_BF16", "KDA_F32", "HEAD_DIM"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +63,11 @@ def load_library():
     lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, vp, vp, vp, fp, fp, ip,
                                       fp, i32, i32, i32, i32, i32, i32, ctypes.c_int, fp, vp]
     lib.kda_recurrent_fwd.restype = ctypes.c_int
+    lib.kda_prologue.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, fp, ip, i32, i64, i32, i32,
+                                 vp, vp, vp, fp, fp, vp]
+    lib.kda_prologue.restype = ctypes.c_int
+    lib.kda_epilogue.argtypes = [fp, fp, fp, i64, i32, i32, fp, vp]
+    lib.kda_epilogue.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -254,3 +262,72 @@ def recurrent_fwd(q, k, v, log_alpha, beta, S, *, replay=None, n_replay=None, co
                                _ptr(o), ctypes.c_void_p(stream))
     _status(rc, "kda_recurrent_fwd")
     return o
+
+
+def prologue(q_raw, k_raw, v_raw, conv_w, a, b, conv_cache=None, cu_seqlens=None):
+    """Layer prologue (see kda_prologue in include/kda.h): short convolution
+    (width 4, with the optional conv cache updated in place), SiLU, L2 norm of
+    q and k, log_alpha = -5 sigmoid(a), beta = sigmoid(b).
+
+    q_raw, k_raw, v_raw [B, T, H, 128] (or packed [T, H, 128] with
+    cu_seqlens); conv_w [3, H, 128, 4]; a like q_raw (float32); b [..., H];
+    conv_cache [N, 3, 3, H, 128] float32 or None.
+    Returns (q, k, v in q_raw's dtype, log_alpha float32, beta float32).
+    """
+    import torch
+    lib = load_library()
+    dev = q_raw.device
+    for name, t in (("q_raw", q_raw), ("k_raw", k_raw), ("v_raw", v_raw)):
+        _check(t, name, q_raw.dtype, dev)
+    for name, t in (("conv_w", conv_w), ("a", a), ("b", b)):
+        _check(t, name, torch.float32, dev)
+    dt = _in_dtype(q_raw)
+    H, dk = q_raw.shape[-2], q_raw.shape[-1]
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        n_seqs, T = cu_seqlens.numel() - 1, q_raw.numel() // (H * dk)
+    else:
+        if q_raw.dim() != 4:
+            raise KDAError("q_raw must be [B, T, H, 128] without cu_seqlens")
+        n_seqs, T = q_raw.shape[0], q_raw.shape[1]
+    if k_raw.shape != q_raw.shape or v_raw.shape != q_raw.shape or a.shape != q_raw.shape \
+            or b.shape != q_raw.shape[:-1] or tuple(conv_w.shape) != (3, H, dk, 4):
+        raise KDAError("prologue input shapes disagree")
+    if conv_cache is not None:
+        _check(conv_cache, "conv_cache", torch.float32, dev)
+        if tuple(conv_cache.shape) != (n_seqs, 3, 3, H, dk):
+            raise KDAError(f"conv_cache must be {(n_seqs, 3, 3, H, dk)}")
+    q, k, v = (torch.empty_like(q_raw) for _ in range(3))
+    log_alpha = torch.empty(q_raw.shape, dtype=torch.float32, device=dev)
+    beta = torch.empty(b.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v_raw), dt, _ptr(conv_w),
+                          _ptr(conv_cache), _ptr(a), _ptr(b), _ptr(cu_seqlens), n_seqs, T, H,
+                          dk, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                          ctypes.c_void_p(stream))
+    _status(rc, "kda_prologue")
+    return q, k, v, log_alpha, beta
+
+
+def epilogue(o, g, w, *, out=None):
+    """Layer epilogue (see kda_epilogue in include/kda.h): RMSNorm of each
+    head's 128 channels with weight w [128], times sigmoid(g).  o, g float32
+    [..., H, 128]; out may be o (in place)."""
+    import torch
+    lib = load_library()
+    dev = o.device
+    for name, t in (("o", o), ("g", g), ("w", w)):
+        _check(t, name, torch.float32, dev)
+    H, dv = o.shape[-2], o.shape[-1]
+    if g.shape != o.shape or tuple(w.shape) != (dv,):
+        raise KDAError("epilogue shapes disagree")
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _check(out, "out", torch.float32, dev)
+    rows = o.numel() // (H * dv)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_epilogue(_ptr(o), _ptr(g), _ptr(w), rows, H, dv, _ptr(out),
+                          ctypes.c_void_p(stream))
+    _status(rc, "kda_epilogue")
+    return out

@@ -316,4 +316,86 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_prologue(const void* q_raw, const void* k_raw, const void* v_raw, int in_dtype,
+                 const float* conv_w, float* conv_cache, const float* a, const float* b,
+                 const int32_t* cu_seqlens, int32_t n_seqs, int64_t T, int32_t H, int32_t dk,
+                 void* q, void* k, void* v, float* log_alpha, float* beta,
+                 hipStream_t stream) {
+    if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
+    if (dk != kHeadDim || H < 1 || n_seqs < 0 || T < 0) return KDA_ERR_BAD_SHAPE;
+    const bool varlen = cu_seqlens != nullptr;
+    int64_t rows = 0, elems = 0, hrows = 0;
+    if (varlen) rows = T;
+    else if (!mul_ok((int64_t)n_seqs, T, &rows)) return KDA_ERR_TOO_LARGE;
+    if (n_seqs == 0) return KDA_OK;
+    if (!mul_ok(rows, (int64_t)H, &hrows) || !mul_ok(hrows, kHeadDim, &elems) ||
+        elems > INT64_MAX / 8 || (hrows + 3) / 4 > kMaxGrid)
+        return KDA_ERR_TOO_LARGE;
+    const int64_t cache_elems = (int64_t)n_seqs * 9 * H * kHeadDim;
+    if (conv_cache && (cache_elems + 255) / 256 > kMaxGrid) return KDA_ERR_TOO_LARGE;
+    if (rows > 0 && (!q_raw || !k_raw || !v_raw || !conv_w || !a || !b || !q || !k || !v ||
+                     !log_alpha || !beta))
+        return KDA_ERR_NULL_POINTER;
+    if (rows > 0 && (!aligned(q_raw, 16) || !aligned(k_raw, 16) || !aligned(v_raw, 16) ||
+                     !aligned(conv_w, 16) || !aligned(a, 16) || !aligned(q, 16) ||
+                     !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) ||
+                     !aligned(b, 4) || !aligned(beta, 4)))
+        return KDA_ERR_MISALIGNED;
+    if ((conv_cache && !aligned(conv_cache, 16)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return KDA_ERR_MISALIGNED;
+    const int64_t es = elem_size(in_dtype);
+    const Range ins[] = {span(q_raw, elems * es), span(k_raw, elems * es), span(v_raw, elems * es),
+                         span(conv_w, rows > 0 ? 3 * (int64_t)H * kHeadDim * 16 : 0),
+                         span(a, elems * 4), span(b, hrows * 4),
+                         span(cu_seqlens, varlen ? ((int64_t)n_seqs + 1) * 4 : 0)};
+    const Range outs[] = {span(q, elems * es), span(k, elems * es), span(v, elems * es),
+                          span(log_alpha, elems * 4), span(beta, hrows * 4),
+                          span(conv_cache, conv_cache ? cache_elems * 4 : 0)};
+    for (int i = 0; i < 6; ++i) {
+        for (const Range& r : ins)
+            if (overlaps(outs[i], r)) return KDA_ERR_ALIASING;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(outs[i], outs[j])) return KDA_ERR_ALIASING;
+    }
+    kda::LayerParams p;
+    p.q_raw = q_raw;
+    p.k_raw = k_raw;
+    p.v_raw = v_raw;
+    p.conv_w = conv_w;
+    p.cache = conv_cache;
+    p.a = a;
+    p.b = b;
+    p.cu = cu_seqlens;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.log_alpha = log_alpha;
+    p.beta = beta;
+    p.rows = rows;
+    p.T = T;
+    p.n_seqs = n_seqs;
+    p.H = H;
+    hipError_t e = kda::launch_prologue(p, in_dtype == KDA_BF16, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, int32_t H,
+                 int32_t dv, float* out, hipStream_t stream) {
+    if (dv != kHeadDim || H < 1 || rows < 0) return KDA_ERR_BAD_SHAPE;
+    int64_t items = 0, elems = 0;
+    if (!mul_ok(rows, (int64_t)H, &items) || !mul_ok(items, kHeadDim, &elems) ||
+        elems > INT64_MAX / 8 || (items + 3) / 4 > kMaxGrid)
+        return KDA_ERR_TOO_LARGE;
+    if (items == 0) return KDA_OK;
+    if (!o || !g || !w || !out) return KDA_ERR_NULL_POINTER;
+    if (!aligned(o, 16) || !aligned(g, 16) || !aligned(w, 16) || !aligned(out, 16))
+        return KDA_ERR_MISALIGNED;
+    const Range ro = span(o, elems * 4), rg = span(g, elems * 4), rw = span(w, kHeadDim * 4);
+    const Range rout = span(out, elems * 4);
+    if (overlaps(rout, rg) || overlaps(rout, rw)) return KDA_ERR_ALIASING;
+    if (out != o && overlaps(rout, ro)) return KDA_ERR_ALIASING;
+    hipError_t e = kda::launch_epilogue(o, g, w, out, items, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -49,6 +49,30 @@ hipError_t launch_recurrent(const void* q, const void* k, const void* v, bool bf
                             int64_t n_states, int32_t H, int32_t T, int32_t Tr, int32_t commit,
                             float* o, hipStream_t stream);
 
+// Layer prologue / epilogue (equal lengths: cu == nullptr, rows = n_seqs * T;
+// packed: rows = T, cu [n_seqs + 1]).  cache [n_seqs, 3 tensors, 3 taps, H, 128]
+// or nullptr.
+struct LayerParams {
+    const void* q_raw;
+    const void* k_raw;
+    const void* v_raw;
+    const float* conv_w;    // [3, H, 128, 4]
+    float* cache;
+    const float* a;         // [rows, H, 128]
+    const float* b;         // [rows, H]
+    const int32_t* cu;
+    void* q;
+    void* k;
+    void* v;
+    float* log_alpha;
+    float* beta;
+    int64_t rows, T;
+    int32_t n_seqs, H;
+};
+hipError_t launch_prologue(const LayerParams& p, bool bf16_in, hipStream_t stream);
+hipError_t launch_epilogue(const float* o, const float* g, const float* w, float* out, int64_t items,
+                           hipStream_t stream);
+
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16_in,
                               const float* log_alpha, const float* beta, float* S,
                               int64_t n_states, float* o, hipStream_t stream);

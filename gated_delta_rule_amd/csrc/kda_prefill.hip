@@ -775,7 +775,11 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     sL[row * LDM + ln] = ln < row ? pbp[0][r] * l00[r] : 0.f;
                 }
                 wave_lds_sync();
+                // the inverse is this phase's longest dependency chain: let it
+                // issue ahead of the other waves on its SIMD
+                __builtin_amdgcn_s_setprio(3);
                 invert16(sL, Tb, lane);
+                __builtin_amdgcn_s_setprio(0);
             } else if (role == 1) {
                 const f32x4 l11 = block(X, X, 16, sY, sY, 16, false);
 #pragma unroll
@@ -784,7 +788,9 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     sL[(16 + row) * LDM + 16 + ln] = ln < row ? pbp[1][r] * l11[r] : 0.f;
                 }
                 wave_lds_sync();
+                __builtin_amdgcn_s_setprio(3);
                 invert16(sL + 16 * LDM + 16, Tb + 16 * LDM + 16, lane);
+                __builtin_amdgcn_s_setprio(0);
             } else {
                 // -L10 (beta-scaled) goes where the consumers read it
                 auto l10 = [&]() {

@@ -33,6 +33,9 @@ import numpy as np
 
 SEED_ROOT = 2026
 T_Q, T_K, T_V, T_LOGA, T_BETA, T_S0, T_LEN = range(7)
+# layer prologue / epilogue inputs
+T_RAW_Q, T_RAW_K, T_RAW_V, T_CONV_W, T_GATE_A, T_GATE_B, T_GATE_O, T_NORM_W, T_CACHE = range(7, 16)
+LAYER_WID = 100
 
 
 @dataclass(frozen=True)
@@ -214,3 +217,31 @@ def decode_state(w: Workload, heads=None) -> np.ndarray:
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, enumerate(heads)))
     return S
+
+
+def layer_inputs(lens, H: int, dtype: str = "bf16", seed: int = 0, with_cache: bool = True,
+                 d: int = 128) -> dict:
+    """Inputs of the layer prologue / epilogue for packed sequences of the
+    given lengths (synthetic weights; the pages give no trained values):
+      q_raw, k_raw, v_raw ~ N(0, 1)  [T, H, d]   (pre-convolution projections)
+      conv_w ~ N(0, 0.5^2)           [3, H, d, 4] (q, k, v; tap 0 on t-3)
+      a ~ N(0, 1) [T, H, d], b ~ N(0, 1) [T, H]   (decay / write pre-activations)
+      g ~ N(0, 1) [T, H, d], w_norm = 1 + 0.1 N(0, 1) [d]   (output gate, norm weight)
+      cache ~ N(0, 1) [N, 3, 3, H, d] or None     (previous raw inputs)
+    Raw inputs and cache are rounded to `dtype`; everything else is float32."""
+    lens = np.asarray(lens, np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, N = int(cu[-1]), len(lens)
+    key = (LAYER_WID + seed,)
+    raw = {n: _to_dtype(_rng(*key, t).standard_normal((T, H, d)), dtype)
+           for n, t in (("q_raw", T_RAW_Q), ("k_raw", T_RAW_K), ("v_raw", T_RAW_V))}
+    out = dict(raw)
+    out["conv_w"] = (0.5 * _rng(*key, T_CONV_W).standard_normal((3, H, d, 4))).astype(np.float32)
+    out["a"] = _rng(*key, T_GATE_A).standard_normal((T, H, d)).astype(np.float32)
+    out["b"] = _rng(*key, T_GATE_B).standard_normal((T, H)).astype(np.float32)
+    out["g"] = _rng(*key, T_GATE_O).standard_normal((T, H, d)).astype(np.float32)
+    out["w_norm"] = (1.0 + 0.1 * _rng(*key, T_NORM_W).standard_normal(d)).astype(np.float32)
+    out["cache"] = (_to_dtype(_rng(*key, T_CACHE).standard_normal((N, 3, 3, H, d)), dtype)
+                    if with_cache else None)
+    out["cu_seqlens"] = cu
+    return out

@@ -185,6 +185,45 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
                       int32_t T, int32_t Tr, int32_t H, int32_t dk, int32_t dv, int commit,
                       float* o, hipStream_t stream);
 
+/*
+ * Layer prologue: from the projected (pre-convolution) q, k, v and the gate
+ * pre-activations to the recurrence's inputs.  Per token t, head h, channel c:
+ *   y = sum_{j<4} w[j] x_{t-3+j}  (causal depthwise convolution of width 4;
+ *       x_{t<0} from the conv cache, or zeros when it is NULL)
+ *   q = l2norm(silu(y_q)), k = l2norm(silu(y_k)), v = silu(y_v),
+ *   log_alpha = -5 sigmoid(a), beta = sigmoid(b),
+ * silu(z) = z sigmoid(z), l2norm over the head's dk channels with eps 1e-6
+ * ("Kimi K3 四个核心模块的公式与真实张量流" section 1.2; "Kimi K3 核心算子拆解"
+ * section 2.6; "Kimi K3 技术报告解读" section 3.3).  The cache then holds each
+ * sequence's last three raw inputs (older entries shift in for sequences
+ * shorter than three tokens).
+ *
+ * Layout: q_raw, k_raw, q, k, a [rows, H, dk]; v_raw, v [rows, H, dk];
+ *   b, beta [rows, H]; log_alpha [rows, H, dk] float32, with rows = n_seqs * T
+ *   (equal lengths, cu_seqlens NULL) or T (packed, cu_seqlens [n_seqs + 1]
+ *   as in kda_chunk_fwd).  q_raw, k_raw, v_raw and q, k, v are in_dtype;
+ *   a, b float32.  conv_w float32 [3, H, dk, 4] (q, k, v; tap 0 applies to
+ *   t-3).  conv_cache float32 [n_seqs, 3, 3, H, dk] (tensor, tap t-3..t-1)
+ *   read and updated in place, or NULL.  Outputs must not overlap inputs
+ *   (the convolution reads neighbouring tokens).  dk = dv = 128.
+ */
+int kda_prologue(const void* q_raw, const void* k_raw, const void* v_raw, int in_dtype,
+                 const float* conv_w, float* conv_cache, const float* a, const float* b,
+                 const int32_t* cu_seqlens, int32_t n_seqs, int64_t T, int32_t H, int32_t dk,
+                 void* q, void* k, void* v, float* log_alpha, float* beta,
+                 hipStream_t stream);
+
+/*
+ * Layer epilogue: out = o / sqrt(mean_c o_c^2 + 1e-6) * w * sigmoid(g) over
+ * each (row, head)'s 128 channels: RMSNorm with a per-channel weight and the
+ * sigmoid output gate ("把注意力换成一块「会遗忘的内存」" section
+ * "层的实现:低秩门控与两条执行路径"; "Kimi K3 四个核心模块的公式与真实张量流"
+ * section 1.4).  o, g, out float32 [rows, H, dv]; w float32 [dv].  out may
+ * be o itself; no other overlap.
+ */
+int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, int32_t H,
+                 int32_t dv, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

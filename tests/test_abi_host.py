@@ -38,7 +38,8 @@ def header_status_codes():
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert names == sorted(["kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_bytes",
-                            "kda_chunk_fwd", "kda_decode_step", "kda_recurrent_fwd"])
+                            "kda_chunk_fwd", "kda_decode_step", "kda_recurrent_fwd",
+                            "kda_prologue", "kda_epilogue"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -164,6 +165,47 @@ def test_recurrent_validation(lib):
     assert recurrent(lib, B=0) == OK
     assert recurrent(lib, T=0, o=None, q=None, k=None, v=None, la=None, b=None,
                      S=P["st"] + 8) == ALIGN             # state still checked with no tokens
+
+
+def prologue(lib, **kw):
+    a = dict(qr=P["q"], kr=P["k"], vr=P["v"], dtype=0, w=P["ws"], cache=None, a=P["la"], b=P["b"],
+             cu=None, n=2, T=64, H=4, dk=128, q=P["o"], k=P["o"] + 2 ** 24, v=P["o"] + 2 ** 25,
+             la=P["st"], beta=P["st"] + 2 ** 25)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.kda_prologue(vp(a["qr"]), vp(a["kr"]), vp(a["vr"]), a["dtype"], vp(a["w"]),
+                            vp(a["cache"]), vp(a["a"]), vp(a["b"]), vp(a["cu"]), a["n"], a["T"],
+                            a["H"], a["dk"], vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["la"]),
+                            vp(a["beta"]), None)
+
+
+def epilogue(lib, **kw):
+    a = dict(o=P["o"], g=P["q"], w=P["b"], rows=64, H=4, dv=128, out=P["st"])
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.kda_epilogue(vp(a["o"]), vp(a["g"]), vp(a["w"]), a["rows"], a["H"], a["dv"],
+                            vp(a["out"]), None)
+
+
+def test_layer_validation(lib):
+    assert prologue(lib, dtype=5) == DTYPE
+    assert prologue(lib, dk=64) == SHAPE
+    assert prologue(lib, H=0) == SHAPE
+    assert prologue(lib, w=None) == NULLP
+    assert prologue(lib, beta=None) == NULLP
+    assert prologue(lib, a=P["la"] + 4) == ALIGN
+    assert prologue(lib, cache=P["s0"] + 4) == ALIGN
+    assert prologue(lib, q=P["q"]) == ALIAS               # in place is refused
+    assert prologue(lib, v=P["o"] + 2 ** 24) == ALIAS      # two outputs overlap
+    assert prologue(lib, cache=P["la"]) == ALIAS
+    assert prologue(lib, n=0) == OK
+    assert epilogue(lib, dv=64) == SHAPE
+    assert epilogue(lib, rows=-1) == SHAPE
+    assert epilogue(lib, g=None) == NULLP
+    assert epilogue(lib, out=P["st"] + 8) == ALIGN
+    assert epilogue(lib, out=P["q"]) == ALIAS              # out on top of g
+    assert epilogue(lib, out=P["o"] + 512) == ALIAS        # partial overlap with o
+    assert epilogue(lib, rows=0) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
