@@ -149,6 +149,51 @@ def multi_token_decode(torch, kda, W, dev, T=8, reps=5):
             "speculative_step": "replay of up to 4 accepted drafts + 4 new drafts, commit after replay"}
 
 
+def layer_steps(torch, kda, W, dev, reps=10):
+    """The layer prologue and epilogue around the headline prefill shape
+    (T=8192, H=96; for information): both stream HBM once, so they are
+    reported against the HBM roofline with their algorithmic bytes."""
+    w = W.workload(1)
+    T, H = w.T, w.H
+    g = torch.Generator(device=dev).manual_seed(11)
+    shp = (1, T, H, 128)
+    raw = [torch.randn(shp, device=dev, generator=g).to(torch.bfloat16) for _ in range(3)]
+    conv_w = 0.5 * torch.randn((3, H, 128, 4), device=dev, generator=g)
+    a = torch.randn(shp, device=dev, generator=g)
+    b = torch.randn((1, T, H), device=dev, generator=g)
+    cache = torch.randn((1, 3, 3, H, 128), device=dev, generator=g)
+    o = torch.randn(shp, device=dev, generator=g)
+    gate = torch.randn(shp, device=dev, generator=g)
+    wn = 1.0 + 0.1 * torch.randn(128, device=dev, generator=g)
+    out = torch.empty_like(o)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_p = timed(lambda: kda.prologue(*raw, conv_w, a, b, cache))
+    ms_e = timed(lambda: kda.epilogue(o, gate, wn, out=out))
+    th = T * H
+    bytes_p = th * (3 * 256 + 512 + 4 + 3 * 256 + 512 + 4)   # raw q,k,v + a + b in; q,k,v + log_alpha + beta out
+    bytes_e = th * 3 * 512                                     # o, g in; out
+    del raw, a, b, cache, o, gate, out
+    torch.cuda.empty_cache()
+    return {"workload": f"layer prologue / epilogue at T={T} H={H} d=128 (bf16 raw q,k,v; device-drawn)",
+            "prologue_ms": ms_p, "prologue_gbps": bytes_p / (ms_p * 1e-3) / 1e9,
+            "prologue_hbm_frac": bytes_p / (ms_p * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "epilogue_ms": ms_e, "epilogue_gbps": bytes_e / (ms_e * 1e-3) / 1e9,
+            "epilogue_hbm_frac": bytes_e / (ms_e * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "bytes_per_token_head": {"prologue": bytes_p // th, "epilogue": bytes_e // th}}
+
+
 def run_decode_only(args, torch, kda, W, dev):
     wd = W.workload(4)
     S = torch.from_numpy(W.decode_state(wd)).to(dev)
@@ -275,6 +320,7 @@ def main():
     # ------------------------------------------------- CPU oracle baseline
     long_ctx = None if args.no_long else long_context(torch, kda, W, dev)
     multi_tok = None if args.no_long else multi_token_decode(torch, kda, W, dev)
+    layer = None if args.no_long else layer_steps(torch, kda, W, dev)
 
     cpu = None
     if not args.no_cpu:
@@ -335,6 +381,7 @@ def main():
         "cpu_baseline": cpu,
         "long_context_prefill": long_ctx,
         "multi_token_decode": multi_tok,
+        "layer_prologue_epilogue": layer,
         "wall_s_timed_prefill": t_wall,
     }
     print(json.dumps(out), flush=True)

@@ -195,6 +195,25 @@ __device__ __forceinline__ void mma_k16(f32x4& acc, const float (&a)[4], const f
     }
 }
 
+// Sum over the 64 lanes of a wave, every lane receiving the total, without
+// an LDS round trip: quad butterflies and row rotations by DPP, then the
+// gfx950 16- and 32-lane swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_mov<0x124>(x);   // row_ror:4
+    x += dpp_mov<0x128>(x);   // row_ror:8
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x += __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x += __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+    return x;
+}
+
 // Make LDS writes of this wave visible to all of its lanes and keep the
 // compiler from moving LDS accesses across this point (one-wave barrier).
 __device__ __forceinline__ void wave_lds_sync() {

@@ -13,10 +13,10 @@
 // section 1.4): out = o / sqrt(mean o^2 + 1e-6) * w * sigmoid(g).
 //
 // All three kernels move each element once and do a few flops on it, so they
-// are HBM-bound: one wave per (token, head) row of 128 channels (two per
-// lane, 8-byte accesses), sums over the row by wave reduction; the previous
-// three tokens of the convolution come from the same rows that neighbouring
-// waves load, so they are served from cache.  The cache update runs as a
+// are HBM-bound: a wave owns one head's 128 channels (two per lane) of one
+// row (epilogue) or of two consecutive rows (prologue, with the conv
+// weights and the last three raw inputs kept in registers), sums over the
+// row by DPP wave reduction.  The cache update runs as a
 // separate launch after the prologue, so no wave reads a cache entry that
 // another already overwrote.
 #include "kda_device.h"
@@ -27,13 +27,11 @@ namespace kda {
 constexpr int LY_THREADS = 256;   // 4 rows per workgroup
 constexpr float LY_EPS = 1e-6f;
 
-__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+// sigmoid with the hardware reciprocal (about 1 ulp) instead of a correctly
+// rounded division
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
+__device__ __forceinline__ float wave_sum(float x) { return wave_sum_dpp(x); }
 
 template <typename T>
 __device__ __forceinline__ float2 load2(const T* p);
@@ -57,8 +55,8 @@ __device__ __forceinline__ void store2(__bf16* p, float2 v) {
 // Sequence of a token row and its position in that sequence.
 __device__ __forceinline__ void locate(int64_t row, const int32_t* cu, int32_t n_seqs, int64_t T,
                                        int64_t& n, int64_t& pos) {
-    if (!cu) {
-        n = row / T;
+    if (!cu) {   // rows < 2^31 (one workgroup column per row)
+        n = (int64_t)((uint32_t)row / (uint32_t)T);
         pos = row - n * T;
         return;
     }
@@ -72,53 +70,96 @@ __device__ __forceinline__ void locate(int64_t row, const int32_t* cu, int32_t n
     pos = row - cu[lo];
 }
 
+constexpr int LY_TOK = 2;   // consecutive token rows per wave in the prologue (1: 0.81 ms, 2: 0.67, 4: 0.68 at T=8192 H=96)
+
 template <typename InT>
 __global__ __launch_bounds__(LY_THREADS) void prologue_kernel(LayerParams p) {
+    // workgroup = (block of LY_TOK token rows, group of four heads, one per
+    // wave); a wave keeps its head's conv weights and the last three raw
+    // inputs in registers while it walks its rows
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * (LY_THREADS / 64) + (threadIdx.x >> 6);
-    if (item >= p.rows * p.H) return;
-    const int64_t row = item / p.H;
-    const int h = (int)(item - row * p.H);
-    int64_t n, pos;
-    locate(row, p.cu, p.n_seqs, p.T, n, pos);
+    const uint32_t nhg = (uint32_t)(p.H + 3) / 4;
+    const uint32_t blk = blockIdx.x;
+    const uint32_t tb = blk / nhg;
+    const int h = (int)(blk - tb * nhg) * (LY_THREADS / 64) + (threadIdx.x >> 6);
+    if (h >= p.H) return;
     const int c = 2 * lane;
     const int64_t HD = (int64_t)p.H * 128;
-    const int64_t base = row * HD + (int64_t)h * 128 + c;
-
+    const int64_t row0 = (int64_t)tb * LY_TOK;
+    const int nt = p.rows - row0 < LY_TOK ? (int)(p.rows - row0) : LY_TOK;
     const InT* raw[3] = {(const InT*)p.q_raw, (const InT*)p.k_raw, (const InT*)p.v_raw};
     InT* out[3] = {(InT*)p.q, (InT*)p.k, (InT*)p.v};
+
+    // every load first (the stores below may not be reordered above them)
+    float4 w[3][2];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         // weights of channels c, c + 1: [tensor, head, channel, tap]
         const float* wp = p.conv_w + (((int64_t)i * p.H + h) * 128 + c) * 4;
-        const float4 w0 = *reinterpret_cast<const float4*>(wp);
-        const float4 w1 = *reinterpret_cast<const float4*>(wp + 4);
-        const float wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
-        float y0 = 0.f, y1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t tp = pos - 3 + j;   // token x_{t-3+j} of this sequence
-            float2 x = make_float2(0.f, 0.f);
-            if (tp >= 0) {
-                x = load2(raw[i] + base + (tp - pos) * HD);
-            } else if (p.cache) {   // cache tap 3 + tp holds x_{tp}
-                x = load2(p.cache + (((n * 3 + i) * 3 + (3 + tp)) * p.H + h) * 128 + c);
-            }
-            y0 = fmaf(wa[j], x.x, y0);
-            y1 = fmaf(wb[j], x.y, y1);
-        }
-        y0 *= sigm(y0);
-        y1 *= sigm(y1);
-        if (i < 2) {
-            const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) + LY_EPS);
-            y0 *= r;
-            y1 *= r;
-        }
-        store2(out[i] + base, make_float2(y0, y1));
+        w[i][0] = *reinterpret_cast<const float4*>(wp);
+        w[i][1] = *reinterpret_cast<const float4*>(wp + 4);
     }
-    const float2 a = load2(p.a + base);
-    store2(p.log_alpha + base, make_float2(-5.f * sigm(a.x), -5.f * sigm(a.y)));
-    if (lane == 0) p.beta[row * p.H + h] = sigm(p.b[row * p.H + h]);
+    float2 cur[LY_TOK][3], av[LY_TOK];
+    float bv[LY_TOK];
+#pragma unroll
+    for (int tt = 0; tt < LY_TOK; ++tt) {
+        if (tt < nt) {
+            const int64_t base = (row0 + tt) * HD + (int64_t)h * 128 + c;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) cur[tt][i] = load2(raw[i] + base);
+            av[tt] = load2(p.a + base);
+            bv[tt] = p.b[(row0 + tt) * p.H + h];
+        }
+    }
+    // the three inputs before a row: x_{t-3}, x_{t-2}, x_{t-1}
+    float2 win[3][3];
+    auto fill_window = [&](int64_t row, int64_t n, int64_t pos) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int64_t tp = pos - 3 + j;
+                win[i][j] = make_float2(0.f, 0.f);
+                if (tp >= 0)
+                    win[i][j] = load2(raw[i] + (row - 3 + j) * HD + (int64_t)h * 128 + c);
+                else if (p.cache)   // cache tap 3 + tp holds x_{tp}
+                    win[i][j] = load2(p.cache + (((n * 3 + i) * 3 + (3 + tp)) * p.H + h) * 128 + c);
+            }
+    };
+#pragma unroll
+    for (int tt = 0; tt < LY_TOK; ++tt) {
+        if (tt >= nt) break;
+        const int64_t row = row0 + tt;
+        int64_t n, pos;
+        locate(row, p.cu, p.n_seqs, p.T, n, pos);
+        if (tt == 0 || pos == 0) fill_window(row, n, pos);
+        const int64_t base = row * HD + (int64_t)h * 128 + c;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const float2 x3 = cur[tt][i];
+            float y0 = w[i][0].x * win[i][0].x;
+            float y1 = w[i][1].x * win[i][0].y;
+            y0 = fmaf(w[i][0].y, win[i][1].x, y0);
+            y1 = fmaf(w[i][1].y, win[i][1].y, y1);
+            y0 = fmaf(w[i][0].z, win[i][2].x, y0);
+            y1 = fmaf(w[i][1].z, win[i][2].y, y1);
+            y0 = fmaf(w[i][0].w, x3.x, y0);
+            y1 = fmaf(w[i][1].w, x3.y, y1);
+            win[i][0] = win[i][1];
+            win[i][1] = win[i][2];
+            win[i][2] = x3;
+            y0 *= sigm(y0);
+            y1 *= sigm(y1);
+            if (i < 2) {
+                const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) + LY_EPS);
+                y0 *= r;
+                y1 *= r;
+            }
+            store2(out[i] + base, make_float2(y0, y1));
+        }
+        store2(p.log_alpha + base, make_float2(-5.f * sigm(av[tt].x), -5.f * sigm(av[tt].y)));
+        if (lane == 0) p.beta[row * p.H + h] = sigm(bv[tt]);
+    }
 }
 
 // New conv cache: taps m = 0..2 hold x_{L-3+m} of each sequence (length L),
@@ -170,7 +211,7 @@ __global__ __launch_bounds__(LY_THREADS) void epilogue_kernel(const float* __res
 
 hipError_t launch_prologue(const LayerParams& p, bool bf16_in, hipStream_t stream) {
     const int64_t items = p.rows * p.H;
-    dim3 grid((unsigned)((items + 3) / 4)), block(LY_THREADS);
+    dim3 grid((unsigned)(((p.rows + LY_TOK - 1) / LY_TOK) * ((p.H + 3) / 4))), block(LY_THREADS);
     if (items > 0) {
         if (bf16_in) hipLaunchKernelGGL(prologue_kernel<__bf16>, grid, block, 0, stream, p);
         else hipLaunchKernelGGL(prologue_kernel<float>, grid, block, 0, stream, p);
