@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It is
 independent of the HIP library: no shared code, headers, tables or helpers.
 
-The recurrence (token by token, fp64, one (sequence, head) unit at a time) is
-written in ``kda_oracle.c``; this module builds it with gcc, loads it with
+The recurrence (token by token, fp64, one (sequence, head) unit at a time) and
+its reverse-mode derivative (the backward pass) are written in
+``kda_oracle.c``; this module builds it with gcc, loads it with
 ctypes and wraps it for numpy arrays.  ``reference.py`` holds small numpy
 restatements of the special cases the pages name (DeltaNet, gated DeltaNet,
 linear attention, the naive DPLR product, the unrolled product) that pin the
@@ -55,6 +56,10 @@ def _load():
         lib.kda_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64,
                                                i64, i64, dp, ctypes.c_int]
         lib.kda_oracle_decode_step.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [dp, dp, dp, dp, dp, dp, lp, i64, i64,
+                                            i64, i64, dp, dp, lp, i64, dp, dp,
+                                            dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_backward.restype = ctypes.c_int
         lib.kda_oracle_max_threads.argtypes = []
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -122,6 +127,50 @@ def forward(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
     if rc != 0:
         raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
     return o.reshape(lead + (H, dv)), st
+
+
+def backward(q, k, v, log_alpha, beta, S0, dO, dS_T=None, cu_seqlens=None, *,
+             units=None, nthreads=0):
+    """Gradients of L = <dO, o> + <dS_T, S_T> through the fp64 recurrence
+    (kda_oracle.c, kda_oracle_backward).  Shapes as forward(); dO like o,
+    dS_T like S_T (None = zero).  units: optional (n, h) pairs (other rows of
+    the outputs stay 0).  Returns (dq, dk, dv, dlog_alpha, dbeta, dS0) in fp64
+    with the input shapes (dS0 [N, H, dk, dv])."""
+    q = np.asarray(q)
+    lead = q.shape[:-2]
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = np.asarray(v).shape[-1]
+    if cu_seqlens is None:
+        B, T = lead if len(lead) == 2 else (1, lead[0])
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    Ttot = int(cu[-1])
+    qf, kf = _f64(q).reshape(Ttot, H, dk), _f64(k).reshape(Ttot, H, dk)
+    vf, lf = _f64(v).reshape(Ttot, H, dv), _f64(log_alpha).reshape(Ttot, H, dk)
+    bf = _f64(beta).reshape(Ttot, H)
+    s0 = None if S0 is None else _f64(S0).reshape(N, H, dk, dv)
+    dof = _f64(dO).reshape(Ttot, H, dv)
+    dst = None if dS_T is None else _f64(dS_T).reshape(N, H, dk, dv)
+    dq, dkk = np.zeros((Ttot, H, dk)), np.zeros((Ttot, H, dk))
+    dvv, dla = np.zeros((Ttot, H, dv)), np.zeros((Ttot, H, dk))
+    db, ds0 = np.zeros((Ttot, H)), np.zeros((N, H, dk, dv))
+    if units is not None:
+        ua = np.ascontiguousarray(np.asarray(units, dtype=np.int64).reshape(-1, 2))
+        nu = ua.shape[0]
+    else:
+        ua, nu = None, 0
+    rc = _load().kda_oracle_backward(
+        _ptr(qf), _ptr(kf), _ptr(vf), _ptr(lf), _ptr(bf), _ptr(s0),
+        _ptr(cu, ctypes.c_int64), N, H, dk, dv, _ptr(dof), _ptr(dst),
+        _ptr(ua, ctypes.c_int64), nu, _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dla),
+        _ptr(db), _ptr(ds0), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_backward failed with code {rc}")
+    return (dq.reshape(lead + (H, dk)), dkk.reshape(lead + (H, dk)),
+            dvv.reshape(lead + (H, dv)), dla.reshape(lead + (H, dk)),
+            db.reshape(lead + (H,)), ds0)
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, nthreads=0):
