@@ -68,6 +68,11 @@ def load_library():
     lib.kda_prologue.restype = ctypes.c_int
     lib.kda_epilogue.argtypes = [fp, fp, fp, i64, i32, i32, fp, vp]
     lib.kda_epilogue.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, ip, i32, i64, i32, i32,
+                                  i32, fp, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -172,6 +177,64 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
                            ctypes.c_void_p(stream))
     _status(rc, "kda_chunk_fwd")
     return o, S_T
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T=None, cu_seqlens=None, *,
+              want_grad_S0: bool = True, workspace=None):
+    """Backward pass of chunk_fwd (see kda_chunk_bwd in include/kda.h).
+
+    Inputs as for chunk_fwd; grad_o float32 like o; grad_S_T [N, H, 128, 128]
+    float32 or None (zero).  Returns (grad_q, grad_k, grad_v, grad_log_alpha,
+    grad_beta, grad_S0), all float32 with the shapes of q, k, v, log_alpha,
+    beta and S0 ([N, H, 128, 128], or None when want_grad_S0 is False).
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    _check(log_alpha, "log_alpha", torch.float32, dev)
+    _check(beta, "beta", torch.float32, dev)
+    _check(grad_o, "grad_o", torch.float32, dev)
+    dt = _in_dtype(q)
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        n_seqs = cu_seqlens.numel() - 1
+        T = q.numel() // (H * dk)
+        if q.dim() == 4 and q.shape[0] != 1:
+            raise KDAError("packed varlen input must have a leading batch of 1 or none")
+    else:
+        if q.dim() != 4:
+            raise KDAError("q must be [B, T, H, 128] without cu_seqlens")
+        n_seqs, T = q.shape[0], q.shape[1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape[:-1] != q.shape[:-1] \
+            or beta.shape != q.shape[:-1] or grad_o.shape != v.shape:
+        raise KDAError("q/k/log_alpha/v/beta/grad_o shapes disagree")
+    st_shape = (n_seqs, H, dk, dv)
+    for name, t in (("S0", S0), ("grad_S_T", grad_S_T)):
+        if t is not None:
+            _check(t, name, torch.float32, dev)
+            if tuple(t.shape) != st_shape:
+                raise KDAError(f"{name} must be {st_shape}, got {tuple(t.shape)}")
+    f32 = dict(dtype=torch.float32, device=dev)
+    gq, gk = torch.empty(q.shape, **f32), torch.empty(q.shape, **f32)
+    gv, gla = torch.empty(v.shape, **f32), torch.empty(q.shape, **f32)
+    gb = torch.empty(beta.shape, **f32)
+    gS0 = torch.empty(st_shape, **f32) if want_grad_S0 else None
+    ws_bytes = int(lib.kda_chunk_bwd_workspace_bytes(n_seqs, T, H, dk, dv,
+                                                     int(cu_seqlens is not None)))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                           _ptr(cu_seqlens), n_seqs, T, H, dk, dv, _ptr(grad_o), _ptr(grad_S_T),
+                           _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gla), _ptr(gb), _ptr(gS0),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           ctypes.c_void_p(stream))
+    _status(rc, "kda_chunk_bwd")
+    return gq, gk, gv, gla, gb, gS0
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None):

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_abi.hip", "kda_prefill.hip", "kda_segment.hip", "kda_decode.hip", "kda_recurrent.hip",
-           "kda_layer.hip"]
+           "kda_layer.hip", "kda_backward.hip"]
 HEADERS = ["kda_device.h", "kda_launch.h"]
 ARCH = "gfx950"
 

@@ -183,6 +183,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     p.seg_len = T;
     p.seg_per_seq = 1;
     p.s0_identity = 0;
+    p.h_states = nullptr;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -395,6 +396,157 @@ int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, i
     if (overlaps(rout, rg) || overlaps(rout, rw)) return KDA_ERR_ALIASING;
     if (out != o && overlaps(rout, ro)) return KDA_ERR_ALIASING;
     hipError_t e = kda::launch_epilogue(o, g, w, out, items, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// Backward workspace layout (floats): states at chunk starts and gradients
+// at chunk ends [slots, H, 128, 128] each, T/M/P [slots, H, 3, 32, 32],
+// W [tokens, H, 128]; slots = tokens / 32 + n_seqs.
+struct BwdLayout {
+    int64_t slots, h, dsn, tmp, w, total;   // offsets and total in floats
+};
+static bool bwd_layout(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayout* L) {
+    L->slots = tokens / kChunk + n_seqs;
+    int64_t sh = 0, st = 0, tmp = 0, wv = 0;
+    if (!mul_ok(L->slots, H, &sh) || !mul_ok(sh, kHeadDim * kHeadDim, &st) ||
+        !mul_ok(sh, 3 * kChunk * kChunk, &tmp) || !mul_ok(tokens, H * kHeadDim, &wv))
+        return false;
+    L->h = 0;
+    L->dsn = st;
+    L->tmp = 2 * st;
+    L->w = 2 * st + tmp;
+    L->total = 2 * st + tmp + wv;
+    return L->total >= 0 && L->total <= INT64_MAX / 8;
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H, int32_t dk, int32_t dv,
+                                     int varlen) {
+    if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim || H < 1 || T < 0) return 0;
+    int64_t tokens = T;
+    if (!varlen && !mul_ok((int64_t)n_seqs, T, &tokens)) return 0;
+    BwdLayout L;
+    if (!bwd_layout(n_seqs, tokens, H, &L)) return 0;
+    return (size_t)L.total * 4;
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
+                  const float* log_alpha, const float* beta, const float* S0,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int64_t T, int32_t H, int32_t dk,
+                  int32_t dv, const float* grad_o, const float* grad_S_T, float* grad_q,
+                  float* grad_k, float* grad_v, float* grad_log_alpha, float* grad_beta,
+                  float* grad_S0, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
+    if (dk != kHeadDim || dv != kHeadDim || H < 1 || n_seqs < 0 || T < 0)
+        return KDA_ERR_BAD_SHAPE;
+    const bool varlen = cu_seqlens != nullptr;
+    int64_t tokens = 0;
+    if (varlen) tokens = T;
+    else if (!mul_ok((int64_t)n_seqs, T, &tokens)) return KDA_ERR_TOO_LARGE;
+    if (n_seqs == 0) return KDA_OK;
+    int64_t rows = 0, elems = 0, units = 0, st_elems = 0;
+    if (!mul_ok(tokens, (int64_t)H, &rows) || !mul_ok(rows, kHeadDim, &elems) ||
+        elems > INT64_MAX / 8 || !mul_ok((int64_t)n_seqs, (int64_t)H, &units) ||
+        !mul_ok(units, kHeadDim * kHeadDim, &st_elems))
+        return KDA_ERR_TOO_LARGE;
+    BwdLayout L;
+    if (!bwd_layout(n_seqs, tokens, H, &L)) return KDA_ERR_TOO_LARGE;
+    const int64_t chunks = L.slots * H;
+    if (units > INT32_MAX / 32 || chunks > INT32_MAX) return KDA_ERR_TOO_LARGE;
+
+    if (tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !grad_o || !grad_q || !grad_k ||
+                       !grad_v || !grad_log_alpha || !grad_beta))
+        return KDA_ERR_NULL_POINTER;
+    if (!workspace) return KDA_ERR_WORKSPACE;
+    if ((size_t)L.total * 4 > workspace_bytes) return KDA_ERR_WORKSPACE;
+    if (tokens > 0) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) ||
+            !aligned(grad_o, 16) || !aligned(grad_q, 16) || !aligned(grad_k, 16) ||
+            !aligned(grad_v, 16) || !aligned(grad_log_alpha, 16) || !aligned(beta, 4) ||
+            !aligned(grad_beta, 4))
+            return KDA_ERR_MISALIGNED;
+    }
+    if ((S0 && !aligned(S0, 16)) || (grad_S_T && !aligned(grad_S_T, 16)) ||
+        (grad_S0 && !aligned(grad_S0, 16)) || (cu_seqlens && !aligned(cu_seqlens, 4)) ||
+        !aligned(workspace, 16))
+        return KDA_ERR_MISALIGNED;
+
+    // Every output (and the workspace) overlaps no input and no other
+    // output; grad_S0 may be the same pointer as grad_S_T.
+    const int64_t es = elem_size(in_dtype);
+    const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+    const Range rla = span(log_alpha, elems * 4), rb = span(beta, rows * 4);
+    const Range rs0 = span(S0, S0 ? st_elems * 4 : 0);
+    const Range rcu = span(cu_seqlens, varlen ? ((int64_t)n_seqs + 1) * 4 : 0);
+    const Range rgo = span(grad_o, elems * 4);
+    const Range rgst = span(grad_S_T, grad_S_T ? st_elems * 4 : 0);
+    const Range outs[] = {span(grad_q, elems * 4), span(grad_k, elems * 4), span(grad_v, elems * 4),
+                          span(grad_log_alpha, elems * 4), span(grad_beta, rows * 4),
+                          span(grad_S0, grad_S0 ? st_elems * 4 : 0),
+                          span(workspace, L.total * 4)};
+    const Range ins[] = {rq, rk, rv, rla, rb, rs0, rcu, rgo};
+    const int n_out = (int)(sizeof(outs) / sizeof(outs[0]));
+    for (int a = 0; a < n_out; ++a) {
+        for (const Range& r : ins)
+            if (overlaps(outs[a], r)) return KDA_ERR_ALIASING;
+        const bool gs0 = a == 5;
+        if (!(gs0 && grad_S0 == grad_S_T) && overlaps(outs[a], rgst)) return KDA_ERR_ALIASING;
+        for (int b = a + 1; b < n_out; ++b)
+            if (overlaps(outs[a], outs[b])) return KDA_ERR_ALIASING;
+    }
+
+    float* ws = (float*)workspace;
+    // 1. forward pass storing the state at every chunk start
+    const int n_slices = units < 256 ? 2 : 1;
+    const int wcols = 128 / (4 * n_slices);
+    if (((units + 7) / 8) * 8 * n_slices > kMaxGrid) return KDA_ERR_TOO_LARGE;
+    kda::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.la = log_alpha;
+    p.beta = beta;
+    p.S0 = S0;
+    p.cu = cu_seqlens;
+    p.order = nullptr;
+    p.o = nullptr;
+    p.S_T = nullptr;
+    p.T = T;
+    p.seg_len = T;
+    p.seg_per_seq = 1;
+    p.s0_identity = 0;
+    p.n_seqs = n_seqs;
+    p.H = H;
+    p.n_slices = n_slices;
+    p.n_units = (int32_t)units;
+    p.h_states = ws + L.h;
+    const bool bf16_in = in_dtype == KDA_BF16;
+    hipError_t e = kda::launch_chunk_fwd(p, bf16_in, wcols, false, stream);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    // 2. chunk matrices, reverse state-gradient scan, chunk gradients
+    kda::BwdParams b;
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.la = log_alpha;
+    b.beta = beta;
+    b.cu = cu_seqlens;
+    b.dO = grad_o;
+    b.dS_T = grad_S_T;
+    b.dq = grad_q;
+    b.dk = grad_k;
+    b.dv = grad_v;
+    b.dla = grad_log_alpha;
+    b.dbeta = grad_beta;
+    b.dS0 = grad_S0;
+    b.h = ws + L.h;
+    b.dsn = ws + L.dsn;
+    b.tmp = ws + L.tmp;
+    b.w = ws + L.w;
+    b.T = T;
+    b.slots = L.slots;
+    b.n_seqs = n_seqs;
+    b.H = H;
+    e = kda::launch_chunk_bwd(b, bf16_in, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

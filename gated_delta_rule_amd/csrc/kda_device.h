@@ -202,16 +202,26 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float wave_sum_dpp(float x) {
+// Sum over the 32 lanes of each half wave (lanes with equal l >> 5).
+__device__ __forceinline__ float half_sum_dpp(float x) {
     x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
     x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
     x += dpp_mov<0x124>(x);   // row_ror:4
     x += dpp_mov<0x128>(x);   // row_ror:8
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x += __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
-    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return x;
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x = half_sum_dpp(x);
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x += __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
     return x;
+}
+// Value of lane l ^ 32.
+__device__ __forceinline__ float swap_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
 // Make LDS writes of this wave visible to all of its lanes and keep the

@@ -27,6 +27,10 @@ struct PrefillParams {
     // v as zero, so its final state is the chain's linear map S_in -> S_out.
     int32_t s0_identity;
     int32_t n_seqs, H, n_slices, n_units;   // n_seqs counts chains (segments)
+    // Optional [slots, H, 128, 128]: the state at the start of every chunk
+    // (unsplit sequences only); chunk j of sequence n starting at token t0
+    // goes to slot t0 / 32 + n + j, which no other chunk uses.
+    float* h_states;
 };
 
 // Enqueue the prefill (and, when `sort`, the sequence-order pass first).
@@ -72,6 +76,35 @@ struct LayerParams {
 hipError_t launch_prologue(const LayerParams& p, bool bf16_in, hipStream_t stream);
 hipError_t launch_epilogue(const float* o, const float* g, const float* w, float* out, int64_t items,
                            hipStream_t stream);
+
+// Backward pass after a forward pass that stored the state at every chunk
+// start in h (see PrefillParams::h_states; chunk j of sequence n in slot
+// start_n / 32 + n + j).  Arrays: h, dsn [slots, H, 128, 128];
+// tmp [slots, H, 3, 32, 32] (T, M, P); w [tokens, H, 128].
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* la;
+    const float* beta;
+    const int32_t* cu;      // device [n_seqs + 1] or nullptr (equal lengths T)
+    const float* dO;
+    const float* dS_T;      // or nullptr (zero)
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dla;
+    float* dbeta;
+    float* dS0;             // or nullptr (not wanted)
+    const float* h;
+    float* dsn;
+    float* tmp;
+    float* w;
+    int64_t T;              // tokens per sequence (equal lengths) or total (packed)
+    int64_t slots;
+    int32_t n_seqs, H;
+};
+hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream);
 
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16_in,
                               const float* log_alpha, const float* beta, float* S,

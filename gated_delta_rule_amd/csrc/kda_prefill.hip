@@ -201,7 +201,7 @@ __device__ __forceinline__ void invert16(const float* L, float* T, int lane) {
 }
 
 // NPROD producer waves (4 or 8) follow the 4 consumer waves.
-template <typename InT, int WCOLS, int NPROD>
+template <typename InT, int WCOLS, int NPROD, bool STORE_H>
 __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillParams p) {
     constexpr bool F32 = std::is_same<InT, float>::value;
     constexpr int NCT = WCOLS / 16;   // 16-column tiles per consumer wave
@@ -530,6 +530,22 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                                    : p.S0 ? p.S0[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 +
                                                  ct * 16 + ln]
                                           : 0.f;
+        // state at the start of chunk j -> slot hslot0 + j
+        float* hbase = nullptr;
+        if constexpr (STORE_H) hbase = p.h_states + ((size_t)(t0 / CH + n) * H + h) * (DK * DK);
+        auto store_h = [&](float* dst, int it, int ct) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(size_t)(it * 16 + g * 4 + r) * DK + col0 + ct * 16 + ln] = S[it][ct][r];
+        };
+        if constexpr (STORE_H) {
+            if (nch > 0) {
+#pragma unroll
+                for (int it = 0; it < 8; ++it)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) store_h(hbase, it, ct);
+            }
+        }
         load_v(0, pv);
         load_beta(0, pb);
         __syncthreads();   // step 0: nothing to finish yet
@@ -723,6 +739,13 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     S[it][ct][2] *= sc4.z;
                     S[it][ct][3] *= sc4.w;
                 }
+                if constexpr (STORE_H) {
+                    if (more) {
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+                            store_h(hbase + (size_t)(cidx + 1) * H * (DK * DK), it, ct);
+                    }
+                }
                 // two separate scalings: their product alone can underflow
                 // (e^{-80} e^{-80}) where the scaled state does not; a select,
                 // not a branch, so the matrix-core chains stay interleaved
@@ -863,17 +886,24 @@ hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, b
     // 16 columns per consumer wave (two slices per head) pairs with eight
     // producer waves, 32 columns (one slice) with four.
     dim3 grid((unsigned)(groups * 8 * p.n_slices));
+    const bool hs = p.h_states != nullptr;
+#define KDA_FWD(T_, W_, P_)                                                                     \
+    do {                                                                                        \
+        if (hs)                                                                                 \
+            hipLaunchKernelGGL((chunk_fwd_kernel<T_, W_, P_, true>), grid, dim3(64 * (4 + P_)), \
+                               0, stream, p);                                                   \
+        else                                                                                    \
+            hipLaunchKernelGGL((chunk_fwd_kernel<T_, W_, P_, false>), grid,                     \
+                               dim3(64 * (4 + P_)), 0, stream, p);                              \
+    } while (0)
     if (bf16_in) {
-        if (wcols == 32)
-            hipLaunchKernelGGL((chunk_fwd_kernel<__bf16, 32, 4>), grid, dim3(512), 0, stream, p);
-        else
-            hipLaunchKernelGGL((chunk_fwd_kernel<__bf16, 16, 8>), grid, dim3(768), 0, stream, p);
+        if (wcols == 32) KDA_FWD(__bf16, 32, 4);
+        else KDA_FWD(__bf16, 16, 8);
     } else {
-        if (wcols == 32)
-            hipLaunchKernelGGL((chunk_fwd_kernel<float, 32, 4>), grid, dim3(512), 0, stream, p);
-        else
-            hipLaunchKernelGGL((chunk_fwd_kernel<float, 16, 8>), grid, dim3(768), 0, stream, p);
+        if (wcols == 32) KDA_FWD(float, 32, 4);
+        else KDA_FWD(float, 16, 8);
     }
+#undef KDA_FWD
     return hipGetLastError();
 }
 

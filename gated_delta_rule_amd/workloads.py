@@ -36,6 +36,8 @@ T_Q, T_K, T_V, T_LOGA, T_BETA, T_S0, T_LEN = range(7)
 # layer prologue / epilogue inputs
 T_RAW_Q, T_RAW_K, T_RAW_V, T_CONV_W, T_GATE_A, T_GATE_B, T_GATE_O, T_NORM_W, T_CACHE = range(7, 16)
 LAYER_WID = 100
+# upstream gradients for the backward pass
+T_GRAD_O, T_GRAD_S = 16, 17
 
 
 @dataclass(frozen=True)
@@ -245,3 +247,28 @@ def layer_inputs(lens, H: int, dtype: str = "bf16", seed: int = 0, with_cache: b
                     if with_cache else None)
     out["cu_seqlens"] = cu
     return out
+
+
+def grad_head(w: Workload, head: int, n_tokens: int, n_seq: int, s_std: float = 1.0):
+    """Upstream gradients for one head: dO ~ N(0, 1) float32 [n_tokens, dv]
+    (the loss gradient at every output) and dS_T ~ N(0, s_std^2) float32
+    [n_seq, dk, dv] (at every final state), or None when s_std is 0."""
+    dO = _rng(w.wid, T_GRAD_O, head).standard_normal((n_tokens, w.dv)).astype(np.float32)
+    dS = (None if s_std == 0.0 else
+          (s_std * _rng(w.wid, T_GRAD_S, head).standard_normal((n_seq, w.dk, w.dv)))
+          .astype(np.float32))
+    return dO, dS
+
+
+def grad_inputs(w: Workload, T: int, N: int, s_std: float = 1.0, heads=None):
+    """dO [T, H, dv] and dS_T [N, H, dk, dv] (or None) for all (or the listed)
+    heads, from grad_head."""
+    heads = list(range(w.H)) if heads is None else list(heads)
+    dO = np.empty((T, len(heads), w.dv), np.float32)
+    dS = None if s_std == 0.0 else np.empty((N, len(heads), w.dk, w.dv), np.float32)
+    for i, h in enumerate(heads):
+        a, b = grad_head(w, h, T, N, s_std)
+        dO[:, i] = a
+        if dS is not None:
+            dS[:, i] = b
+    return dO, dS

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -223,6 +223,52 @@ int kda_prologue(const void* q_raw, const void* k_raw, const void* v_raw, int in
  */
 int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, int32_t H,
                  int32_t dv, float* out, hipStream_t stream);
+
+/*
+ * Workspace size in bytes for kda_chunk_bwd (always required): with
+ * tokens = n_seqs * T (equal lengths) or T (varlen != 0) and
+ * slots = tokens / 32 + n_seqs, it holds the state at the start and the
+ * state gradient at the end of every 32-token chunk (2 * slots * H * 64 KiB),
+ * three 32 x 32 chunk matrices (slots * H * 12 KiB) and one fp32 value row
+ * per token and head (tokens * H * 512 bytes).  0 for invalid sizes.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
+                                     int32_t dk, int32_t dv, int varlen);
+
+/*
+ * Backward pass of kda_chunk_fwd: the gradients of a scalar loss L with
+ * respect to every input, given grad_o = dL/do and grad_S_T = dL/dS_T.
+ * Needed for training ("尝试对Kimi KDA的数学推导&算子实现分析" lists the
+ * chunk backward kernel beside the forward); the pages give no formula, so
+ * it is the reverse-mode derivative of the same chunk form (eqs. (51)-(66)
+ * of that page), evaluated chunk by chunk: a forward pass storing each
+ * chunk's incoming state, the chunk matrices, one backward walk per
+ * (sequence, head) carrying dL/dS, and the per-chunk gradients.
+ *
+ * Inputs q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, T, H, dk, dv and
+ * in_dtype exactly as for the kda_chunk_fwd call being differentiated.
+ *   grad_o   : float32 like o.
+ *   grad_S_T : float32 [n_seqs, H, dk, dv], or NULL for zero.
+ * Outputs (float32, overwritten, all token rows of every sequence):
+ *   grad_q, grad_k, grad_log_alpha like q; grad_v like v; grad_beta like
+ *   beta; grad_S0 [n_seqs, H, dk, dv] or NULL to skip (it may be the same
+ *   pointer as grad_S_T; any other overlap between an output, an input or
+ *   the workspace is rejected).
+ *   workspace: kda_chunk_bwd_workspace_bytes(...) bytes, 16-byte aligned,
+ *   contents clobbered.
+ * Numerics: every product of the backward pass runs on fp32 matrix cores
+ * with fp32 accumulation (the states come from the same kernel as
+ * kda_chunk_fwd, so with KDA_BF16 inputs they carry its split-bf16
+ * rounding).  Deterministic: no atomics.
+ */
+int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
+                  const float* log_alpha, const float* beta, const float* S0,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
+                  int32_t H, int32_t dk, int32_t dv, const float* grad_o,
+                  const float* grad_S_T, float* grad_q, float* grad_k,
+                  float* grad_v, float* grad_log_alpha, float* grad_beta,
+                  float* grad_S0, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

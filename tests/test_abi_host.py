@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert names == sorted(["kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_bytes",
                             "kda_chunk_fwd", "kda_decode_step", "kda_recurrent_fwd",
-                            "kda_prologue", "kda_epilogue"])
+                            "kda_prologue", "kda_epilogue", "kda_chunk_bwd_workspace_bytes",
+                            "kda_chunk_bwd"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -213,3 +214,51 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(kda.KDAError):
         kda.load_library()
+
+
+def test_bwd_workspace_query(lib):
+    ws = lib.kda_chunk_bwd_workspace_bytes
+    # slots = tokens / 32 + n_seqs; per slot and head 2 states + 3 [32, 32]
+    # matrices, plus one fp32 row per token and head
+    def expect(tokens, n, H):
+        slots = tokens // 32 + n
+        return (slots * H * (2 * 128 * 128 + 3 * 32 * 32) + tokens * H * 128) * 4
+    assert ws(1, 8192, 96, 128, 128, 0) == expect(8192, 1, 96)
+    assert ws(3, 100, 2, 128, 128, 0) == expect(300, 3, 2)
+    assert ws(32, 270000, 96, 128, 128, 1) == expect(270000, 32, 96)
+    assert ws(2, 64, 4, 64, 128, 0) == 0
+    assert ws(-1, 64, 4, 128, 128, 0) == 0
+
+
+def bwd(lib, **kw):
+    G = {n: A + (16 + i) * 0x100000000 for i, n in enumerate(["go", "gst", "gq", "gk", "gv", "gla",
+                                                              "gb", "gs0"])}
+    a = dict(q=P["q"], k=P["k"], v=P["v"], dtype=0, la=P["la"], b=P["b"], s0=None, cu=None,
+             n=2, T=64, H=4, dk=128, dv=128, go=G["go"], gst=None, gq=G["gq"], gk=G["gk"],
+             gv=G["gv"], gla=G["gla"], gb=G["gb"], gs0=G["gs0"], ws=P["ws"], wsb=1 << 30)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.kda_chunk_bwd(vp(a["q"]), vp(a["k"]), vp(a["v"]), a["dtype"], vp(a["la"]),
+                             vp(a["b"]), vp(a["s0"]), vp(a["cu"]), a["n"], a["T"], a["H"], a["dk"],
+                             a["dv"], vp(a["go"]), vp(a["gst"]), vp(a["gq"]), vp(a["gk"]),
+                             vp(a["gv"]), vp(a["gla"]), vp(a["gb"]), vp(a["gs0"]), vp(a["ws"]),
+                             a["wsb"], None)
+
+
+def test_chunk_bwd_validation(lib):
+    """Only error paths (they return before anything is enqueued)."""
+    assert bwd(lib, dtype=9) == DTYPE
+    assert bwd(lib, dk=64) == SHAPE
+    assert bwd(lib, H=0) == SHAPE
+    assert bwd(lib, T=-5) == SHAPE
+    assert bwd(lib, go=None) == NULLP
+    assert bwd(lib, gb=None) == NULLP
+    assert bwd(lib, ws=None) == WS
+    assert bwd(lib, wsb=1000) == WS
+    assert bwd(lib, gq=P["q"] + 16) == ALIAS            # gradient on top of an input
+    assert bwd(lib, gk=P["ws"] + 4096) == ALIAS         # gradient inside the workspace
+    assert bwd(lib, gs0=P["st"], gst=P["st"] + 4096) == ALIAS
+    assert bwd(lib, gla=P["la"] + 8) == ALIGN
+    assert bwd(lib, ws=P["ws"] + 4) == ALIGN
+    assert bwd(lib, n=2 ** 31 - 1, T=2 ** 40) == LARGE
+    assert bwd(lib, n=0) == OK

@@ -1,0 +1,151 @@
+"""GPU parity of kda_chunk_bwd (through the C ABI) against the fp64 oracle's
+backward pass (oracle.backward, the reverse-mode derivative of the token
+loop).  Small and ragged cases compare every element of all six gradients;
+the full-size prefill shape compares sampled heads, which the oracle follows
+on their own (every (sequence, head) chain is independent)."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_amd import workloads as W
+from kda_testlib import TOL_BF16, TOL_F32, rel_err, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU-only container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gated_delta_rule_amd as kda  # noqa: E402
+import oracle  # noqa: E402
+
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0")
+
+
+def inputs(w, lens, s0, ds_std, la_const=None):
+    """Token-major packed inputs for sequences of the given lengths (one
+    seeded stream per head, cut into the sequences)."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, N = int(cu[-1]), len(lens)
+    w = w.shrink(s0_std=s0)
+    a = {n: np.empty((T, w.H) + ((w.dk,) if n != "beta" else ()), np.float32)
+         for n in ("q", "k", "v", "log_alpha", "beta")}
+    S0 = np.empty((N, w.H, w.dk, w.dv), np.float32) if s0 else None
+    for h in range(w.H):
+        s = W.head_stream(w, h, T)
+        for n in a:
+            a[n][:, h] = s[n]
+        if S0 is not None:
+            S0[:, h] = W.initial_state_head(w, h, N)
+    if la_const is not None:
+        a["log_alpha"][:] = la_const
+    dO, dS = W.grad_inputs(w, T, N, ds_std)
+    return w, a, S0, dO, dS, cu
+
+
+def run(w, a, S0, dO, dS, cu, equal=None):
+    """GPU backward; `equal` = (B, T) passes the equal-length layout instead
+    of cu_seqlens."""
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = {n: torch.from_numpy(np.ascontiguousarray(a[n])).cuda() for n in a}
+    for n in ("q", "k", "v"):
+        d[n] = d[n].to(dt)
+    s0 = None if S0 is None else torch.from_numpy(S0).cuda()
+    go = torch.from_numpy(dO).cuda()
+    gst = None if dS is None else torch.from_numpy(dS).cuda()
+    cu_dev = None
+    if equal is not None:
+        B, T = equal
+        for n in d:
+            d[n] = d[n].reshape((B, T) + tuple(d[n].shape[1:]))
+        go = go.reshape((B, T) + tuple(go.shape[1:]))
+    else:
+        cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
+    g = kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s0, go, gst, cu_dev)
+    torch.cuda.synchronize()
+    T = a["q"].shape[0]
+    out = [t.cpu().numpy() for t in g]
+    for i in range(5):
+        out[i] = out[i].reshape((T,) + out[i].shape[2 if equal else 1:])
+    return out
+
+
+def compare(w, a, S0, dO, dS, cu, tol, label, equal=None):
+    say(f"[bwd] {label}: GPU")
+    got = run(w, a, S0, dO, dS, cu, equal)
+    say(f"[bwd] {label}: oracle")
+    ref = oracle.backward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], S0, dO, dS, cu)
+    errs = {n: rel_err(x, r) for n, x, r in zip(NAMES, got, ref)}
+    say(f"[bwd] {label}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f" (tol {tol})")
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+    return errs
+
+
+@pytest.mark.parametrize("lens,H,s0,ds", [([100, 100], 3, 0.02, 1.0), ([1], 1, 0.0, 0.0),
+                                          ([32], 2, 0.02, 1.0), ([33, 33], 1, 0.0, 1.0),
+                                          ([257], 2, 0.02, 0.0)])
+def test_bwd_equal_lengths_bf16(lens, H, s0, ds):
+    w, a, S0, dO, dS, cu = inputs(W.workload(1).shrink(H=H), lens, s0, ds)
+    compare(w, a, S0, dO, dS, cu, TOL_BF16, f"bf16 lens={lens} H={H} s0={s0} dS={ds}",
+            equal=(len(lens), lens[0]))
+
+
+def test_bwd_varlen_bf16_edges():
+    """Empty, one-token, exactly-one-chunk and chunk-plus-one sequences, packed."""
+    w, a, S0, dO, dS, cu = inputs(W.workload(2).shrink(H=2), [0, 1, 31, 32, 33, 70, 0, 5],
+                                  0.02, 1.0)
+    compare(w, a, S0, dO, dS, cu, TOL_BF16, "bf16 varlen edges")
+
+
+def test_bwd_workload0_fp32():
+    """Single fp32 head, T=256, S0 = 0, no state gradient."""
+    w, a, S0, dO, dS, cu = inputs(W.workload(0), [256], 0.0, 0.0)
+    compare(w, a, S0, dO, dS, cu, TOL_F32, "fp32 T=256", equal=(1, 256))
+
+
+@pytest.mark.parametrize("la", [-5.0, 0.0])
+def test_bwd_decay_extremes(la):
+    """log alpha = -5 everywhere (the fastest forgetting: 16 tokens span e^-80)
+    and log alpha = 0 (no decay, DeltaNet)."""
+    w, a, S0, dO, dS, cu = inputs(W.workload(1).shrink(H=2), [70, 45], 0.02, 1.0, la_const=la)
+    compare(w, a, S0, dO, dS, cu, TOL_BF16, f"bf16 log_alpha={la}")
+
+
+def test_bwd_full_size_sampled_heads():
+    """The full prefill shape (T=8192, H=96, bf16) on the GPU; two heads
+    followed by the oracle on their own."""
+    w = W.workload(1)
+    T, H = w.T, w.H
+    say("[bwd] full size: inputs")
+    dt = torch.bfloat16
+    d = {n: torch.empty((1, T, H, 128), dtype=dt, device="cuda") for n in ("q", "k", "v")}
+    d["log_alpha"] = torch.empty((1, T, H, 128), device="cuda")
+    d["beta"] = torch.empty((1, T, H), device="cuda")
+    go = torch.empty((1, T, H, 128), device="cuda")
+    gst = torch.empty((1, H, 128, 128), device="cuda")
+    for h in range(H):
+        s = W.head_stream(w, h, T)
+        for n in ("q", "k", "v", "log_alpha"):
+            d[n][0, :, h] = torch.from_numpy(s[n]).cuda().to(d[n].dtype)
+        d["beta"][0, :, h] = torch.from_numpy(s["beta"]).cuda()
+        a, b = W.grad_head(w, h, T, 1)
+        go[0, :, h] = torch.from_numpy(a).cuda()
+        gst[:, h] = torch.from_numpy(b).cuda()
+    say("[bwd] full size: GPU")
+    g = kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, go, gst)
+    torch.cuda.synchronize()
+    for h in (0, 77):
+        say(f"[bwd] full size: oracle head {h}")
+        s = W.head_stream(w, h, T)
+        a, b = W.grad_head(w, h, T, 1)
+        ref = oracle.backward(s["q"][:, None], s["k"][:, None], s["v"][:, None],
+                              s["log_alpha"][:, None], s["beta"][:, None], None, a[:, None],
+                              b[:, None])
+        errs = {}
+        for i, n in enumerate(NAMES):
+            x = g[i][0, :, h].cpu().numpy() if i < 5 else g[i][:, h].cpu().numpy()
+            r = ref[i][:, 0] if i < 5 else ref[i][:, 0]
+            errs[n] = rel_err(x, r)
+        say(f"[bwd] full size head {h}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= TOL_BF16, (h, n, e)
