@@ -18,6 +18,9 @@ constexpr int64_t kMinSegTokens = 2048;    // shortest segment worth a separate 
 constexpr int64_t kStateBytes = kHeadDim * kHeadDim * 4;
 constexpr int64_t kFillUnits = 256;        // compute units to cover
 constexpr int32_t kMaxRecurrent = 64;      // tokens per request on the recurrent path
+// floats per (chunk, head) of the backward's chunk matrices: T^T, M^T, P
+// [32][32] each, K_end^T, Q+^T, -(B_beta K+)^T [128][32] each, e^{g_C} [128]
+constexpr int64_t kBwdChunkElems = 3 * 32 * 32 + 3 * 128 * 32 + 128;
 
 // Sequence-parallel split of an equal-length batch: segments per sequence
 // (1 = none) and tokens per segment (a multiple of the chunk).  Used when
@@ -400,8 +403,9 @@ int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, i
 }
 
 // Backward workspace layout (floats): states at chunk starts and gradients
-// at chunk ends [slots, H, 128, 128] each, T/M/P [slots, H, 3, 32, 32],
-// W [tokens, H, 128]; slots = tokens / 32 + n_seqs.
+// at chunk ends [slots, H, 128, 128] each, the chunk matrices of the first
+// backward pass [slots, H, kBwdChunkElems], W [tokens, H, 128];
+// slots = tokens / 32 + n_seqs.
 struct BwdLayout {
     int64_t slots, h, dsn, tmp, w, total;   // offsets and total in floats
 };
@@ -409,7 +413,7 @@ static bool bwd_layout(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayout* L) 
     L->slots = tokens / kChunk + n_seqs;
     int64_t sh = 0, st = 0, tmp = 0, wv = 0;
     if (!mul_ok(L->slots, H, &sh) || !mul_ok(sh, kHeadDim * kHeadDim, &st) ||
-        !mul_ok(sh, 3 * kChunk * kChunk, &tmp) || !mul_ok(tokens, H * kHeadDim, &wv))
+        !mul_ok(sh, kBwdChunkElems, &tmp) || !mul_ok(tokens, H * kHeadDim, &wv))
         return false;
     L->h = 0;
     L->dsn = st;

@@ -58,7 +58,16 @@ constexpr int BD = 128;       // head dimension
 constexpr int LS = BD + 1;    // LDS row stride of [*][128] tiles (odd: rows read across lanes
                               // fall in distinct banks)
 constexpr int LC = BC + 1;    // row stride of [32][32] tiles
-constexpr int TMP_ELEMS = 3 * BC * BC;   // T, M, P per (chunk, head)
+// Per (chunk, head) matrices from the first pass, in the orders the
+// second and third passes read them (floats):
+constexpr int OFF_TT = 0;        // T^T            [32][32]
+constexpr int OFF_MT = 1024;     // M^T            [32][32]
+constexpr int OFF_P = 2048;      // P              [32][32] (strictly lower)
+constexpr int OFF_KE = 3072;     // K_end^T        [128][32]
+constexpr int OFF_QT = 7168;     // Q+^T           [128][32]
+constexpr int OFF_KB = 11264;    // -(B_beta K+)^T [128][32]
+constexpr int OFF_GC = 15360;    // e^{g_C}        [128]
+constexpr int TMP_ELEMS = 15488;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -132,8 +141,7 @@ __device__ __forceinline__ void chunk_scan(const float* la, int64_t c0, int nv, 
 // ---------------------------------------------------------------- pass 1
 template <typename InT>
 __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
-    __shared__ float sX[BC * LS], sY[BC * LS], sQ[BC * LS];
-    __shared__ float sA[BC * LC];
+    __shared__ float sX[BC * LS], sY[BC * LS], sQ[BC * LS];   // sX holds A once P is done
     __shared__ float sTot[2 * BD];
     __shared__ float sBeta[BC];
     const int64_t m = blockIdx.x / p.H;
@@ -141,28 +149,77 @@ __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
     const Chunk ch = slot_chunk(p, m);
     if (ch.nv == 0) return;
     const int H = p.H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = tid & (BD - 1), half = tid >> 7;
-    float g[16];
-    chunk_scan(p.la, ch.c0, ch.nv, H, h, c, half, g, sTot);
-    if (tid < BC) sBeta[tid] = tid < ch.nv ? p.beta[(ch.c0 + tid) * H + h] : 0.f;
-    __syncthreads();
-    const float e0 = sTot[c];                  // g at token 15
-    const float off = half ? e0 : 0.f;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = tid & (BD - 1), half = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const int rowb = H * BD * 4;
+    const int64_t e0i = (ch.c0 * H + h) * BD;
+    const int span = (ch.nv - 1) * rowb + BD * 4;
+    constexpr int ES = (int)sizeof(InT);
+    const auto rla = make_rsrc(p.la + e0i, span);
+    const auto rk = make_rsrc((const InT*)p.k + e0i, span / (4 / ES));
+    const auto rq = make_rsrc((const InT*)p.q + e0i, span / (4 / ES));
+    const auto rb = make_rsrc(p.beta + ch.c0 * H + h, ((ch.nv - 1) * H + 1) * 4);
+    float la[16], kr[16], qr[16], br[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int t = 16 * half + i;
-        const int64_t idx = ((ch.c0 + t) * H + h) * BD + c;
-        const float kf = t < ch.nv ? ld_in<InT>(p.k, idx) : 0.f;
-        const float qf = t < ch.nv ? ld_in<InT>(p.q, idx) : 0.f;
-        const float d = g[i] + off - e0;
-        const float fx = expf(d), fy = expf(-d);
-        sX[t * LS + c] = kf * fx;
-        sY[t * LS + c] = kf * fy;
-        sQ[t * LS + c] = qf * fx;
+        // the whole offset in the per-lane operand, so that the range check
+        // covers it (rows past the sequence end read as zero)
+        la[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rla, t * rowb + c * 4, 0, 0));
+        if constexpr (ES == 4) {
+            kr[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, t * rowb + c * 4, 0, 0));
+            qr[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rq, t * rowb + c * 4, 0, 0));
+        } else {
+            kr[i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rk, t * (rowb / 2) + c * 2, 0, 0) << 16);
+            qr[i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, t * (rowb / 2) + c * 2, 0, 0) << 16);
+        }
+        br[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, t * H * 4, 0, 0));
     }
-    __syncthreads();
+    {
+        float so = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) so += la[i];
+        sTot[half * BD + c] = so;
+        if (c == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sBeta[16 * half + i] = br[i];
+        }
+    }
+    lds_barrier();
     float* tmp = p.tmp + ((size_t)m * H + h) * TMP_ELEMS;
+    {
+        const float E0 = sTot[c];                    // g at token 15
+        const float gC = sTot[c] + sTot[BD + c];
+        float g = half ? E0 : 0.f;
+        float ke[16], qp[16], kb[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = 16 * half + i;
+            g += la[i];
+            const float d = g - E0;
+            const float fx = expf(d), fy = expf(-d), G = expf(g);
+            sX[t * LS + c] = kr[i] * fx;
+            sY[t * LS + c] = kr[i] * fy;
+            sQ[t * LS + c] = qr[i] * fx;
+            ke[i] = kr[i] * expf(gC - g);
+            qp[i] = qr[i] * G;
+            kb[i] = -br[i] * kr[i] * G;
+        }
+        // channel-major rows c of K_end^T, Q+^T, Kb^T (this thread's 16 tokens)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int o = c * BC + 16 * half + 4 * v;
+            *reinterpret_cast<float4*>(tmp + OFF_KE + o) =
+                make_float4(ke[4 * v], ke[4 * v + 1], ke[4 * v + 2], ke[4 * v + 3]);
+            *reinterpret_cast<float4*>(tmp + OFF_QT + o) =
+                make_float4(qp[4 * v], qp[4 * v + 1], qp[4 * v + 2], qp[4 * v + 3]);
+            *reinterpret_cast<float4*>(tmp + OFF_KB + o) =
+                make_float4(kb[4 * v], kb[4 * v + 1], kb[4 * v + 2], kb[4 * v + 3]);
+        }
+        if (half == 0) tmp[OFF_GC + c] = expf(gC);
+    }
+    lds_barrier();
     const int i0 = lane & 31, kh = lane >> 5;
     if (wave == 0) {
         // P = StrictTril(X Y^T); A = Diag(beta) P; T = (I + A)^{-1}
@@ -170,16 +227,17 @@ __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
 #pragma unroll 8
         for (int k0 = 0; k0 < BD; k0 += 2)
             acc = mma(sX[i0 * LS + k0 + kh], sY[i0 * LS + k0 + kh], acc);
+        float* sA = sX;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = crow(r, lane);
             const float pv = i0 < i ? acc[r] : 0.f;
-            tmp[2 * BC * BC + i * BC + i0] = pv;
+            tmp[OFF_P + i * BC + i0] = pv;
             sA[i * LC + i0] = sBeta[i] * pv;
         }
-        wave_lds_sync();
+        wave_lds_fence();
         if (lane < BC) {
-            // column `lane` of T by forward substitution
+            // column `lane` of T by forward substitution, stored as row `lane` of T^T
             float x[BC];
 #pragma unroll
             for (int t = 0; t < BC; ++t) {
@@ -189,10 +247,12 @@ __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
                 x[t] = s;
             }
 #pragma unroll
-            for (int t = 0; t < BC; ++t) tmp[t * BC + lane] = x[t];
+            for (int v = 0; v < BC / 4; ++v)
+                *reinterpret_cast<float4*>(tmp + OFF_TT + lane * BC + 4 * v) =
+                    make_float4(x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]);
         }
     } else if (wave == 1) {
-        // M = Tril(Qr Y^T)
+        // M = Tril(Qr Y^T), stored transposed
         f32x16 acc = zero16();
 #pragma unroll 8
         for (int k0 = 0; k0 < BD; k0 += 2)
@@ -200,28 +260,31 @@ __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = crow(r, lane);
-            tmp[BC * BC + i * BC + i0] = i0 <= i ? acc[r] : 0.f;
+            tmp[OFF_MT + i0 * BC + i] = i0 <= i ? acc[r] : 0.f;
         }
     }
 }
 
 // ---------------------------------------------------------------- pass 2
+// One workgroup of 8 waves per (sequence, head, 64 value columns): wave
+// (sw, rw) owns key rows 32 rw .. of value columns 64 sp + 32 sw ..  Per
+// chunk, walking backwards:
+//   phase 1  part = K_end[:, rows] dS_rows  (+ M^T dO on the rw = 1 waves),
+//            QdO = Q+^T dO for its rows;  partial sums to LDS
+//   phase 2  (rw = 0) dU = sum of the parts, W = T^T dU, to LDS and memory
+//   phase 3  dS = Diag(e^{g_C}) dS + QdO - (B_beta K+)^T W
+// Operands are read straight from the first pass's matrices in MFMA order;
+// each group is loaded for the next chunk as soon as this chunk's use ends.
 template <typename InT>
-__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
-    __shared__ float sKe[BC * LS];     // k e^{g_C - g}
-    __shared__ float sQp[BC * LS];     // q e^{g}
-    __shared__ float sKb[BC * LS];     // -beta k e^{g}
-    __shared__ float sdO[BC * LC], sM[BC * LC], sT[BC * LC], sW[BC * LC];
-    __shared__ float sPart[4][BC * LC];
-    __shared__ float sTot[2 * BD];
-    __shared__ float sGc[BD];
-    __shared__ float sBeta[BC];
+__global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
+    __shared__ float sPart[2][4][BC * LC];
+    __shared__ float sW[2][BC * LC];
 
     const int blk = blockIdx.x;
     const int xcd = blk & 7;
     const int grp = blk >> 3;
-    const int slice = grp & 3;
-    const int unit = (grp >> 2) * 8 + xcd;
+    const int sp = grp & 1;
+    const int unit = (grp >> 1) * 8 + xcd;
     if (unit >= p.n_seqs * p.H) return;
     const int n = unit / p.H, h = unit - n * p.H;
     const int H = p.H;
@@ -229,17 +292,79 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
     const int64_t nch = (t1 - t0 + BC - 1) / BC;
     const int64_t slot0 = t0 / BC + n;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = tid & (BD - 1), half = tid >> 7;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sw = wave >> 2, rw = wave & 3;
     const int i0 = lane & 31, kh = lane >> 5;
-    const int col = slice * 32 + i0;   // this lane's value column
+    const int col = 64 * sp + 32 * sw + i0;   // this lane's value column
+    const int row0 = 32 * rw;                 // this wave's first key row
     const size_t unit_el = ((size_t)n * H + h) * (BD * BD);
+    const int rowb = H * BD * 4;
 
-    // dS rows 32 wave + crow(r), column col
+    // Operands, loaded for the next chunk as soon as this chunk's use ends.
+    // Group A (phase 1): K_end^T entries, Q+^T row, e^{g_C} of the rows, the
+    // dO column and, on the rw = 1 waves, the M^T row.  The T^T row of the
+    // rw = 0 waves (phase 2) shares the registers of the M^T row.  Group B
+    // (phase 3): the Kb^T row.
+    float ke[16], dOr[16];
+    float4 qt[4], gc[4], spc[4], kbt[4];
+    // buffer loads: one per-lane offset register per operand, the per-load
+    // part of the offset in the scalar offset
+    auto tmp_rsrc = [&](int64_t j) {
+        return make_rsrc(p.tmp + ((size_t)(slot0 + j) * H + h) * TMP_ELEMS, TMP_ELEMS * 4);
+    };
+    auto ld1 = [](__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
+    };
+    auto ld4 = [](__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
+        return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                           __uint_as_float(u[3]));
+    };
+    const int vo_ke = ((row0 + 4 * kh) * BC + i0) * 4;   // + (8 (r/4) + r%4) rows
+    const int vo_row = ((row0 + i0) * BC + 4 * kh) * 4;  // row row0 + i0 of a [128][32] matrix
+    const int vo_sq = (i0 * BC + 4 * kh) * 4;             // row i0 of a [32][32] matrix
+    const int vo_gc = (row0 + 4 * kh) * 4;
+    auto load_a = [&](int64_t j) {
+        const int64_t c0 = t0 + j * BC;
+        const int nv = (int)(t1 - c0 < BC ? t1 - c0 : BC);
+        const auto rt = tmp_rsrc(j);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            ke[r] = ld1(rt, vo_ke, (OFF_KE + (8 * (r >> 2) + (r & 3)) * BC) * 4);
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            qt[m4] = ld4(rt, vo_row, (OFF_QT + 8 * m4) * 4);
+            gc[m4] = ld4(rt, vo_gc, (OFF_GC + 8 * m4) * 4);
+            if (rw == 1) spc[m4] = ld4(rt, vo_sq, (OFF_MT + 8 * m4) * 4);
+        }
+        const auto rdo = make_rsrc(p.dO + (c0 * H + h) * BD, (nv - 1) * rowb + BD * 4);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dOr[r] = ld1(rdo, crow(r, lane) * rowb + col * 4, 0);   // range-checked offset
+    };
+    auto load_t = [&](int64_t j) {   // rw = 0 waves
+        const auto rt = tmp_rsrc(j);
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) spc[m4] = ld4(rt, vo_sq, (OFF_TT + 8 * m4) * 4);
+    };
+    auto load_b = [&](int64_t j) {
+        const auto rt = tmp_rsrc(j);
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) kbt[m4] = ld4(rt, vo_row, (OFF_KB + 8 * m4) * 4);
+    };
+    auto f4 = [](const float4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; };
+
+    // dS rows row0 + crow(r), column col
     f32x16 dS;
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-        dS[r] = p.dS_T ? p.dS_T[unit_el + (size_t)(32 * wave + crow(r, lane)) * BD + col] : 0.f;
+        dS[r] = p.dS_T ? p.dS_T[unit_el + (size_t)(row0 + crow(r, lane)) * BD + col] : 0.f;
+    if (nch > 0) {
+        load_a(nch - 1);
+        if (rw == 0) load_t(nch - 1);
+        load_b(nch - 1);
+    }
 
     for (int64_t j = nch - 1; j >= 0; --j) {
         const int64_t c0 = t0 + j * BC;
@@ -248,93 +373,54 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
         // gradient at the end of this chunk
         float* dsn = p.dsn + sl * (BD * BD);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dsn[(size_t)(32 * wave + crow(r, lane)) * BD + col] = dS[r];
+        for (int r = 0; r < 16; ++r) dsn[(size_t)(row0 + crow(r, lane)) * BD + col] = dS[r];
 
-        // operands of the chunk
-        float g[16];
-        chunk_scan(p.la, c0, nv, H, h, c, half, g, sTot);
-        if (tid < BC) sBeta[tid] = tid < nv ? p.beta[(c0 + tid) * H + h] : 0.f;
-        {
-            const float* tm = p.tmp + sl * TMP_ELEMS;
+        // ---- phase 1 (the k order of every product below pairs row / token
+        // crow(r, lane) of the two lane halves; r = 4 m4 + s)
+        f32x16 part = zero16();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int idx = tid + 256 * e;   // 0..1023
-                const int r = idx >> 5, cc = idx & 31;
-                sT[r * LC + cc] = tm[idx];
-                sM[r * LC + cc] = tm[BC * BC + idx];
-                sdO[r * LC + cc] = r < nv ? p.dO[((c0 + r) * H + h) * BD + slice * 32 + cc] : 0.f;
-            }
+        for (int r = 0; r < 16; ++r) part = mma(ke[r], dS[r], part);
+        if (rw == 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part = mma(f4(spc[r >> 2], r & 3), dOr[r], part);
         }
-        __syncthreads();
-        {
-            const float off = half ? sTot[c] : 0.f;
-            const float gC = sTot[c] + sTot[BD + c];
-            if (half == 0) sGc[c] = expf(gC);
+        // dS <- Diag(e^{g_C}) dS + Q+^T dO
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = 16 * half + i;
-                const int64_t idx = ((c0 + t) * H + h) * BD + c;
-                const float kf = t < nv ? ld_in<InT>(p.k, idx) : 0.f;
-                const float qf = t < nv ? ld_in<InT>(p.q, idx) : 0.f;
-                const float gt = g[i] + off;
-                const float G = expf(gt);
-                sKe[t * LS + c] = kf * expf(gC - gt);
-                sQp[t * LS + c] = qf * G;
-                sKb[t * LS + c] = -sBeta[t] * kf * G;
-            }
-        }
-        __syncthreads();
-        // K_end (this wave's 32 key rows) times its dS rows, k in accumulator order
-        {
-            f32x16 part = zero16();
+        for (int r = 0; r < 16; ++r) dS[r] *= f4(gc[r >> 2], r & 3);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                part = mma(sKe[i0 * LS + 32 * wave + crow(r, lane)], dS[r], part);
+        for (int r = 0; r < 16; ++r) dS = mma(f4(qt[r >> 2], r & 3), dOr[r], dS);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sPart[wave][crow(r, lane) * LC + i0] = part[r];
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // dU = M^T dO + sum of the partial products;  W = T^T dU
-            f32x16 dU = zero16();
-#pragma unroll
-            for (int k0 = 0; k0 < BC; k0 += 2)
-                dU = mma(sM[(k0 + kh) * LC + i0], sdO[(k0 + kh) * LC + i0], dU);
+        for (int r = 0; r < 16; ++r) sPart[sw][rw][crow(r, lane) * LC + i0] = part[r];
+        if (j > 0) load_a(j - 1);
+        lds_barrier();
+        // ---- phase 2: W = T^T dU
+        if (rw == 0) {
+            f32x16 W = zero16();
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int e = crow(r, lane) * LC + i0;
-                dU[r] += (sPart[0][e] + sPart[1][e]) + (sPart[2][e] + sPart[3][e]);
+                const float dU = (sPart[sw][0][e] + sPart[sw][1][e]) + (sPart[sw][2][e] + sPart[sw][3][e]);
+                W = mma(f4(spc[r >> 2], r & 3), dU, W);
             }
-            f32x16 W = zero16();
-#pragma unroll
-            for (int r = 0; r < 16; ++r) W = mma(sT[crow(r, lane) * LC + i0], dU[r], W);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int t = crow(r, lane);
-                sW[t * LC + i0] = W[r];
-                if (t < nv) {
-                    const size_t o = ((size_t)(c0 + t) * H + h) * BD + col;
-                    p.w[o] = W[r];
-                    p.dv[o] = sBeta[t] * W[r];
-                }
+                sW[sw][t * LC + i0] = W[r];
+                if (t < nv) p.w[((size_t)(c0 + t) * H + h) * BD + col] = W[r];
             }
+            if (j > 0) load_t(j - 1);
         }
-        __syncthreads();
-        // dS <- Diag(e^{g_C}) dS + Q+^T dO - K+^T Diag(beta) W
+        lds_barrier();
+        // ---- phase 3: dS <- dS - (B_beta K+)^T W
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dS[r] *= sGc[32 * wave + crow(r, lane)];
-#pragma unroll
-        for (int k0 = 0; k0 < BC; k0 += 2) {
-            const int t = k0 + kh;
-            dS = mma(sQp[t * LS + 32 * wave + i0], sdO[t * LC + i0], dS);
-            dS = mma(sKb[t * LS + 32 * wave + i0], sW[t * LC + i0], dS);
-        }
-        __syncthreads();
+        for (int r = 0; r < 16; ++r)
+            dS = mma(f4(kbt[r >> 2], r & 3), sW[sw][crow(r, lane) * LC + i0], dS);
+        if (j > 0) load_b(j - 1);
     }
     if (p.dS0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            p.dS0[unit_el + (size_t)(32 * wave + crow(r, lane)) * BD + col] = dS[r];
+            p.dS0[unit_el + (size_t)(row0 + crow(r, lane)) * BD + col] = dS[r];
     }
 }
 
@@ -396,20 +482,22 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
                 const size_t o = ((size_t)(c0 + r) * H + h) * BD + cc;
                 a = *reinterpret_cast<const float4*>(p.dO + o);
                 b = *reinterpret_cast<const float4*>(p.w + o);
+                const float bt = p.beta[(c0 + r) * H + h];   // dv = beta W
+                *reinterpret_cast<float4*>(p.dv + o) = make_float4(bt * b.x, bt * b.y, bt * b.z, bt * b.w);
             }
             sA2[r * LS + cc] = a.x; sA2[r * LS + cc + 1] = a.y;
             sA2[r * LS + cc + 2] = a.z; sA2[r * LS + cc + 3] = a.w;
             sA3[r * LS + cc] = b.x; sA3[r * LS + cc + 1] = b.y;
             sA3[r * LS + cc + 2] = b.z; sA3[r * LS + cc + 3] = b.w;
         }
-        const float* tm = p.tmp + sl * TMP_ELEMS;
+        const float* tm = p.tmp + sl * TMP_ELEMS + OFF_TT;   // T^T
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int idx = tid + 256 * e;
-            sT[(idx >> 5) * LC + (idx & 31)] = tm[idx];
+            sT[(idx & 31) * LC + (idx >> 5)] = tm[idx];
         }
     }
-    __syncthreads();
+    lds_barrier();
     const float e0 = sTot[c];
     const float gC = sTot[c] + sTot[BD + c];
     const float off = half ? e0 : 0.f;
@@ -418,7 +506,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
         const int t = 16 * half + i;
         sA1[t * LS + c] = kv[i] * expf(g[i] + off);   // K+ (may underflow: only ever small)
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 1: R = V - K+ S, dbeta (first part), U = T Diag(beta) R
     const int vcol = 32 * wave + i0;   // value column (phase 1) / key column (later)
@@ -447,7 +535,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sU[crow(r, lane) * LS + vcol] = U[r];
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 2: dM = dO U^T (waves 0, 1), dA' = W U^T (waves 2, 3), each
     // pair splitting the value columns; X1 = dO S^T, X2 = W S^T for key
@@ -471,12 +559,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
             X2 = mma(sA3[i0 * LS + k0 + kh], b, X2);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 3: finish dM / dA'; Sn over S with rowsum(Sn * S); X, Y, Qr
     if (!(wave & 1)) {
         float* dst = wave == 0 ? sdM : sdA;
-        const float* P = p.tmp + sl * TMP_ELEMS + 2 * BC * BC;
+        const float* P = p.tmp + sl * TMP_ELEMS + OFF_P;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = crow(r, lane);
@@ -514,7 +602,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
         sA2[t * LS + c] = kv[i] * fy;
         sA3[t * LS + c] = qv[i] * fx;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 4: X3 = U Sn^T, Y1 = dM Y, Y2 = dPm Y, Y34 = dM^T Qr + dPm^T X
     f32x16 X3 = zero16(), Y1 = zero16(), Y2 = zero16(), Y34 = zero16();
@@ -530,11 +618,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
         Y34 = mma(sdM[t * LC + i0], sA3[t * LS + vcol], Y34);
         Y34 = mma(sdA[t * LC + i0], sA1[t * LS + vcol], Y34);
     }
-    __syncthreads();
+    lds_barrier();
     // g (with the half offset) for the elementwise phase
 #pragma unroll
     for (int i = 0; i < 16; ++i) sU[(16 * half + i) * LS + c] = g[i] + off;
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 5: chain rule through the scalings, per (token, key column)
     {
@@ -565,7 +653,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
         for (int r = 0; r < 16; ++r) sA1[crow(r, lane) * LS + vcol] = dgv[r];
         if (kh == 0) sGx[vcol] = colsum + expf(GC) * sRow[vcol];
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < BD) {
         // dlog_alpha_r = sum_{t >= r} dg_t + dg_C, over the chunk's tokens
         float run = sGx[tid];
@@ -589,9 +677,9 @@ hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream
         else hipLaunchKernelGGL(bwd_tmp_kernel<float>, dim3((unsigned)chunks), dim3(256), 0, stream, p);
     }
     if (units > 0) {
-        const dim3 grid((unsigned)(((units + 7) / 8) * 8 * 4));
-        if (bf16_in) hipLaunchKernelGGL(bwd_scan_kernel<__bf16>, grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(bwd_scan_kernel<float>, grid, dim3(256), 0, stream, p);
+        const dim3 grid((unsigned)(((units + 7) / 8) * 8 * 2));
+        if (bf16_in) hipLaunchKernelGGL(bwd_scan_kernel<__bf16>, grid, dim3(512), 0, stream, p);
+        else hipLaunchKernelGGL(bwd_scan_kernel<float>, grid, dim3(512), 0, stream, p);
     }
     if (chunks > 0) {
         if (bf16_in) hipLaunchKernelGGL(bwd_grad_kernel<__bf16>, dim3((unsigned)chunks), dim3(256), 0, stream, p);

@@ -107,12 +107,6 @@ __device__ __forceinline__ float in_f32(InT x) {
     return to_f32(x);
 }
 
-// Raw buffer resource over `bytes` bytes from `base`: loads at offsets
-// beyond the range return 0, which masks the tokens past a sequence's end
-// without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
 
 __device__ __forceinline__ float2 bf2_to_f2(uint32_t u) {
     return make_float2(bf2_first(u), bf2_second(u));
