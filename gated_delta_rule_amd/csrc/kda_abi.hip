@@ -187,6 +187,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     p.seg_per_seq = 1;
     p.s0_identity = 0;
     p.h_states = nullptr;
+    p.r_out = nullptr;
+    p.u_out = nullptr;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -404,10 +406,10 @@ int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, i
 
 // Backward workspace layout (floats): states at chunk starts and gradients
 // at chunk ends [slots, H, 128, 128] each, the chunk matrices of the first
-// backward pass [slots, H, kBwdChunkElems], W [tokens, H, 128];
-// slots = tokens / 32 + n_seqs.
+// backward pass [slots, H, kBwdChunkElems], and W, V - K+ S and U of every
+// token [tokens, H, 128] each; slots = tokens / 32 + n_seqs.
 struct BwdLayout {
-    int64_t slots, h, dsn, tmp, w, total;   // offsets and total in floats
+    int64_t slots, h, dsn, tmp, w, r, u, total;   // offsets and total in floats
 };
 static bool bwd_layout(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayout* L) {
     L->slots = tokens / kChunk + n_seqs;
@@ -419,7 +421,9 @@ static bool bwd_layout(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayout* L) 
     L->dsn = st;
     L->tmp = 2 * st;
     L->w = 2 * st + tmp;
-    L->total = 2 * st + tmp + wv;
+    L->r = L->w + wv;
+    L->u = L->r + wv;
+    L->total = 2 * st + tmp + 3 * wv;
     return L->total >= 0 && L->total <= INT64_MAX / 8;
 }
 
@@ -523,6 +527,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     p.n_slices = n_slices;
     p.n_units = (int32_t)units;
     p.h_states = ws + L.h;
+    p.r_out = ws + L.r;
+    p.u_out = ws + L.u;
     const bool bf16_in = in_dtype == KDA_BF16;
     hipError_t e = kda::launch_chunk_fwd(p, bf16_in, wcols, false, stream);
     if (e != hipSuccess) return KDA_ERR_HIP;
@@ -543,6 +549,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     b.dbeta = grad_beta;
     b.dS0 = grad_S0;
     b.h = ws + L.h;
+    b.r = ws + L.r;
+    b.u = ws + L.u;
     b.dsn = ws + L.dsn;
     b.tmp = ws + L.tmp;
     b.w = ws + L.w;

@@ -120,22 +120,6 @@ __device__ Chunk slot_chunk(const BwdParams& p, int64_t m) {
     return c;
 }
 
-// Decay scan of one chunk by 256 threads: thread (channel c = tid % 128,
-// half = tid / 128) sums log alpha over tokens 16 half .. 16 half + 15.
-// Returns the running sums in g[] (without the other half's offset) and
-// leaves both halves' totals in tot[2][128].
-__device__ __forceinline__ void chunk_scan(const float* la, int64_t c0, int nv, int H, int h,
-                                           int c, int half, float (&g)[16], float* tot) {
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = 16 * half + i;
-        a += t < nv ? la[((c0 + t) * H + h) * BD + c] : 0.f;
-        g[i] = a;
-    }
-    tot[half * BD + c] = a;
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------- pass 1
@@ -425,19 +409,21 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- pass 3
+// One workgroup (4 waves) per (chunk, head).  Wave w owns key columns
+// 32 w .. 32 w + 31 of every [32 tokens x 128 keys] gradient; lane
+// (i0, kh) holds key column dk = 32 w + i0 and tokens t = crow(r, lane),
+// r = 0..15, both in the accumulators and in its per-element values (q, k,
+// decay sums), so the chain rule needs no data movement.  The products
+// over the value columns stream rows of dO, W, U (token i0) and of S, Sn
+// (key dk) from memory, 4 consecutive value columns per lane and load:
+// the k order pairs column 8 m + s (lanes 0-31) with 8 m + 4 + s.
 template <typename InT>
-__global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
-    __shared__ float sS[BD * LS];      // S, then Sn, then g
-    __shared__ float sA1[BC * LS];     // K+, then X, then dg
-    __shared__ float sA2[BC * LS];     // dO, then Y
-    __shared__ float sA3[BC * LS];     // W, then Qr
-    __shared__ float sU[BC * LS];      // U, then g
-    __shared__ float sT[BC * LC];
-    __shared__ float sdM[BC * LC], sdA[BC * LC];
-    __shared__ float sTot[2 * BD];
-    __shared__ float sRow[BD], sGx[BD];
-    __shared__ float sBeta[BC];
+__global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
+    __shared__ float sPm[4][BC * LC];   // dM by value quarter
+    __shared__ float sPa[4][BC * LC];   // dA' by value quarter
+    __shared__ float sdM[BC * LC], sdP[BC * LC];   // dM, dPm = -Diag(beta) dA'
     __shared__ float sDb[5][BC];
+    __shared__ float sBeta[BC];
 
     const int64_t m = blockIdx.x / p.H;
     const int h = (int)(blockIdx.x - m * p.H);
@@ -446,227 +432,200 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdParams p) {
     const int H = p.H, nv = ch.nv;
     const int64_t c0 = ch.c0;
     const size_t sl = (size_t)m * H + h;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = tid & (BD - 1), half = tid >> 7;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i0 = lane & 31, kh = lane >> 5;
+    const int dk = 32 * wave + i0;
+    const int rowb = H * BD * 4;
+    const int64_t e0i = (c0 * H + h) * BD;
+    const int span = (nv - 1) * rowb + BD * 4;
+    constexpr int ES = (int)sizeof(InT);
+    auto ld1 = [](__amdgpu_buffer_rsrc_t r, int vo) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, vo, 0, 0));
+    };
+    auto ld4 = [](__amdgpu_buffer_rsrc_t r, int vo) {
+        const u32x4 u = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, 0, 0));
+        return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
+                           __uint_as_float(u[3]));
+    };
+    auto f4 = [](const float4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; };
+    // token-major tiles of this chunk (rows past the sequence end read 0)
+    const auto rdo = make_rsrc(p.dO + e0i, span);
+    const auto rw = make_rsrc(p.w + e0i, span);
+    const auto ru = make_rsrc(p.u + e0i, span);
+    const auto rr = make_rsrc(p.r + e0i, span);
+    const auto rla = make_rsrc(p.la + e0i, span);
+    const auto rk = make_rsrc((const InT*)p.k + e0i, span / (4 / ES));
+    const auto rq = make_rsrc((const InT*)p.q + e0i, span / (4 / ES));
+    const auto rb = make_rsrc(p.beta + c0 * H + h, ((nv - 1) * H + 1) * 4);
+    const auto rs_ = make_rsrc(p.h + sl * (BD * BD), BD * BD * 4);
+    const auto rsn = make_rsrc(p.dsn + sl * (BD * BD), BD * BD * 4);
 
-    // ---- phase 0: loads
-    float g[16], kv[16], qv[16];
-    chunk_scan(p.la, c0, nv, H, h, c, half, g, sTot);
+    // per-element values at (t = crow(r), dk)
+    float lav[16], kv[16], qv[16], bv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = 16 * half + i;
-        const int64_t idx = ((c0 + t) * H + h) * BD + c;
-        kv[i] = t < nv ? ld_in<InT>(p.k, idx) : 0.f;
-        qv[i] = t < nv ? ld_in<InT>(p.q, idx) : 0.f;
+    for (int r = 0; r < 16; ++r) {
+        const int t = crow(r, lane);
+        lav[r] = ld1(rla, t * rowb + dk * 4);
+        if constexpr (ES == 4) {
+            kv[r] = ld1(rk, t * rowb + dk * 4);
+            qv[r] = ld1(rq, t * rowb + dk * 4);
+        } else {
+            kv[r] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rk, t * (rowb / 2) + dk * 2, 0, 0) << 16);
+            qv[r] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, t * (rowb / 2) + dk * 2, 0, 0) << 16);
+        }
+        bv[r] = ld1(rb, t * H * 4);
     }
-    if (tid < BC) sBeta[tid] = tid < nv ? p.beta[(c0 + tid) * H + h] : 0.f;
+    if (tid < BC) sBeta[tid] = ld1(rb, tid * H * 4);
     {
-        const float* hs = p.h + sl * (BD * BD);
-#pragma unroll 4
-        for (int e = 0; e < 16; ++e) {
-            const int idx = (tid + 256 * e) * 4;   // float4 index * 4
-            const int r = idx >> 7, cc = idx & 127;
-            const float4 v4 = *reinterpret_cast<const float4*>(hs + idx);
-            sS[r * LS + cc] = v4.x;
-            sS[r * LS + cc + 1] = v4.y;
-            sS[r * LS + cc + 2] = v4.z;
-            sS[r * LS + cc + 3] = v4.w;
-        }
+        // dv = Diag(beta) W: token tid / 8, value columns 16 (tid % 8) ..
+        const int t = tid >> 3, v0 = 16 * (tid & 7);
+        if (t < nv) {
+            const float bt = ld1(rb, t * H * 4);
+            float* dst = p.dv + ((size_t)(c0 + t) * H + h) * BD + v0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = (tid + 256 * e) * 4;
-            const int r = idx >> 7, cc = idx & 127;
-            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-            if (r < nv) {
-                const size_t o = ((size_t)(c0 + r) * H + h) * BD + cc;
-                a = *reinterpret_cast<const float4*>(p.dO + o);
-                b = *reinterpret_cast<const float4*>(p.w + o);
-                const float bt = p.beta[(c0 + r) * H + h];   // dv = beta W
-                *reinterpret_cast<float4*>(p.dv + o) = make_float4(bt * b.x, bt * b.y, bt * b.z, bt * b.w);
+            for (int v = 0; v < 4; ++v) {
+                const float4 w4 = ld4(rw, t * rowb + (v0 + 4 * v) * 4);
+                *reinterpret_cast<float4*>(dst + 4 * v) = make_float4(bt * w4.x, bt * w4.y, bt * w4.z, bt * w4.w);
             }
-            sA2[r * LS + cc] = a.x; sA2[r * LS + cc + 1] = a.y;
-            sA2[r * LS + cc + 2] = a.z; sA2[r * LS + cc + 3] = a.w;
-            sA3[r * LS + cc] = b.x; sA3[r * LS + cc + 1] = b.y;
-            sA3[r * LS + cc + 2] = b.z; sA3[r * LS + cc + 3] = b.w;
         }
-        const float* tm = p.tmp + sl * TMP_ELEMS + OFF_TT;   // T^T
+    }
+
+    // ---- products over the value columns
+    f32x16 X1 = zero16(), X2 = zero16(), X3 = zero16();
+    float rsum = 0.f;   // row dk of Sn * S
+    const int vo_tok = i0 * rowb + 4 * kh * 4;   // token i0, columns 4 kh ..
+    const int vo_key = (dk * BD + 4 * kh) * 4;   // key row dk, columns 4 kh ..
+#pragma unroll 4
+    for (int m8 = 0; m8 < 16; ++m8) {
+        const float4 a_do = ld4(rdo, vo_tok + 32 * m8), a_w = ld4(rw, vo_tok + 32 * m8);
+        const float4 a_u = ld4(ru, vo_tok + 32 * m8);
+        const float4 b_s = ld4(rs_, vo_key + 32 * m8), b_sn = ld4(rsn, vo_key + 32 * m8);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            X1 = mma(f4(a_do, s4), f4(b_s, s4), X1);
+            X2 = mma(f4(a_w, s4), f4(b_s, s4), X2);
+            X3 = mma(f4(a_u, s4), f4(b_sn, s4), X3);
+            rsum += f4(b_s, s4) * f4(b_sn, s4);
+        }
+    }
+    rsum += swap_halves(rsum);
+    {
+        // dM = dO U^T and dA' = W U^T over this wave's value quarter, and
+        // the quarter's W . R per token
+        f32x16 PM = zero16(), PA = zero16();
+        float db = 0.f;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int o = vo_tok + 32 * (4 * wave + q4);
+            const float4 a_do = ld4(rdo, o), a_w = ld4(rw, o), a_u = ld4(ru, o), a_r = ld4(rr, o);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                PM = mma(f4(a_do, s4), f4(a_u, s4), PM);
+                PA = mma(f4(a_w, s4), f4(a_u, s4), PA);
+                db += f4(a_w, s4) * f4(a_r, s4);
+            }
+        }
+        db += swap_halves(db);
+        if (kh == 0) sDb[wave][i0] = db;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            sPm[wave][crow(r, lane) * LC + i0] = PM[r];
+            sPa[wave][crow(r, lane) * LC + i0] = PA[r];
+        }
+    }
+    lds_barrier();
+    {
+        // dM (j <= t), dPm = -beta_t dA' (j < t), dbeta_t -= sum_j dA'_tj P_tj
+        const auto rt = make_rsrc(p.tmp + sl * TMP_ELEMS, TMP_ELEMS * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int idx = tid + 256 * e;
-            sT[(idx & 31) * LC + (idx >> 5)] = tm[idx];
+            const int t = idx >> 5, j = idx & 31;
+            const int o = t * LC + j;
+            const float dm = (sPm[0][o] + sPm[1][o]) + (sPm[2][o] + sPm[3][o]);
+            const float da = j < t ? (sPa[0][o] + sPa[1][o]) + (sPa[2][o] + sPa[3][o]) : 0.f;
+            sdM[o] = j <= t ? dm : 0.f;
+            sdP[o] = -sBeta[t] * da;
+            const float s2 = half_sum_dpp(-da * ld1(rt, (OFF_P + idx) * 4));
+            if (j == 0) sDb[4][t] = s2;
         }
     }
     lds_barrier();
-    const float e0 = sTot[c];
-    const float gC = sTot[c] + sTot[BD + c];
-    const float off = half ? e0 : 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = 16 * half + i;
-        sA1[t * LS + c] = kv[i] * expf(g[i] + off);   // K+ (may underflow: only ever small)
-    }
-    lds_barrier();
 
-    // ---- phase 1: R = V - K+ S, dbeta (first part), U = T Diag(beta) R
-    const int vcol = 32 * wave + i0;   // value column (phase 1) / key column (later)
-    f32x16 U;
+    // ---- decay sums at the lane's tokens: prefix over t with the partner
+    // half (lane ^ 32) holding the other four tokens of every group of eight
+    float g[16], gC, E0;
     {
-        f32x16 R = zero16();
-#pragma unroll 8
-        for (int k0 = 0; k0 < BD; k0 += 2)
-            R = mma(sA1[i0 * LS + k0 + kh], sS[(k0 + kh) * LS + vcol], R);
+        float run = 0.f, e0 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int t = crow(r, lane);
-            const float vv = t < nv ? ld_in<InT>(p.v, ((c0 + t) * H + h) * BD + vcol) : 0.f;
-            R[r] = vv - R[r];
-        }
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const float G = lav[4 * m4] + lav[4 * m4 + 1] + lav[4 * m4 + 2] + lav[4 * m4 + 3];
+            const float P = swap_halves(G);
+            float a = run + (kh ? P : 0.f);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float s = half_sum_dpp(sA3[crow(r, lane) * LS + vcol] * R[r]);
-            if (i0 == 0) sDb[wave][crow(r, lane)] = s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) R[r] *= sBeta[crow(r, lane)];
-        U = zero16();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) U = mma(sT[i0 * LC + crow(r, lane)], R[r], U);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sU[crow(r, lane) * LS + vcol] = U[r];
-    }
-    lds_barrier();
-
-    // ---- phase 2: dM = dO U^T (waves 0, 1), dA' = W U^T (waves 2, 3), each
-    // pair splitting the value columns; X1 = dO S^T, X2 = W S^T for key
-    // columns 32 wave ..
-    f32x16 X1 = zero16(), X2 = zero16(), CC = zero16();
-    {
-        const float* Ain = wave < 2 ? sA2 : sA3;
-        const int kb = (wave & 1) * 64;
-#pragma unroll 8
-        for (int k0 = 0; k0 < 64; k0 += 2)
-            CC = mma(Ain[i0 * LS + kb + k0 + kh], sU[i0 * LS + kb + k0 + kh], CC);
-        if (wave & 1) {
-            float* dst = wave == 1 ? sdM : sdA;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dst[crow(r, lane) * LC + i0] = CC[r];
-        }
-#pragma unroll 8
-        for (int k0 = 0; k0 < BD; k0 += 2) {
-            const float b = sS[vcol * LS + k0 + kh];
-            X1 = mma(sA2[i0 * LS + k0 + kh], b, X1);
-            X2 = mma(sA3[i0 * LS + k0 + kh], b, X2);
-        }
-    }
-    lds_barrier();
-
-    // ---- phase 3: finish dM / dA'; Sn over S with rowsum(Sn * S); X, Y, Qr
-    if (!(wave & 1)) {
-        float* dst = wave == 0 ? sdM : sdA;
-        const float* P = p.tmp + sl * TMP_ELEMS + OFF_P;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = crow(r, lane);
-            const float v = CC[r] + dst[i * LC + i0];
-            if (wave == 0) {
-                dst[i * LC + i0] = i0 <= i ? v : 0.f;                       // dM
-            } else {
-                const float da = i0 < i ? v : 0.f;                          // dA'
-                dst[i * LC + i0] = -sBeta[i] * da;                          // dPm
-                const float s = half_sum_dpp(-da * P[i * BC + i0]);
-                if (i0 == 0) sDb[4][i] = s;
+            for (int s4 = 0; s4 < 4; ++s4) {
+                a += lav[4 * m4 + s4];
+                g[4 * m4 + s4] = a;
             }
+            run += G + P;
+            if (m4 == 1) e0 = run;   // tokens 0..15
+        }
+        gC = run;
+        E0 = e0;
+    }
+    // ---- products over the chunk's tokens
+    f32x16 Y1 = zero16(), Y2 = zero16(), Y34 = zero16();
+    float Gr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int t = crow(r, lane);
+        Gr[r] = expf(g[r] - E0);
+        const float Gri = expf(E0 - g[r]);
+        const float yr = kv[r] * Gri;
+        Y1 = mma(sdM[i0 * LC + t], yr, Y1);
+        Y2 = mma(sdP[i0 * LC + t], yr, Y2);
+        Y34 = mma(sdM[t * LC + i0], qv[r] * Gr[r], Y34);
+        Y34 = mma(sdP[t * LC + i0], kv[r] * Gr[r], Y34);
+    }
+
+    // ---- chain rule through the scalings; dlog_alpha by suffix sums
+    float dg[16], colsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int t = crow(r, lane);
+        const float G = expf(g[r]), Ge = expf(gC - g[r]), Gri = expf(E0 - g[r]);
+        const float dq = X1[r] * G + Y1[r] * Gr[r];
+        const float dkp = -bv[r] * X2[r] * G + Y2[r] * Gr[r];
+        const float dkm = Y34[r] * Gri;
+        const float dke = X3[r] * Ge;
+        dg[r] = qv[r] * dq + kv[r] * (dkp - dkm - dke);
+        colsum += kv[r] * dke;
+        if (t < nv) {
+            const size_t o = ((size_t)(c0 + t) * H + h) * BD + dk;
+            p.dq[o] = dq;
+            p.dk[o] = dkp + dkm + dke;
         }
     }
+    colsum += swap_halves(colsum);
     {
-        const float* sn = p.dsn + sl * (BD * BD);
-        const int r = tid >> 1, cb = (tid & 1) * 64;
-        float acc = 0.f;
-#pragma unroll 4
-        for (int e = 0; e < 16; ++e) {
-            const float4 v4 = *reinterpret_cast<const float4*>(sn + r * BD + cb + 4 * e);
-            float* d = &sS[r * LS + cb + 4 * e];
-            acc += v4.x * d[0] + v4.y * d[1] + v4.z * d[2] + v4.w * d[3];
-            d[0] = v4.x; d[1] = v4.y; d[2] = v4.z; d[3] = v4.w;
-        }
-        acc += dpp_mov<0xB1>(acc);   // partner thread tid ^ 1 holds the other half row
-        if (!(tid & 1)) sRow[r] = acc;
-    }
+        float run = colsum + expf(gC) * rsum;   // dg_C
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = 16 * half + i;
-        const float d = g[i] + off - e0;
-        const float fx = expf(d), fy = expf(-d);
-        sA1[t * LS + c] = kv[i] * fx;
-        sA2[t * LS + c] = kv[i] * fy;
-        sA3[t * LS + c] = qv[i] * fx;
-    }
-    lds_barrier();
-
-    // ---- phase 4: X3 = U Sn^T, Y1 = dM Y, Y2 = dPm Y, Y34 = dM^T Qr + dPm^T X
-    f32x16 X3 = zero16(), Y1 = zero16(), Y2 = zero16(), Y34 = zero16();
-#pragma unroll 8
-    for (int k0 = 0; k0 < BD; k0 += 2)
-        X3 = mma(sU[i0 * LS + k0 + kh], sS[vcol * LS + k0 + kh], X3);
+        for (int m4 = 3; m4 >= 0; --m4) {
+            const float G = dg[4 * m4] + dg[4 * m4 + 1] + dg[4 * m4 + 2] + dg[4 * m4 + 3];
+            const float P = swap_halves(G);
+            float a = run + (kh ? 0.f : P);
 #pragma unroll
-    for (int k0 = 0; k0 < BC; k0 += 2) {
-        const int t = k0 + kh;
-        const float y = sA2[t * LS + vcol];
-        Y1 = mma(sdM[i0 * LC + t], y, Y1);
-        Y2 = mma(sdA[i0 * LC + t], y, Y2);
-        Y34 = mma(sdM[t * LC + i0], sA3[t * LS + vcol], Y34);
-        Y34 = mma(sdA[t * LC + i0], sA1[t * LS + vcol], Y34);
-    }
-    lds_barrier();
-    // g (with the half offset) for the elementwise phase
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sU[(16 * half + i) * LS + c] = g[i] + off;
-    lds_barrier();
-
-    // ---- phase 5: chain rule through the scalings, per (token, key column)
-    {
-        const float E0 = sTot[vcol], GC = sTot[vcol] + sTot[BD + vcol];
-        float colsum = 0.f;
-        float dgv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int t = crow(r, lane);
-            const float gt = sU[t * LS + vcol];
-            const float G = expf(gt), Gr = expf(gt - E0), Gri = expf(E0 - gt), Ge = expf(GC - gt);
-            const int64_t idx = ((c0 + t) * H + h) * BD + vcol;
-            const float kf = t < nv ? ld_in<InT>(p.k, idx) : 0.f;
-            const float qf = t < nv ? ld_in<InT>(p.q, idx) : 0.f;
-            const float dq = X1[r] * G + Y1[r] * Gr;
-            const float dkp = -sBeta[t] * X2[r] * G + Y2[r] * Gr;
-            const float dkm = Y34[r] * Gri;
-            const float dke = X3[r] * Ge;
-            dgv[r] = qf * dq + kf * (dkp - dkm - dke);
-            colsum += kf * dke;
-            if (t < nv) {
-                p.dq[idx] = dq;
-                p.dk[idx] = dkp + dkm + dke;
+            for (int s4 = 3; s4 >= 0; --s4) {
+                a += dg[4 * m4 + s4];
+                const int t = 8 * m4 + 4 * kh + s4;
+                if (t < nv) p.dla[((size_t)(c0 + t) * H + h) * BD + dk] = a;
             }
+            run += G + P;
         }
-        colsum += swap_halves(colsum);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sA1[crow(r, lane) * LS + vcol] = dgv[r];
-        if (kh == 0) sGx[vcol] = colsum + expf(GC) * sRow[vcol];
     }
-    lds_barrier();
-    if (tid < BD) {
-        // dlog_alpha_r = sum_{t >= r} dg_t + dg_C, over the chunk's tokens
-        float run = sGx[tid];
-        for (int t = nv - 1; t >= 0; --t) {
-            run += sA1[t * LS + tid];
-            p.dla[((c0 + t) * H + h) * BD + tid] = run;
-        }
-    } else if (tid < BD + BC) {
-        const int t = tid - BD;
-        if (t < nv)
-            p.dbeta[(c0 + t) * H + h] =
-                ((sDb[0][t] + sDb[1][t]) + (sDb[2][t] + sDb[3][t])) + sDb[4][t];
-    }
+    if (tid < BC && tid < nv)
+        p.dbeta[(c0 + tid) * H + h] = ((sDb[0][tid] + sDb[1][tid]) + (sDb[2][tid] + sDb[3][tid])) + sDb[4][tid];
 }
 
 hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream) {

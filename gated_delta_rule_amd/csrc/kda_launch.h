@@ -31,6 +31,9 @@ struct PrefillParams {
     // (unsplit sequences only); chunk j of sequence n starting at token t0
     // goes to slot t0 / 32 + n + j, which no other chunk uses.
     float* h_states;
+    // With h_states: V - K+ S and U of every chunk, token-major like o.
+    float* r_out;
+    float* u_out;
 };
 
 // Enqueue the prefill (and, when `sort`, the sequence-order pass first).
@@ -97,6 +100,8 @@ struct BwdParams {
     float* dbeta;
     float* dS0;             // or nullptr (not wanted)
     const float* h;
+    const float* r;         // [tokens, H, 128]: V - K+ S of the forward pass
+    const float* u;         // [tokens, H, 128]: U of the forward pass
     float* dsn;
     float* tmp;
     float* w;

@@ -607,7 +607,21 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     }
                 }
             }
-            // R' = B_beta (V - K+ S)
+            // R' = B_beta (V - K+ S)  (V - K+ S itself kept for the backward pass)
+            if constexpr (STORE_H) {
+                const int64_t cs = t0 + cidx * CH;
+                const auto rr = make_rsrc(p.r_out + ((size_t)cs * H + h) * DK, span_bytes(n_valid(cs), 4));
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int el = (tb * 16 + g * 4 + r) * rowel + col0 + ct * 16 + ln;
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                __float_as_uint(pv[tb][ct][r] - R[tb][ct][r]), rr, el * 4, 0, 0);
+                        }
+            }
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -645,6 +659,19 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     for (int r = 0; r < 4; ++r) b[r] = rhs[r];
                     mma_k16<F32, SPLITB>(U1[ct], t11, b);
                 }
+            }
+            if constexpr (STORE_H) {
+                const int64_t cs = t0 + cidx * CH;
+                const auto ru = make_rsrc(p.u_out + ((size_t)cs * H + h) * DK, span_bytes(n_valid(cs), 4));
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int el = (g * 4 + r) * rowel + col0 + ct * 16 + ln;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(U0[ct][r]), ru, el * 4, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(U1[ct][r]), ru,
+                                                              (el + 16 * rowel) * 4, 0, 0);
+                    }
             }
             // U as the B operand of M U and Y^T U (tile order: U0 rows, U1 rows).
 #pragma unroll

@@ -230,8 +230,8 @@ int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, i
  * slots = tokens / 32 + n_seqs, it holds the state at the start and the
  * state gradient at the end of every 32-token chunk (2 * slots * H * 64 KiB),
  * the chunk's matrices (three 32 x 32, three 128 x 32 and one 128-vector of
- * fp32: slots * H * 61952 bytes) and one fp32 value row per token and head
- * (tokens * H * 512 bytes).  0 for invalid sizes.
+ * fp32: slots * H * 61952 bytes) and three fp32 value rows per token and
+ * head (tokens * H * 1536 bytes).  0 for invalid sizes.
  */
 size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
                                      int32_t dk, int32_t dv, int varlen);

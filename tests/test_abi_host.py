@@ -223,7 +223,7 @@ def test_bwd_workspace_query(lib):
     def expect(tokens, n, H):
         slots = tokens // 32 + n
         return (slots * H * (2 * 128 * 128 + 3 * 32 * 32 + 3 * 128 * 32 + 128)
-                + tokens * H * 128) * 4
+                + 3 * tokens * H * 128) * 4
     assert ws(1, 8192, 96, 128, 128, 0) == expect(8192, 1, 96)
     assert ws(3, 100, 2, 128, 128, 0) == expect(300, 3, 2)
     assert ws(32, 270000, 96, 128, 128, 1) == expect(270000, 32, 96)
