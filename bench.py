@@ -30,6 +30,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix
+PEAK_F32_TFLOPS = 157.3         # MI355X dense fp32 matrix
+# Backward pass, algorithmic flops per token and head: the forward pass it
+# repeats (131072) plus its own products per 32-token chunk (P, M: 2 x
+# 2*32*32*128; the state-gradient walk: K_end dS, Q+^T dO, Kb^T W at
+# 2*32*128*128 and M^T dO, T^T dU at 2*32*32*128; the gradient kernel: dO S^T,
+# W S^T, U Sn^T at 2*32*128*128 and dM, dA', dM Y, dPm Y, dM^T Qr, dPm^T X at
+# 2*32*32*128), 8912896 per chunk = 278528 per token.
+BWD_FLOPS_PER_TOKEN_HEAD = 131072 + 278528
 PREFILL_BYTES_PER_TOKEN_HEAD = 1796      # q,k,v bf16 768 + log alpha 512 + beta 4 + o fp32 512
 PREFILL_FLOPS_PER_TOKEN_HEAD = 131072    # chunkwise algorithm, 64-token chunks, d = 128
 STATE_BYTES = 128 * 128 * 4
@@ -194,6 +202,48 @@ def layer_steps(torch, kda, W, dev, reps=10):
             "bytes_per_token_head": {"prologue": bytes_p // th, "epilogue": bytes_e // th}}
 
 
+def backward_step(torch, kda, W, dev, reps=5):
+    """kda_chunk_bwd on the headline prefill shape (T=8192, H=96, bf16) with
+    an upstream gradient on o and on the final state (for information)."""
+    w = W.workload(1)
+    T, H = w.T, w.H
+    g = torch.Generator(device=dev).manual_seed(13)
+    shp = (1, T, H, 128)
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+    q = unit(torch.randn(shp, device=dev, generator=g)).to(torch.bfloat16)
+    k = unit(torch.randn(shp, device=dev, generator=g)).to(torch.bfloat16)
+    v = torch.randn(shp, device=dev, generator=g).to(torch.bfloat16)
+    la = -5.0 * torch.sigmoid(torch.randn(shp, device=dev, generator=g))
+    beta = torch.sigmoid(torch.randn((1, T, H), device=dev, generator=g))
+    go = torch.randn(shp, device=dev, generator=g)
+    gst = torch.randn((1, H, 128, 128), device=dev, generator=g)
+    ws = torch.empty(kda.load_library().kda_chunk_bwd_workspace_bytes(1, T, H, 128, 128, 0),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    kda.chunk_bwd(q, k, v, la, beta, None, go, gst, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        kda.chunk_bwd(q, k, v, la, beta, None, go, gst, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = BWD_FLOPS_PER_TOKEN_HEAD * T * H
+    del q, k, v, la, beta, go, gst, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"KDA backward B=1 T={T} H={H} d=128, bf16 q/k/v, fp32 gates, "
+                        "dL/do and dL/dS_T ~ N(0,1) (device-drawn)",
+            "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+            "algorithmic_flops": flops, "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
+            "mfma_f32_peak_tflops": PEAK_F32_TFLOPS,
+            "frac_f32_peak": flops / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
+            "passes": "forward keeping chunk states, V - K+S and U; chunk matrices; "
+                      "reverse state-gradient walk; per-chunk gradients"}
+
+
 def run_decode_only(args, torch, kda, W, dev):
     wd = W.workload(4)
     S = torch.from_numpy(W.decode_state(wd)).to(dev)
@@ -321,6 +371,7 @@ def main():
     long_ctx = None if args.no_long else long_context(torch, kda, W, dev)
     multi_tok = None if args.no_long else multi_token_decode(torch, kda, W, dev)
     layer = None if args.no_long else layer_steps(torch, kda, W, dev)
+    bwd = None if args.no_long else backward_step(torch, kda, W, dev)
 
     cpu = None
     if not args.no_cpu:
@@ -382,6 +433,7 @@ def main():
         "long_context_prefill": long_ctx,
         "multi_token_decode": multi_tok,
         "layer_prologue_epilogue": layer,
+        "backward": bwd,
         "wall_s_timed_prefill": t_wall,
     }
     print(json.dumps(out), flush=True)
