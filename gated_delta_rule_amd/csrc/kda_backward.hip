@@ -46,6 +46,8 @@
 // 8 (r / 4) + 4 (l / 32) + r % 4 (r = 0..15).  Like the forward, the k order
 // of a product is chosen so that accumulators feed the next product's B
 // operand without a round trip through LDS.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -73,6 +75,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mma(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+// bf16 matrix cores: acc += A B over 16 k, lane half kh supplying
+// k = 8 kh + j from element j of its operands
+__device__ __forceinline__ f32x16 mfb(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// Split-bf16 product of fp32 operands (hi + lo of each; lo * lo dropped,
+// about 2^-16 relative per term), small terms first.
+__device__ __forceinline__ f32x16 mma3(const SplitBF<8>& a, const SplitBF<8>& b, f32x16 c) {
+    c = mfb(a.lo, b.hi, c);
+    c = mfb(a.hi, b.lo, c);
+    return mfb(a.hi, b.hi, c);
 }
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
@@ -425,6 +439,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
     __shared__ float sDb[5][BC];
     __shared__ float sBeta[BC];
 
+    constexpr bool F32 = std::is_same<InT, float>::value;
     const int64_t m = blockIdx.x / p.H;
     const int h = (int)(blockIdx.x - m * p.H);
     const Chunk ch = slot_chunk(p, m);
@@ -491,22 +506,41 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
         }
     }
 
-    // ---- products over the value columns
+    // ---- products over the value columns: block mb covers columns
+    // 16 mb .. 16 mb + 15, lane half kh supplying 16 mb + 8 kh + j (j = 0..7).
+    // fp32 inputs: fp32 matrix cores, one k pair per instruction; bf16
+    // inputs: split-bf16 operands on bf16 matrix cores.
     f32x16 X1 = zero16(), X2 = zero16(), X3 = zero16();
     float rsum = 0.f;   // row dk of Sn * S
-    const int vo_tok = i0 * rowb + 4 * kh * 4;   // token i0, columns 4 kh ..
-    const int vo_key = (dk * BD + 4 * kh) * 4;   // key row dk, columns 4 kh ..
-#pragma unroll 4
-    for (int m8 = 0; m8 < 16; ++m8) {
-        const float4 a_do = ld4(rdo, vo_tok + 32 * m8), a_w = ld4(rw, vo_tok + 32 * m8);
-        const float4 a_u = ld4(ru, vo_tok + 32 * m8);
-        const float4 b_s = ld4(rs_, vo_key + 32 * m8), b_sn = ld4(rsn, vo_key + 32 * m8);
+    const int vo_tok = i0 * rowb + 8 * kh * 4;   // token i0, columns 8 kh ..
+    const int vo_key = (dk * BD + 8 * kh) * 4;   // key row dk, columns 8 kh ..
+    auto ld8 = [&](__amdgpu_buffer_rsrc_t r, int vo, float (&x)[8]) {
+        const float4 a = ld4(r, vo), b = ld4(r, vo + 16);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    };
+#pragma unroll 2
+    for (int mb = 0; mb < 8; ++mb) {
+        float a_do[8], a_w[8], a_u[8], b_s[8], b_sn[8];
+        ld8(rdo, vo_tok + 64 * mb, a_do);
+        ld8(rw, vo_tok + 64 * mb, a_w);
+        ld8(ru, vo_tok + 64 * mb, a_u);
+        ld8(rs_, vo_key + 64 * mb, b_s);
+        ld8(rsn, vo_key + 64 * mb, b_sn);
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            X1 = mma(f4(a_do, s4), f4(b_s, s4), X1);
-            X2 = mma(f4(a_w, s4), f4(b_s, s4), X2);
-            X3 = mma(f4(a_u, s4), f4(b_sn, s4), X3);
-            rsum += f4(b_s, s4) * f4(b_sn, s4);
+        for (int j = 0; j < 8; ++j) rsum += b_s[j] * b_sn[j];
+        if constexpr (F32) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                X1 = mma(a_do[j], b_s[j], X1);
+                X2 = mma(a_w[j], b_s[j], X2);
+                X3 = mma(a_u[j], b_sn[j], X3);
+            }
+        } else {
+            const SplitBF<8> ss = split8(b_s);
+            X1 = mma3(split8(a_do), ss, X1);
+            X2 = mma3(split8(a_w), ss, X2);
+            X3 = mma3(split8(a_u), split8(b_sn), X3);
         }
     }
     rsum += swap_halves(rsum);
@@ -516,14 +550,25 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
         f32x16 PM = zero16(), PA = zero16();
         float db = 0.f;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int o = vo_tok + 32 * (4 * wave + q4);
-            const float4 a_do = ld4(rdo, o), a_w = ld4(rw, o), a_u = ld4(ru, o), a_r = ld4(rr, o);
+        for (int qb = 0; qb < 2; ++qb) {
+            const int o = vo_tok + 64 * (2 * wave + qb);
+            float a_do[8], a_w[8], a_u[8], a_r[8];
+            ld8(rdo, o, a_do);
+            ld8(rw, o, a_w);
+            ld8(ru, o, a_u);
+            ld8(rr, o, a_r);
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                PM = mma(f4(a_do, s4), f4(a_u, s4), PM);
-                PA = mma(f4(a_w, s4), f4(a_u, s4), PA);
-                db += f4(a_w, s4) * f4(a_r, s4);
+            for (int j = 0; j < 8; ++j) db += a_w[j] * a_r[j];
+            if constexpr (F32) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    PM = mma(a_do[j], a_u[j], PM);
+                    PA = mma(a_w[j], a_u[j], PA);
+                }
+            } else {
+                const SplitBF<8> su = split8(a_u);
+                PM = mma3(split8(a_do), su, PM);
+                PA = mma3(split8(a_w), su, PA);
             }
         }
         db += swap_halves(db);
@@ -574,19 +619,46 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
         gC = run;
         E0 = e0;
     }
-    // ---- products over the chunk's tokens
+    // ---- products over the chunk's tokens (k = token crow(r, lane) of the
+    // lane's own values; bf16 inputs: blocks r = 8 b + j as split-bf16)
     f32x16 Y1 = zero16(), Y2 = zero16(), Y34 = zero16();
-    float Gr[16];
+    float Gr[16], Gri[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int t = crow(r, lane);
         Gr[r] = expf(g[r] - E0);
-        const float Gri = expf(E0 - g[r]);
-        const float yr = kv[r] * Gri;
-        Y1 = mma(sdM[i0 * LC + t], yr, Y1);
-        Y2 = mma(sdP[i0 * LC + t], yr, Y2);
-        Y34 = mma(sdM[t * LC + i0], qv[r] * Gr[r], Y34);
-        Y34 = mma(sdP[t * LC + i0], kv[r] * Gr[r], Y34);
+        Gri[r] = expf(E0 - g[r]);
+    }
+    if constexpr (F32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = crow(r, lane);
+            const float yr = kv[r] * Gri[r];
+            Y1 = mma(sdM[i0 * LC + t], yr, Y1);
+            Y2 = mma(sdP[i0 * LC + t], yr, Y2);
+            Y34 = mma(sdM[t * LC + i0], qv[r] * Gr[r], Y34);
+            Y34 = mma(sdP[t * LC + i0], kv[r] * Gr[r], Y34);
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float am[8], ap[8], amt[8], apt[8], y8[8], q8[8], x8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = 8 * b + j, t = crow(r, lane);
+                am[j] = sdM[i0 * LC + t];
+                ap[j] = sdP[i0 * LC + t];
+                amt[j] = sdM[t * LC + i0];
+                apt[j] = sdP[t * LC + i0];
+                y8[j] = kv[r] * Gri[r];
+                q8[j] = qv[r] * Gr[r];
+                x8[j] = kv[r] * Gr[r];
+            }
+            const SplitBF<8> sy = split8(y8);
+            Y1 = mma3(split8(am), sy, Y1);
+            Y2 = mma3(split8(ap), sy, Y2);
+            Y34 = mma3(split8(amt), split8(q8), Y34);
+            Y34 = mma3(split8(apt), split8(x8), Y34);
+        }
     }
 
     // ---- chain rule through the scalings; dlog_alpha by suffix sums
@@ -594,10 +666,10 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int t = crow(r, lane);
-        const float G = expf(g[r]), Ge = expf(gC - g[r]), Gri = expf(E0 - g[r]);
+        const float G = expf(g[r]), Ge = expf(gC - g[r]);
         const float dq = X1[r] * G + Y1[r] * Gr[r];
         const float dkp = -bv[r] * X2[r] * G + Y2[r] * Gr[r];
-        const float dkm = Y34[r] * Gri;
+        const float dkm = Y34[r] * Gri[r];
         const float dke = X3[r] * Ge;
         dg[r] = qv[r] * dq + kv[r] * (dkp - dkm - dke);
         colsum += kv[r] * dke;
