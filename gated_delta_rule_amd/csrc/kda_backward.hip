@@ -29,23 +29,29 @@
 // Qr = q e^{g - E0}; then P = X Y^T, M = Qr Y^T, dM K- G = (dM Y) e^{g - E0},
 // dM^T Q+ / G = (dM^T Qr) e^{E0 - g}, and so on.
 //
-// MI355X design: three passes after a forward pass that stores the state
-// at every chunk start (the prefill kernel with its state output):
+// MI355X design: three passes after a forward pass that keeps the state at
+// every chunk start and V - K+ S and U of every token (the prefill kernel
+// with its extra outputs):
 //   1. tmp:  one workgroup per (chunk, head), all chunks at once: the decay
-//            scan, P and M on the matrix cores, T by forward substitution.
-//   2. scan: one workgroup per (sequence, head, 32 value columns) walks the
-//            chunks backwards with its 128 x 32 slice of dS in MFMA
-//            accumulators (each wave 32 key rows); it writes W, dv and the
-//            gradient at every chunk end, and dS0.
-//   3. grad: one workgroup per (chunk, head), all chunks at once: every
-//            remaining product of the list above from S, Sn, W and the
-//            chunk's inputs, then the elementwise chain rule and the
-//            in-chunk reverse scan of dg.
-// All products run on the fp32 matrix cores (v_mfma_f32_32x32x2f32): a
-// wave's 32 x 32 accumulator gives lane l column l % 32 and rows
-// 8 (r / 4) + 4 (l / 32) + r % 4 (r = 0..15).  Like the forward, the k order
-// of a product is chosen so that accumulators feed the next product's B
-// operand without a round trip through LDS.
+//            sums, P and M on the matrix cores, T by forward substitution,
+//            and the operands of pass 2 in the orders it reads them.
+//   2. scan: the only serial part.  8 waves per (sequence, head, 64 value
+//            columns) walk the chunks backwards with their slice of dS in
+//            MFMA accumulators (a wave owns 32 key rows x 32 value columns);
+//            per chunk three phases between two LDS-only barriers; operands
+//            buffer-loaded straight into registers one phase ahead.  Writes
+//            W and the gradient at every chunk end, and dS0.
+//   3. grad: one workgroup per (chunk, head), all chunks at once: streams
+//            rows of dO, W, U and of S, Sn into matrix-core operands, then
+//            the products over the chunk's tokens, the elementwise chain
+//            rule and the in-chunk suffix sums of dg, all in registers.
+// Products run on the fp32 matrix cores (v_mfma_f32_32x32x2f32), except
+// the gradient kernel's with bf16 inputs, which use split-bf16 operands
+// (hi + lo) on the bf16 matrix cores.  A wave's 32 x 32 accumulator gives
+// lane l column l % 32 and rows 8 (r / 4) + 4 (l / 32) + r % 4 (r = 0..15);
+// which k a lane supplies only has to agree between the two operands of a
+// product, so every product picks the order its operands are stored in (or
+// the order an accumulator already holds them).
 #include <type_traits>
 
 #include "kda_device.h"
@@ -97,10 +103,6 @@ __device__ __forceinline__ f32x16 zero16() {
 // row of accumulator element r in lane l (its column is l % 32)
 __device__ __forceinline__ int crow(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-template <typename InT>
-__device__ __forceinline__ float ld_in(const void* base, int64_t idx) {
-    return to_f32(reinterpret_cast<const InT*>(base)[idx]);
-}
 
 // First token of sequence n (clamped into [0, T] like the forward).
 __device__ __forceinline__ int64_t seq_start(const BwdParams& p, int n) {

@@ -149,3 +149,73 @@ def test_bwd_full_size_sampled_heads():
         say(f"[bwd] full size head {h}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
         for n, e in errs.items():
             assert e <= TOL_BF16, (h, n, e)
+
+
+def test_bwd_varlen_multichunk_with_state():
+    """Packed sequences of several chunks each, S0 and dL/dS_T given."""
+    w, a, S0, dO, dS, cu = inputs(W.workload(2).shrink(H=3), [200, 513, 64, 1000, 31], 0.02, 1.0)
+    compare(w, a, S0, dO, dS, cu, TOL_BF16, "bf16 varlen multi-chunk")
+
+
+def test_bwd_deterministic_and_in_place_state_gradient():
+    """Two calls give bitwise equal gradients (no atomics anywhere), and
+    grad_S0 written over grad_S_T equals the separate result."""
+    w, a, S0, dO, dS, cu = inputs(W.workload(1).shrink(H=2), [150, 77], 0.02, 1.0)
+    g1 = run(w, a, S0, dO, dS, cu)
+    g2 = run(w, a, S0, dO, dS, cu)
+    for x, y in zip(g1, g2):
+        assert np.array_equal(x, y)
+    d = {n: torch.from_numpy(np.ascontiguousarray(a[n])).cuda() for n in a}
+    for n in ("q", "k", "v"):
+        d[n] = d[n].to(torch.bfloat16)
+    gst = torch.from_numpy(dS).cuda()
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
+    lib = kda.load_library()
+    T, H = a["q"].shape[0], a["q"].shape[1]
+    outs = [torch.empty_like(d["log_alpha"]) for _ in range(4)] + [torch.empty_like(d["beta"])]
+    ws = torch.empty(lib.kda_chunk_bwd_workspace_bytes(len(cu) - 1, T, H, 128, 128, 1),
+                     dtype=torch.uint8, device="cuda")
+    import ctypes
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = lib.kda_chunk_bwd(vp(d["q"]), vp(d["k"]), vp(d["v"]), 0, vp(d["log_alpha"]), vp(d["beta"]),
+                           vp(torch.from_numpy(S0).cuda()), vp(cu_dev), len(cu) - 1, T, H, 128, 128,
+                           vp(torch.from_numpy(dO).cuda()), vp(gst), *[vp(o) for o in outs], vp(gst),
+                           vp(ws), ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert np.array_equal(gst.cpu().numpy(), g1[5])
+
+
+def test_bwd_full_size_varlen_lengths_sampled():
+    """The packed lengths of the varlen workload (32 sequences of 512-16384
+    tokens, S0 ~ N(0, 0.02^2)) on 4 heads; the oracle follows two
+    (sequence, head) units on their own."""
+    w = W.workload(2).shrink(H=4)
+    cu = W.cu_seqlens(w)
+    T, N = int(cu[-1]), len(cu) - 1
+    say(f"[bwd] varlen lengths T={T}: inputs")
+    a = W.prefill_inputs(w)
+    dO, dS = W.grad_inputs(w, T, N)
+    d = {n: torch.from_numpy(np.ascontiguousarray(a[n])).cuda() for n in ("q", "k", "v", "log_alpha", "beta")}
+    for n in ("q", "k", "v"):
+        d[n] = d[n].to(torch.bfloat16)
+    cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
+    say("[bwd] varlen lengths: GPU")
+    g = kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                      torch.from_numpy(a["S0"]).cuda(), torch.from_numpy(dO).cuda(),
+                      torch.from_numpy(dS).cuda(), cu_dev)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in g]
+    del g, d
+    for n, h in ((int(np.argmax(np.diff(cu))), 1), (5, 3)):
+        say(f"[bwd] varlen lengths: oracle sequence {n} head {h}")
+        ref = oracle.backward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["S0"], dO, dS, cu,
+                              units=[(n, h)])
+        rows = slice(int(cu[n]), int(cu[n + 1]))
+        errs = {}
+        for i, nm in enumerate(NAMES):
+            x, r = (got[i][rows, h], ref[i][rows, h]) if i < 5 else (got[i][n, h], ref[i][n, h])
+            errs[nm] = rel_err(x, r)
+        say(f"[bwd] varlen sequence {n} head {h}: " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()))
+        for nm, e in errs.items():
+            assert e <= TOL_BF16, (n, h, nm, e)
