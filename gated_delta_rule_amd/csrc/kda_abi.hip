@@ -335,7 +335,7 @@ int kda_prologue(const void* q_raw, const void* k_raw, const void* v_raw, int in
     else if (!mul_ok((int64_t)n_seqs, T, &rows)) return KDA_ERR_TOO_LARGE;
     if (n_seqs == 0) return KDA_OK;
     if (!mul_ok(rows, (int64_t)H, &hrows) || !mul_ok(hrows, kHeadDim, &elems) ||
-        elems > INT64_MAX / 8 || ((rows + 1) / 2) * ((H + 3) / 4) > kMaxGrid)
+        elems > INT64_MAX / 8 || ((rows + 7) / 8) * ((H + 3) / 4) > kMaxGrid)
         return KDA_ERR_TOO_LARGE;
     const int64_t cache_elems = (int64_t)n_seqs * 9 * H * kHeadDim;
     if (conv_cache && (cache_elems + 255) / 256 > kMaxGrid) return KDA_ERR_TOO_LARGE;

@@ -14,11 +14,14 @@
 //
 // All three kernels move each element once and do a few flops on it, so they
 // are HBM-bound: a wave owns one head's 128 channels (two per lane) of one
-// row (epilogue) or of two consecutive rows (prologue, with the conv
+// row (epilogue) or of eight consecutive rows (prologue, with the conv
 // weights and the last three raw inputs kept in registers), sums over the
-// row by DPP wave reduction.  The cache update runs as a
-// separate launch after the prologue, so no wave reads a cache entry that
-// another already overwrote.
+// row by DPP wave reduction.  The prologue reads and writes through buffer
+// resources with 32-bit offsets from its first row (rows past the end read
+// as zero, and the window before a sequence start takes the cache entry
+// through the same out-of-range trick instead of a branch).  The cache
+// update runs as a separate launch after the prologue, so no wave reads a
+// cache entry that another already overwrote.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -70,32 +73,73 @@ __device__ __forceinline__ void locate(int64_t row, const int32_t* cu, int32_t n
     pos = row - cu[lo];
 }
 
-constexpr int LY_TOK = 2;   // consecutive token rows per wave in the prologue (1: 0.81 ms, 2: 0.67, 4: 0.68 at T=8192 H=96)
+constexpr int LY_TOK = 8;   // consecutive token rows per wave in the prologue (2: 0.55 ms, 4: 0.42, 8: 0.39, 16: 0.88 at T=8192 H=96)
+
+// Two channels of one row through a buffer resource (offsets past its
+// range read as zero).
+template <typename T>
+__device__ __forceinline__ float2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ float2 bload2<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x2 u = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return make_float2(__uint_as_float(u[0]), __uint_as_float(u[1]));
+}
+template <>
+__device__ __forceinline__ float2 bload2<__bf16>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+__device__ __forceinline__ void bstore2(float2 v, __amdgpu_buffer_rsrc_t r, uint32_t off, float) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_float2(v.x, v.y)), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore2(float2 v, __amdgpu_buffer_rsrc_t r, uint32_t off, __bf16) {
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf2(v.x, v.y), r, off, 0, 0);
+}
+constexpr uint32_t OOB = 0x80000000u;   // an offset past every range: reads 0
 
 template <typename InT>
 __global__ __launch_bounds__(LY_THREADS) void prologue_kernel(LayerParams p) {
     // workgroup = (block of LY_TOK token rows, group of four heads, one per
     // wave); a wave keeps its head's conv weights and the last three raw
     // inputs in registers while it walks its rows
+    constexpr int ES = (int)sizeof(InT);
     const int lane = threadIdx.x & 63;
     const uint32_t nhg = (uint32_t)(p.H + 3) / 4;
     const uint32_t blk = blockIdx.x;
     const uint32_t tb = blk / nhg;
-    const int h = (int)(blk - tb * nhg) * (LY_THREADS / 64) + (threadIdx.x >> 6);
+    const int h = (int)(blk - tb * nhg) * (LY_THREADS / 64) +
+                  __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (h >= p.H) return;
+    const int H = p.H;
     const int c = 2 * lane;
-    const int64_t HD = (int64_t)p.H * 128;
+    const int64_t HD = (int64_t)H * 128;
     const int64_t row0 = (int64_t)tb * LY_TOK;
     const int nt = p.rows - row0 < LY_TOK ? (int)(p.rows - row0) : LY_TOK;
-    const InT* raw[3] = {(const InT*)p.q_raw, (const InT*)p.k_raw, (const InT*)p.v_raw};
-    InT* out[3] = {(InT*)p.q, (InT*)p.k, (InT*)p.v};
+    // buffer resources over this head's rows [wb, row0 + nt): offsets count
+    // from row wb, channel 0; rows past the end read as zero
+    const int64_t wb = row0 >= 3 ? row0 - 3 : 0;
+    const int nrow = (int)(row0 + nt - wb);
+    const int rb_in = (int)HD * ES, rb_f = (int)HD * 4;   // bytes per token row
+    const int64_t e0 = wb * HD + (int64_t)h * 128;
+    const int sp_in = (nrow - 1) * rb_in + 128 * ES, sp_f = (nrow - 1) * rb_f + 512;
+    __amdgpu_buffer_rsrc_t rin[3], rout[3];
+    rin[0] = make_rsrc((const InT*)p.q_raw + e0, sp_in);
+    rin[1] = make_rsrc((const InT*)p.k_raw + e0, sp_in);
+    rin[2] = make_rsrc((const InT*)p.v_raw + e0, sp_in);
+    rout[0] = make_rsrc((InT*)p.q + e0, sp_in);
+    rout[1] = make_rsrc((InT*)p.k + e0, sp_in);
+    rout[2] = make_rsrc((InT*)p.v + e0, sp_in);
+    const auto ra = make_rsrc(p.a + e0, sp_f);
+    const auto rla = make_rsrc(p.log_alpha + e0, sp_f);
+    const auto rbi = make_rsrc(p.b + wb * H + h, ((nrow - 1) * H + 1) * 4);
+    const auto rbo = make_rsrc(p.beta + wb * H + h, ((nrow - 1) * H + 1) * 4);
 
     // every load first (the stores below may not be reordered above them)
     float4 w[3][2];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         // weights of channels c, c + 1: [tensor, head, channel, tap]
-        const float* wp = p.conv_w + (((int64_t)i * p.H + h) * 128 + c) * 4;
+        const float* wp = p.conv_w + (((int64_t)i * H + h) * 128 + c) * 4;
         w[i][0] = *reinterpret_cast<const float4*>(wp);
         w[i][1] = *reinterpret_cast<const float4*>(wp + 4);
     }
@@ -103,27 +147,28 @@ __global__ __launch_bounds__(LY_THREADS) void prologue_kernel(LayerParams p) {
     float bv[LY_TOK];
 #pragma unroll
     for (int tt = 0; tt < LY_TOK; ++tt) {
-        if (tt < nt) {
-            const int64_t base = (row0 + tt) * HD + (int64_t)h * 128 + c;
+        const int r = (int)(row0 + tt - wb);   // rows past nt read as zero
 #pragma unroll
-            for (int i = 0; i < 3; ++i) cur[tt][i] = load2(raw[i] + base);
-            av[tt] = load2(p.a + base);
-            bv[tt] = p.b[(row0 + tt) * p.H + h];
-        }
+        for (int i = 0; i < 3; ++i) cur[tt][i] = bload2<InT>(rin[i], r * rb_in + c * ES);
+        av[tt] = bload2<float>(ra, r * rb_f + c * 4);
+        bv[tt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbi, r * H * 4, 0, 0));
     }
-    // the three inputs before a row: x_{t-3}, x_{t-2}, x_{t-1}
+    // the three inputs before a row: x_{t-3}, x_{t-2}, x_{t-1}, each from
+    // the raw rows or, before the sequence start, from the cache (the
+    // other source's offset is out of range, so the sum is the one value)
     float2 win[3][3];
     auto fill_window = [&](int64_t row, int64_t n, int64_t pos) {
+        const auto rc = make_rsrc(p.cache ? p.cache + n * 9 * HD : nullptr, p.cache ? (int)(9 * HD * 4) : 0);
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
                 const int64_t tp = pos - 3 + j;
-                win[i][j] = make_float2(0.f, 0.f);
-                if (tp >= 0)
-                    win[i][j] = load2(raw[i] + (row - 3 + j) * HD + (int64_t)h * 128 + c);
-                else if (p.cache)   // cache tap 3 + tp holds x_{tp}
-                    win[i][j] = load2(p.cache + (((n * 3 + i) * 3 + (3 + tp)) * p.H + h) * 128 + c);
+                const uint32_t o_raw = tp >= 0 ? (uint32_t)((row - 3 + j - wb) * rb_in + c * ES) : OOB;
+                // cache tap 3 + tp holds x_{tp}
+                const uint32_t o_c = tp < 0 ? (uint32_t)((((i * 3 + 3 + tp) * H + h) * 128 + c) * 4) : OOB;
+                const float2 x = bload2<InT>(rin[i], o_raw), y = bload2<float>(rc, o_c);
+                win[i][j] = make_float2(x.x + y.x, x.y + y.y);
             }
     };
 #pragma unroll
@@ -133,7 +178,7 @@ __global__ __launch_bounds__(LY_THREADS) void prologue_kernel(LayerParams p) {
         int64_t n, pos;
         locate(row, p.cu, p.n_seqs, p.T, n, pos);
         if (tt == 0 || pos == 0) fill_window(row, n, pos);
-        const int64_t base = row * HD + (int64_t)h * 128 + c;
+        const uint32_t o_in = (uint32_t)((row - wb) * rb_in + c * ES), o_f = (uint32_t)((row - wb) * rb_f + c * 4);
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
             const float2 x3 = cur[tt][i];
@@ -155,10 +200,12 @@ __global__ __launch_bounds__(LY_THREADS) void prologue_kernel(LayerParams p) {
                 y0 *= r;
                 y1 *= r;
             }
-            store2(out[i] + base, make_float2(y0, y1));
+            bstore2(make_float2(y0, y1), rout[i], o_in, InT());
         }
-        store2(p.log_alpha + base, make_float2(-5.f * sigm(av[tt].x), -5.f * sigm(av[tt].y)));
-        if (lane == 0) p.beta[row * p.H + h] = sigm(bv[tt]);
+        bstore2(make_float2(-5.f * sigm(av[tt].x), -5.f * sigm(av[tt].y)), rla, o_f, 0.f);
+        if (lane == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sigm(bv[tt])), rbo,
+                                                  (uint32_t)((row - wb) * H * 4), 0, 0);
     }
 }
 
