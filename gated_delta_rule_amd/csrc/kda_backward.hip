@@ -295,6 +295,10 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int sw = wave >> 2, rw = wave & 3;
+    // The wave that forms W (role 0) and the one that adds M^T dO to its
+    // partial product (role 1) sit on different SIMDs for the two column
+    // halves (wave w runs on SIMD w % 4 = rw), so no SIMD carries two of them.
+    const int role = (rw + 2 * sw) & 3;
     const int i0 = lane & 31, kh = lane >> 5;
     const int col = 64 * sp + 32 * sw + i0;   // this lane's value column
     const int row0 = 32 * rw;                 // this wave's first key row
@@ -336,14 +340,14 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
         for (int m4 = 0; m4 < 4; ++m4) {
             qt[m4] = ld4(rt, vo_row, (OFF_QT + 8 * m4) * 4);
             gc[m4] = ld4(rt, vo_gc, (OFF_GC + 8 * m4) * 4);
-            if (rw == 1) spc[m4] = ld4(rt, vo_sq, (OFF_MT + 8 * m4) * 4);
+            if (role == 1) spc[m4] = ld4(rt, vo_sq, (OFF_MT + 8 * m4) * 4);
         }
         const auto rdo = make_rsrc(p.dO + (c0 * H + h) * BD, (nv - 1) * rowb + BD * 4);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             dOr[r] = ld1(rdo, crow(r, lane) * rowb + col * 4, 0);   // range-checked offset
     };
-    auto load_t = [&](int64_t j) {   // rw = 0 waves
+    auto load_t = [&](int64_t j) {   // role 0 waves
         const auto rt = tmp_rsrc(j);
 #pragma unroll
         for (int m4 = 0; m4 < 4; ++m4) spc[m4] = ld4(rt, vo_sq, (OFF_TT + 8 * m4) * 4);
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
         dS[r] = p.dS_T ? p.dS_T[unit_el + (size_t)(row0 + crow(r, lane)) * BD + col] : 0.f;
     if (nch > 0) {
         load_a(nch - 1);
-        if (rw == 0) load_t(nch - 1);
+        if (role == 0) load_t(nch - 1);
         load_b(nch - 1);
     }
 
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
         f32x16 part = zero16();
 #pragma unroll
         for (int r = 0; r < 16; ++r) part = mma(ke[r], dS[r], part);
-        if (rw == 1) {
+        if (role == 1) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) part = mma(f4(spc[r >> 2], r & 3), dOr[r], part);
         }
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
         if (j > 0) load_a(j - 1);
         lds_barrier();
         // ---- phase 2: W = T^T dU
-        if (rw == 0) {
+        if (role == 0) {
             f32x16 W = zero16();
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
