@@ -45,9 +45,9 @@
 //            rows of dO, W, U and of S, Sn into matrix-core operands, then
 //            the products over the chunk's tokens, the elementwise chain
 //            rule and the in-chunk suffix sums of dg, all in registers.
-// Products run on the fp32 matrix cores (v_mfma_f32_32x32x2f32), except
-// the gradient kernel's with bf16 inputs, which use split-bf16 operands
-// (hi + lo) on the bf16 matrix cores.  A wave's 32 x 32 accumulator gives
+// With fp32 inputs the products run on the fp32 matrix cores
+// (v_mfma_f32_32x32x2f32); with bf16 inputs those of passes 2 and 3 use
+// split-bf16 operands (hi + lo) on the bf16 matrix cores.  A wave's 32 x 32 accumulator gives
 // lane l column l % 32 and rows 8 (r / 4) + 4 (l / 32) + r % 4 (r = 0..15);
 // which k a lane supplies only has to agree between the two operands of a
 // product, so every product picks the order its operands are stored in (or
@@ -93,6 +93,28 @@ __device__ __forceinline__ f32x16 mma3(const SplitBF<8>& a, const SplitBF<8>& b,
     c = mfb(a.lo, b.hi, c);
     c = mfb(a.hi, b.lo, c);
     return mfb(a.hi, b.hi, c);
+}
+// acc += A B over 32 k given as 16 values per lane (k order r <-> crow(r,
+// lane) for both operands): fp32 matrix cores one k pair per instruction, or
+// split-bf16 in two blocks of 16 k (r = 8 b + j).
+template <bool F32>
+__device__ __forceinline__ f32x16 mma32k(const float (&a)[16], const float (&b)[16], f32x16 c) {
+    if constexpr (F32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[r], b[r], c, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            float x[8], y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                x[j] = a[8 * blk + j];
+                y[j] = b[8 * blk + j];
+            }
+            c = mma3(split8(x), split8(y), c);
+        }
+    }
+    return c;
 }
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
@@ -277,6 +299,7 @@ __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
 // each group is loaded for the next chunk as soon as this chunk's use ends.
 template <typename InT>
 __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
+    constexpr bool F32 = std::is_same<InT, float>::value;
     __shared__ float sPart[2][4][BC * LC];
     __shared__ float sW[2][BC * LC];
 
@@ -381,31 +404,37 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
 
         // ---- phase 1 (the k order of every product below pairs row / token
         // crow(r, lane) of the two lane halves; r = 4 m4 + s)
-        f32x16 part = zero16();
+        float dsv[16], qv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part = mma(ke[r], dS[r], part);
+        for (int r = 0; r < 16; ++r) {
+            dsv[r] = dS[r];
+            qv[r] = f4(qt[r >> 2], r & 3);
+        }
+        f32x16 part = mma32k<F32>(ke, dsv, zero16());
         if (role == 1) {
+            float mv[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) part = mma(f4(spc[r >> 2], r & 3), dOr[r], part);
+            for (int r = 0; r < 16; ++r) mv[r] = f4(spc[r >> 2], r & 3);
+            part = mma32k<F32>(mv, dOr, part);
         }
         // dS <- Diag(e^{g_C}) dS + Q+^T dO
 #pragma unroll
         for (int r = 0; r < 16; ++r) dS[r] *= f4(gc[r >> 2], r & 3);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dS = mma(f4(qt[r >> 2], r & 3), dOr[r], dS);
+        dS = mma32k<F32>(qv, dOr, dS);
 #pragma unroll
         for (int r = 0; r < 16; ++r) sPart[sw][rw][crow(r, lane) * LC + i0] = part[r];
         if (j > 0) load_a(j - 1);
         lds_barrier();
         // ---- phase 2: W = T^T dU
         if (role == 0) {
-            f32x16 W = zero16();
+            float tv[16], du[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int e = crow(r, lane) * LC + i0;
-                const float dU = (sPart[sw][0][e] + sPart[sw][1][e]) + (sPart[sw][2][e] + sPart[sw][3][e]);
-                W = mma(f4(spc[r >> 2], r & 3), dU, W);
+                du[r] = (sPart[sw][0][e] + sPart[sw][1][e]) + (sPart[sw][2][e] + sPart[sw][3][e]);
+                tv[r] = f4(spc[r >> 2], r & 3);
             }
+            const f32x16 W = mma32k<F32>(tv, du, zero16());
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int t = crow(r, lane);
@@ -416,9 +445,15 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
         }
         lds_barrier();
         // ---- phase 3: dS <- dS - (B_beta K+)^T W
+        {
+            float kv[16], wv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dS = mma(f4(kbt[r >> 2], r & 3), sW[sw][crow(r, lane) * LC + i0], dS);
+            for (int r = 0; r < 16; ++r) {
+                kv[r] = f4(kbt[r >> 2], r & 3);
+                wv[r] = sW[sw][crow(r, lane) * LC + i0];
+            }
+            dS = mma32k<F32>(kv, wv, dS);
+        }
         if (j > 0) load_b(j - 1);
     }
     if (p.dS0) {
