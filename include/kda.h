@@ -257,10 +257,11 @@ size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  *   the workspace is rejected).
  *   workspace: kda_chunk_bwd_workspace_bytes(...) bytes, 16-byte aligned,
  *   contents clobbered.
- * Numerics: every product of the backward pass runs on fp32 matrix cores
- * with fp32 accumulation (the states come from the same kernel as
- * kda_chunk_fwd, so with KDA_BF16 inputs they carry its split-bf16
- * rounding).  Deterministic: no atomics.
+ * Numerics: fp32 accumulation throughout.  With KDA_F32 inputs every
+ * product runs on fp32 matrix cores; with KDA_BF16 inputs the products of
+ * the state-gradient walk and of the per-chunk gradients use split (hi + lo)
+ * bf16 operands, and the states come from the same kernel as kda_chunk_fwd
+ * (its split-bf16 rounding).  Deterministic: no atomics.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
                   const float* log_alpha, const float* beta, const float* S0,
