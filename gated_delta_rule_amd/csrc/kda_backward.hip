@@ -79,6 +79,11 @@ constexpr int TMP_ELEMS = 15488;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Decay sums are kept in base 2 (log alpha * log2 e), so every factor is one
+// hardware exp2 of a difference of sums.
+constexpr float LOG2E_F = 1.4426950408889634f;
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x16 mma(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
         const int t = 16 * half + i;
         // the whole offset in the per-lane operand, so that the range check
         // covers it (rows past the sequence end read as zero)
-        la[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rla, t * rowb + c * 4, 0, 0));
+        la[i] = LOG2E_F * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rla, t * rowb + c * 4, 0, 0));
         if constexpr (ES == 4) {
             kr[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rk, t * rowb + c * 4, 0, 0));
             qr[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rq, t * rowb + c * 4, 0, 0));
@@ -220,11 +225,11 @@ __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
             const int t = 16 * half + i;
             g += la[i];
             const float d = g - E0;
-            const float fx = expf(d), fy = expf(-d), G = expf(g);
+            const float fx = ex2(d), fy = ex2(-d), G = ex2(g);
             sX[t * LS + c] = kr[i] * fx;
             sY[t * LS + c] = kr[i] * fy;
             sQ[t * LS + c] = qr[i] * fx;
-            ke[i] = kr[i] * expf(gC - g);
+            ke[i] = kr[i] * ex2(gC - g);
             qp[i] = qr[i] * G;
             kb[i] = -br[i] * kr[i] * G;
         }
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(256) void bwd_tmp_kernel(BwdParams p) {
             *reinterpret_cast<float4*>(tmp + OFF_KB + o) =
                 make_float4(kb[4 * v], kb[4 * v + 1], kb[4 * v + 2], kb[4 * v + 3]);
         }
-        if (half == 0) tmp[OFF_GC + c] = expf(gC);
+        if (half == 0) tmp[OFF_GC + c] = ex2(gC);
     }
     lds_barrier();
     const int i0 = lane & 31, kh = lane >> 5;
@@ -522,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int t = crow(r, lane);
-        lav[r] = ld1(rla, t * rowb + dk * 4);
+        lav[r] = LOG2E_F * ld1(rla, t * rowb + dk * 4);
         if constexpr (ES == 4) {
             kv[r] = ld1(rk, t * rowb + dk * 4);
             qv[r] = ld1(rq, t * rowb + dk * 4);
@@ -666,8 +671,8 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
     float Gr[16], Gri[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        Gr[r] = expf(g[r] - E0);
-        Gri[r] = expf(E0 - g[r]);
+        Gr[r] = ex2(g[r] - E0);
+        Gri[r] = ex2(E0 - g[r]);
     }
     if constexpr (F32) {
 #pragma unroll
@@ -707,7 +712,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int t = crow(r, lane);
-        const float G = expf(g[r]), Ge = expf(gC - g[r]);
+        const float G = ex2(g[r]), Ge = ex2(gC - g[r]);
         const float dq = X1[r] * G + Y1[r] * Gr[r];
         const float dkp = -bv[r] * X2[r] * G + Y2[r] * Gr[r];
         const float dkm = Y34[r] * Gri[r];
@@ -722,7 +727,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
     }
     colsum += swap_halves(colsum);
     {
-        float run = colsum + expf(gC) * rsum;   // dg_C
+        float run = colsum + ex2(gC) * rsum;   // dg_C
 #pragma unroll
         for (int m4 = 3; m4 >= 0; --m4) {
             const float G = dg[4 * m4] + dg[4 * m4 + 1] + dg[4 * m4 + 2] + dg[4 * m4 + 3];
