@@ -55,15 +55,11 @@ __device__ __forceinline__ void store2(__bf16* p, float2 v) {
     *reinterpret_cast<bf16x2_t*>(p) = r;
 }
 
-// Sequence of a token row and its position in that sequence.
-__device__ __forceinline__ void locate(int64_t row, const int32_t* cu, int32_t n_seqs, int64_t T,
-                                       int64_t& n, int64_t& pos) {
-    if (!cu) {   // rows < 2^31 (one workgroup column per row)
-        n = (int64_t)((uint32_t)row / (uint32_t)T);
-        pos = row - n * T;
-        return;
-    }
-    int lo = 0, hi = n_seqs;   // largest s with cu[s] <= row
+// Packed sequences: the sequence of a token row (largest s with
+// cu[s] <= row) and the row's position in it.
+__device__ __forceinline__ void locate_packed(int64_t row, const int32_t* cu, int32_t n_seqs,
+                                              int64_t& n, int64_t& pos) {
+    int lo = 0, hi = n_seqs;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if ((int64_t)cu[mid] <= row) lo = mid;
@@ -171,12 +167,22 @@ __global__ __launch_bounds__(LY_THREADS) void prologue_kernel(LayerParams p) {
                 win[i][j] = make_float2(x.x + y.x, x.y + y.y);
             }
     };
+    // equal lengths: sequence and position of the first row, then counted on
+    int64_t n = 0, pos = 0;
+    if (!p.cu) {
+        n = row0 / p.T;
+        pos = row0 - n * p.T - 1;
+    }
 #pragma unroll
     for (int tt = 0; tt < LY_TOK; ++tt) {
         if (tt >= nt) break;
         const int64_t row = row0 + tt;
-        int64_t n, pos;
-        locate(row, p.cu, p.n_seqs, p.T, n, pos);
+        if (p.cu) {
+            locate_packed(row, p.cu, p.n_seqs, n, pos);
+        } else if (++pos == p.T) {
+            ++n;
+            pos = 0;
+        }
         if (tt == 0 || pos == 0) fill_window(row, n, pos);
         const uint32_t o_in = (uint32_t)((row - wb) * rb_in + c * ES), o_f = (uint32_t)((row - wb) * rb_f + c * 4);
 #pragma unroll
@@ -221,9 +227,11 @@ __global__ __launch_bounds__(LY_THREADS) void conv_cache_kernel(LayerParams p) {
     const int i = (int)(rem / HD);
     const int64_t ch = rem - (int64_t)i * HD;   // h * 128 + c
     int64_t start, L;
-    if (p.cu) {
-        start = p.cu[n];
-        L = p.cu[n + 1] - start;
+    if (p.cu) {   // clamped into [0, rows]: a malformed table never reads out of bounds
+        const int64_t a = p.cu[n], b = p.cu[n + 1];
+        start = a < 0 ? 0 : (a > p.rows ? p.rows : a);
+        const int64_t e = b < start ? start : (b > p.rows ? p.rows : b);
+        L = e - start;
     } else {
         start = n * p.T;
         L = p.T;

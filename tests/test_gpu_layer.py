@@ -146,3 +146,24 @@ def test_layer_step_end_to_end():
     e1, e2 = rel_err(out.cpu().numpy(), rout), rel_err(st.cpu().numpy(), rs)
     say(f"[layer] end to end: out {e1:.2e}  S_T {e2:.2e}")
     assert e1 <= TOL_BF16 and e2 <= TOL_BF16
+
+
+@pytest.mark.parametrize("T,B", [(1, 7), (3, 5), (9, 3)])
+def test_prologue_equal_lengths_shorter_than_a_wave_block(T, B):
+    """Equal-length batches whose sequences end inside one wave's block of
+    rows (the position is counted on from the block's first row), with a
+    cache."""
+    lens = [T] * B
+    x = layer_inputs(lens, 2, seed=11)
+    d = dev_layer(x, "bf16")
+    shp = (B, T, 2, 128)
+    cache = d["cache"].clone()
+    q, k, v, la, be = kda.prologue(d["q_raw"].view(shp), d["k_raw"].view(shp),
+                                   d["v_raw"].view(shp), d["conv_w"], d["a"].view(shp),
+                                   d["b"].view(B, T, 2), cache)
+    torch.cuda.synchronize()
+    ref, rc = oracle_prologue(x)
+    for m, t in (("q", q), ("k", k), ("v", v)):
+        assert bf16_err(t.float().cpu().numpy().reshape(ref[m].shape), ref[m]) <= 1.0, m
+    assert rel_err(la.cpu().numpy().reshape(ref["log_alpha"].shape), ref["log_alpha"]) <= TOL_F32
+    assert np.array_equal(cache.cpu().numpy(), rc.astype(np.float32))
