@@ -80,7 +80,9 @@ const char* kda_status_str(int status);
  *       workspace is then required.
  *   equal lengths: when n_seqs * H is small (at most 64 (sequence, head)
  *       pairs) and T is long, the sequence-parallel path cuts every
- *       sequence into P segments and needs 3 * n_seqs * P * H * 64 KiB
+ *       sequence into P = min(256 / (n_seqs * H), T / 2048) segments (rounded
+ *       so every segment is a whole number of 32-token chunks) and needs
+ *       3 * n_seqs * P * H * 64 KiB
  *       (each segment's transition, local final state and incoming state).
  *       That workspace is optional: without it (NULL or smaller), the
  *       sequential path runs instead, with the same result up to rounding.

@@ -65,7 +65,7 @@ def test_workspace_query(lib):
     assert ws(-1, 1000, 96, 128, 128, 1) == 0
     # equal lengths, few (sequence, head) pairs, long T: sequence-parallel
     # path with P segments, 3 state-sized arrays per segment and head
-    assert ws(1, 1 << 20, 16, 128, 128, 0) == 3 * 8 * 16 * 65536      # P = 256 / (2 * 16)
+    assert ws(1, 1 << 20, 16, 128, 128, 0) == 3 * 16 * 16 * 65536     # P = 256 / 16
     assert ws(2, 6000, 3, 128, 128, 0) == 3 * 2 * 2 * 3 * 65536       # P limited by T / 2048
     assert ws(1, 8192, 16, 128, 128, 0) == 3 * 4 * 16 * 65536        # P = 8192 / 2048
     assert ws(1, 4095, 16, 128, 128, 0) == 0                           # too short to split
