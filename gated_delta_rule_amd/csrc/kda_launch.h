@@ -36,6 +36,11 @@ struct PrefillParams {
     float* u_out;
 };
 
+// The bf16 prefill with 16 value columns per consumer wave and no
+// per-chunk stores, as a three-stage pipeline (scan, tiles, chain) with one
+// workgroup barrier per chunk.  Same arguments, grid and results.
+hipError_t launch_chunk_fwd_pipe(const PrefillParams& p, hipStream_t stream);
+
 // Enqueue the prefill (and, when `sort`, the sequence-order pass first).
 hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, bool sort,
                             hipStream_t stream);
