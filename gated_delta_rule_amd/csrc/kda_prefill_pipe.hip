@@ -34,6 +34,7 @@ namespace kda {
 namespace {
 
 constexpr int PLDR = DK + 8;   // token-major bf16 row stride
+constexpr int LDMB = CH + 8;   // row stride of bf16 [CH][CH] tiles
 
 // One lane's 8 k-values (tokens 4g..4g+3 and 16+4g..16+4g+3, "tile order")
 // of the A operand Y^T[key0 + ln][token] from a token-major [CH][PLDR] tile.
@@ -52,6 +53,27 @@ __device__ __forceinline__ bf16x8 load_tr(uint32_t a, int key0) {
     const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(uintptr_t)(a + 2 * (key0 + 16 * PLDR)));
     const v8s c = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     return __builtin_bit_cast(bf16x8, c);
+}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Two floats to a packed fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    f16x2 r;
+    r[0] = (_Float16)a;
+    r[1] = (_Float16)b;
+    uint32_t u = __builtin_bit_cast(uint32_t, r);
+    asm("" : "+v"(u));
+    return u;
+}
+__device__ __forceinline__ f32x4 mfma32h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// 8 fp16 values in tile order (p[0..3], p[16..19]).
+__device__ __forceinline__ f16x8 load_tile_h(const uint16_t* p) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+    const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
+    return __builtin_bit_cast(f16x8, v);
 }
 // LDS byte address of an element of a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const __bf16* p) {
@@ -107,19 +129,22 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
     // [c % 3]: written by the scan at step c - 2, read up to step c.
     // [c & 1]: written at step c - 2 or c - 1, read up to step c.
     __shared__ __attribute__((aligned(16))) __bf16 sX[3][CH * LDR];    // k e^{g - E0}
-    __shared__ __attribute__((aligned(16))) __bf16 sQX[3][CH * LDR];   // q e^{g - E0} (hi)
+    __shared__ __attribute__((aligned(16))) __bf16 sQX[2][CH * LDR];   // q e^{g - E0} (hi)
     __shared__ __attribute__((aligned(16))) __bf16 sY[3][CH * LDR];    // k e^{E0 - g} (hi)
     __shared__ __attribute__((aligned(16))) __bf16 sYl[3][CH * LDR];   // (lo)
     __shared__ __attribute__((aligned(16))) __bf16 sQXl[2][CH * LDR];  // (lo)
     __shared__ __attribute__((aligned(16))) float sVec[3][2][DK];      // e^{E0}, e^{E1 - E0}
-    __shared__ __attribute__((aligned(16))) float sOne[DK];
-    __shared__ __attribute__((aligned(16))) float sL[CH * LDM];        // beta-scaled L00, L11
+    __shared__ __attribute__((aligned(16))) uint16_t sQp[3][CH * LDR];  // q e^{g} (fp16)
     __shared__ __attribute__((aligned(16))) float sT[2][CH * LDM];     // T00, T11, -L10 (beta-scaled)
-    __shared__ __attribute__((aligned(16))) uint32_t sM[2][CH * LDM];  // M as (hi | lo << 16)
+    __shared__ __attribute__((aligned(16))) __bf16 sMh[2][CH * LDMB];  // M (hi)
+    __shared__ __attribute__((aligned(16))) __bf16 sMl[2][CH * LDMB];  // M (lo)
 
     // M's upper-right 16 x 16 block is identically zero; never rewritten.
-    if (tid < 512) sM[tid >> 8][((tid & 255) >> 4) * LDM + 16 + (tid & 15)] = 0u;
-    if (tid < DK) sOne[tid] = 1.f;
+    if (tid < 512) {
+        const int e = ((tid & 255) >> 4) * LDMB + 16 + (tid & 15);
+        sMh[tid >> 8][e] = (__bf16)0.f;
+        sMl[tid >> 8][e] = (__bf16)0.f;
+    }
 
     auto n_valid = [&](int64_t c) -> int {
         const int64_t nv = t1 - c;
@@ -164,22 +189,16 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
         }
         return acc;
     };
-    // Store an M block (C layout) at rows r0, columns c0, keeping j <= t if diag.
-    auto store_m = [&](uint32_t* Mb, const f32x4& m, int r0, int c0, bool diag) {
-        float v[4];
+    // Store an M block (C layout) at rows r0, columns c0 as hi and lo bf16
+    // tiles, keeping j <= t if diag.
+    auto store_m = [&](__bf16* Mh, __bf16* Ml, const f32x4& m, int r0, int c0, bool diag) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (!diag || ln <= g * 4 + r) ? m[r] : 0.f;
-        const uint32_t h01 = f2_to_bf2(v[0], v[1]), h23 = f2_to_bf2(v[2], v[3]);
-        const float2 f01 = bf2_to_f2(h01), f23 = bf2_to_f2(h23);
-        const uint32_t l01 = f2_to_bf2(v[0] - f01.x, v[1] - f01.y);
-        const uint32_t l23 = f2_to_bf2(v[2] - f23.x, v[3] - f23.y);
-        uint32_t w[4];
-        w[0] = perm2(l01, h01, LO_HALVES);
-        w[1] = perm2(l01, h01, HI_HALVES);
-        w[2] = perm2(l23, h23, LO_HALVES);
-        w[3] = perm2(l23, h23, HI_HALVES);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Mb[(r0 + g * 4 + r) * LDM + c0 + ln] = w[r];
+        for (int r = 0; r < 4; ++r) {
+            const float v = (!diag || ln <= g * 4 + r) ? m[r] : 0.f;
+            const __bf16 hi = (__bf16)v;
+            Mh[(r0 + g * 4 + r) * LDMB + c0 + ln] = hi;
+            Ml[(r0 + g * 4 + r) * LDMB + c0 + ln] = (__bf16)(v - (float)hi);
+        }
     };
 
     // One barrier per step; step s runs the scan of chunk s + 2, the tiles of
@@ -223,19 +242,12 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 const int b3 = (int)(s % 3), b2 = (int)(s & 1);
                 const float* Tb = sT[b2];
                 float4 t00v, t11v, l10v;
-                // S~ = e^{E0} S (for later chunks the previous update applied it)
-                if (s == 0) {
-                    const float* e0 = sVec[b3][0];
-#pragma unroll
-                    for (int it = 0; it < 8; ++it) {
-                        const float4 sc4 = *reinterpret_cast<const float4*>(e0 + it * 16 + g * 4);
-                        S[it][0] *= sc4.x;
-                        S[it][1] *= sc4.y;
-                        S[it][2] *= sc4.z;
-                        S[it][3] *= sc4.w;
-                    }
-                }
-                // K+ S -> R and Q+ S -> O
+                // K+ S = X (e^{E0} S) on bf16 matrix cores with the scaled
+                // state's hi part (the delta rule corrects that rounding), and
+                // Q+ S with both operands in fp16 (q e^{g} <= |q|, so in range):
+                // per k-slice the state is packed to fp16, then scaled to
+                // S~ = e^{E0} S in place (the update adds to S~) and packed to
+                // bf16; the next k-slice's operands load meanwhile.
                 f32x4 R[2], O[2];
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
@@ -243,13 +255,16 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                     O[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
                 const __bf16* Xb = sX[b3] + aoff;
-                const __bf16* Qb = sQX[b3] + aoff;
-                // the next k-slice's operands load while this one's products issue
-                Fr aK[2][2], aQ[2][2];   // [slot][tb]
+                const uint16_t* Qb = sQp[b3] + aoff;
+                const float* e0 = sVec[b3][0] + g * 4;
+                Fr aK[2][2];
+                f16x8 aQ[2][2];   // [slot][tb]
+                float4 ev[2][2];  // e^{E0} rows of the slice's two state tiles
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
                     load_tile(aK[0][tb], Xb + tb * 16 * LDR);
-                    load_tile(aQ[0][tb], Qb + tb * 16 * LDR);
+                    aQ[0][tb] = load_tile_h(Qb + tb * 16 * LDR);
+                    ev[0][tb] = *reinterpret_cast<const float4*>(e0 + tb * 16);
                 }
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
@@ -258,29 +273,43 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
 #pragma unroll
                         for (int tb = 0; tb < 2; ++tb) {
                             load_tile(aK[cur ^ 1][tb], Xb + tb * 16 * LDR + (ks + 1) * 32);
-                            load_tile(aQ[cur ^ 1][tb], Qb + tb * 16 * LDR + (ks + 1) * 32);
+                            aQ[cur ^ 1][tb] = load_tile_h(Qb + tb * 16 * LDR + (ks + 1) * 32);
+                            ev[cur ^ 1][tb] = *reinterpret_cast<const float4*>(e0 + (2 * ks + 2 + tb) * 16);
                         }
                     }
-                    Fr bS, bSl;
+                    f16x8 bS16;
+                    Fr bS;
                     {
+                        u32x4 w;
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            w[2 * i] = pack_h2(S[2 * ks + i][0], S[2 * ks + i][1]);
+                            w[2 * i + 1] = pack_h2(S[2 * ks + i][2], S[2 * ks + i][3]);
+                        }
+                        bS16 = __builtin_bit_cast(f16x8, w);
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const float4 sc4 = ev[cur][i];
+                            S[2 * ks + i][0] *= sc4.x;
+                            S[2 * ks + i][1] *= sc4.y;
+                            S[2 * ks + i][2] *= sc4.z;
+                            S[2 * ks + i][3] *= sc4.w;
+                        }
                         float f[8];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             f[r] = S[2 * ks][r];
                             f[4 + r] = S[2 * ks + 1][r];
                         }
-                        SplitBF<8> s8 = split8(f);
-                        bS.v = s8.hi;
-                        bSl.v = s8.lo;
+                        bS.v = round8(f);
                     }
-                    // K+ S takes the state's hi part only: its rounding is
-                    // corrected by the delta rule; Q+ S reaches o directly.
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb) {
-                        mma(O[tb], aQ[cur][tb], bSl);
                         mma(R[tb], aK[cur][tb], bS);
-                        mma(O[tb], aQ[cur][tb], bS);
+                        O[tb] = mfma32h(aQ[cur][tb], bS16, O[tb]);
                     }
+                    // keep the next slice's loads ahead of this slice's products
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 t00v = *reinterpret_cast<const float4*>(Tb + ln * LDM + g * 4);
                 t11v = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + 16 + g * 4);
@@ -294,12 +323,11 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 // next chunk's values and beta
                 load_v(s + 1);
                 load_beta(s + 1, pb);
-                uint4 mraw[2][2];
+                Fr aM[2], aMl[2];
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
-                    const uint32_t* mr = sM[b2] + (tb * 16 + ln) * LDM + g * 4;
-                    mraw[tb][0] = *reinterpret_cast<const uint4*>(mr);
-                    mraw[tb][1] = *reinterpret_cast<const uint4*>(mr + 16);
+                    load_tile(aM[tb], sMh[b2] + (tb * 16 + ln) * LDMB + g * 4);
+                    load_tile(aMl[tb], sMl[b2] + (tb * 16 + ln) * LDMB + g * 4);
                 }
                 // Block forward substitution of (I + L) U = R':
                 //   U0 = T00 R'0,  U1 = T11 (R'1 - L10 U0)
@@ -342,20 +370,9 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                     const auto ro = make_rsrc(p.o + ((size_t)c0 * H + h) * DK, span_bytes(n_valid(c0), 4));
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb) {
-                        Fr aM, aMl;
-                        {
-                            const uint4 m0 = mraw[tb][0], m1 = mraw[tb][1];
-                            uint4 hv, lv;
-                            hv.x = perm2(m0.y, m0.x, LO_HALVES); hv.y = perm2(m0.w, m0.z, LO_HALVES);
-                            hv.z = perm2(m1.y, m1.x, LO_HALVES); hv.w = perm2(m1.w, m1.z, LO_HALVES);
-                            lv.x = perm2(m0.y, m0.x, HI_HALVES); lv.y = perm2(m0.w, m0.z, HI_HALVES);
-                            lv.z = perm2(m1.y, m1.x, HI_HALVES); lv.w = perm2(m1.w, m1.z, HI_HALVES);
-                            aM.v = __builtin_bit_cast(bf16x8, hv);
-                            aMl.v = __builtin_bit_cast(bf16x8, lv);
-                        }
-                        mma(O[tb], aMl, bUh);
-                        mma(O[tb], aM, bUl);
-                        mma(O[tb], aM, bUh);
+                        mma(O[tb], aMl[tb], bUh);
+                        mma(O[tb], aM[tb], bUl);
+                        mma(O[tb], aM[tb], bUh);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int el = (tb * 16 + g * 4 + r) * rowel + col0 + ln;
@@ -363,14 +380,12 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                         }
                     }
                 }
-                // S <- e^{E1 - E0} (S~ + Y^T U), then the next chunk's S~ (two
-                // separate scalings: their product alone can underflow where the
-                // scaled state does not).  The operands of tile it + 1 load while
-                // tile it's products issue; tile it - 1 is scaled meanwhile.
+                // S <- e^{E1 - E0} (S~ + Y^T U): the unscaled state at the chunk
+                // end.  The operands of tile it + 1 load while tile it's products
+                // issue; tile it - 1 is scaled meanwhile.
                 const uint32_t Yb = lds_addr(sY[b3] + troff);
                 const uint32_t Ylb = lds_addr(sYl[b3] + troff);
                 const float* e1 = sVec[b3][1] + g * 4;
-                const float* e0n = (s + 1 < nch ? sVec[(s + 1) % 3][0] : sOne) + g * 4;
                 bf16x8 aY[2], aYl[2];
                 aY[0] = load_tr(Yb, 0);
                 aYl[0] = load_tr(Ylb, 0);
@@ -386,20 +401,19 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                     S[it] = mfma32(aY[cur], bUh.v, S[it]);
                     if (it > 0) {
                         const float4 a4 = *reinterpret_cast<const float4*>(e1 + (it - 1) * 16);
-                        const float4 b4 = *reinterpret_cast<const float4*>(e0n + (it - 1) * 16);
-                        S[it - 1][0] = S[it - 1][0] * a4.x * b4.x;
-                        S[it - 1][1] = S[it - 1][1] * a4.y * b4.y;
-                        S[it - 1][2] = S[it - 1][2] * a4.z * b4.z;
-                        S[it - 1][3] = S[it - 1][3] * a4.w * b4.w;
+                        S[it - 1][0] *= a4.x;
+                        S[it - 1][1] *= a4.y;
+                        S[it - 1][2] *= a4.z;
+                        S[it - 1][3] *= a4.w;
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 {
                     const float4 a4 = *reinterpret_cast<const float4*>(e1 + 7 * 16);
-                    const float4 b4 = *reinterpret_cast<const float4*>(e0n + 7 * 16);
-                    S[7][0] = S[7][0] * a4.x * b4.x;
-                    S[7][1] = S[7][1] * a4.y * b4.y;
-                    S[7][2] = S[7][2] * a4.z * b4.z;
-                    S[7][3] = S[7][3] * a4.w * b4.w;
+                    S[7][0] *= a4.x;
+                    S[7][1] *= a4.y;
+                    S[7][2] *= a4.z;
+                    S[7][3] *= a4.w;
                 }
             }
             __syncthreads();
@@ -413,12 +427,14 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
         }
     } else if (kind == 1) {
         // ==================================================== scan waves
-        // A lane handles 8 consecutive tokens of the channel pair (2 cp,
-        // 2 cp + 1); the two lanes l and l + 32 cover the 16-token sub-tile sb.
-        constexpr int TPL = 32 / NSCAN, PARTS = 16 / TPL, LPP = 64 / PARTS, WPS = NSCAN / 2;
-        const int sb = role / WPS;
-        const int cp = (role % WPS) * LPP + lane % LPP;
-        const int part = lane / LPP;
+        // A wave covers 16 channel pairs for the whole chunk: lane l handles
+        // the 8 consecutive tokens 8 (l >> 4) .. of the pair (2 cp, 2 cp + 1),
+        // cp = 16 role + (l & 15), so every lane learns the decay E0 after the
+        // first 16 tokens from the cross-lane scan.
+        static_assert(NSCAN == 4, "one scan wave per SIMD");
+        constexpr int TPL = 8;
+        const int cp = role * 16 + (lane & 15);
+        const int part = lane >> 4;
         const int sc = 2 * cp;
         uint32_t xk[TPL], xq[TPL];
         float2 xl[TPL];
@@ -434,14 +450,27 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                            make_rsrc(p.la + eoff, span_bytes(nv, 4))};
         };
         auto load_kq = [&](const ScanSrc& r, int tau) {
-            const int el = (sb * 16 + part * TPL + tau) * rowel + sc;
+            const int el = (part * TPL + tau) * rowel + sc;
             xk[tau] = __builtin_amdgcn_raw_buffer_load_b32(r.k, el * 2, 0, 0);
             xq[tau] = __builtin_amdgcn_raw_buffer_load_b32(r.q, el * 2, 0, 0);
         };
         auto load_la = [&](const ScanSrc& r, int tau) {
-            const int el = (sb * 16 + part * TPL + tau) * rowel + sc;
+            const int el = (part * TPL + tau) * rowel + sc;
             auto lv = __builtin_amdgcn_raw_buffer_load_b64(r.l, el * 4, 0, 0);
             xl[tau] = make_float2(__uint_as_float(lv[0]), __uint_as_float(lv[1]));
+        };
+        // Exclusive prefix `pre` over the four parts, the decay `e0` of parts
+        // 0 and 1 and the chunk total `tot`, each formed in one fixed order.
+        auto scan4 = [&](float a, float& pre, float& e0, float& tot) {
+            const bool odd = part & 1, upper = part & 2;
+            const float b = lane_xor16(a);
+            const float lo = odd ? b : a, hi = odd ? a : b;
+            const float ps = lo + hi;
+            const float c = lane_xor32(ps);
+            const float plo = upper ? c : ps, phi = upper ? ps : c;
+            tot = plo + phi;
+            e0 = plo;
+            pre = (upper ? plo : 0.f) + (odd ? lo : 0.f);
         };
         {
             const ScanSrc r = scan_src(0);
@@ -467,21 +496,22 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 }
 #pragma unroll
                 for (int tau = 0; tau < TPL; ++tau) load_la(nx, tau);
-                float pre0, pre1, tot0, tot1;
-                parts_scan<PARTS>(a0, part, pre0, tot0);
-                parts_scan<PARTS>(a1, part, pre1, tot1);
-                const float ref0 = sb == 0 ? tot0 : 0.f, ref1 = sb == 0 ? tot1 : 0.f;
-                if (part == 0)
-                    *reinterpret_cast<float2*>(&sVec[b3][sb][sc]) =
-                        make_float2(__builtin_amdgcn_exp2f(tot0), __builtin_amdgcn_exp2f(tot1));
-                const int tc = sb * 16 + part * TPL;
-                const float o0 = pre0 - ref0, o1 = pre1 - ref1;
+                float pre0, pre1, E00, E01, tot0, tot1;
+                scan4(a0, pre0, E00, tot0);
+                scan4(a1, pre1, E01, tot1);
+                const float ee0 = __builtin_amdgcn_exp2f(E00), ee1 = __builtin_amdgcn_exp2f(E01);
+                if (part == 0) {
+                    *reinterpret_cast<float2*>(&sVec[b3][0][sc]) = make_float2(ee0, ee1);
+                    *reinterpret_cast<float2*>(&sVec[b3][1][sc]) =
+                        make_float2(__builtin_amdgcn_exp2f(tot0 - E00), __builtin_amdgcn_exp2f(tot1 - E01));
+                }
+                const float o0 = pre0 - E00, o1 = pre1 - E01;
                 // LDS byte addresses of this lane's first row; rows follow at
                 // constant strides, which the stores take as immediate offsets
-                const int e0 = tc * LDR + sc;
-                const uint32_t aX = lds_addr(sX[b3] + e0), aQ = lds_addr(sQX[b3] + e0),
+                const int e0 = part * TPL * LDR + sc;
+                const uint32_t aX = lds_addr(sX[b3] + e0), aQ = lds_addr(sQX[b2] + e0),
                                aQl = lds_addr(sQXl[b2] + e0), aY = lds_addr(sY[b3] + e0),
-                               aYl = lds_addr(sYl[b3] + e0);
+                               aYl = lds_addr(sYl[b3] + e0), aQp = lds_addr((const __bf16*)(sQp[b3] + e0));
                 auto st = [](uint32_t a, uint32_t v) {
                     *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)a = v;
                 };
@@ -504,6 +534,8 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                     st(aQl + ro, f2_to_bf2(Q0 - qhf.x, Q1 - qhf.y));
                     st(aY + ro, yh);
                     st(aYl + ro, f2_to_bf2(Y0 - yhf.x, Y1 - yhf.y));
+                    // q e^{g} = QX e^{E0} in fp16 (at most |q|)
+                    st(aQp + ro, pack_h2(Q0 * ee0, Q1 * ee1));
                 }
             }
             __syncthreads();
@@ -521,39 +553,40 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
             if (c >= 0 && c < nch) {
                 const int b3 = (int)(c % 3), b2 = (int)(c & 1);
                 const __bf16* X = sX[b3];
-                const __bf16* QX = sQX[b3];
+                const __bf16* QX = sQX[b2];
                 const __bf16* Yh = sY[b3];
                 const __bf16* Yl = sYl[b3];
                 const __bf16* QXl = sQXl[b2];
                 float* Tb = sT[b2];
-                uint32_t* Mb = sM[b2];
+                __bf16* Mh = sMh[b2];
+                __bf16* Ml = sMl[b2];
                 if (role == 0) {
                     const f32x4 l00 = block(X, X, 0, Yh, Yh, 0, false);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = g * 4 + r;
-                        sL[row * LDM + ln] = ln < row ? pbp[0][r] * l00[r] : 0.f;
+                        Tb[row * LDM + ln] = ln < row ? pbp[0][r] * l00[r] : 0.f;
                     }
                     wave_lds_sync();
-                    invert16(sL, Tb, lane);
+                    invert16(Tb, Tb, lane);   // in place: all reads precede the writes
                 } else if (role == 1) {
                     const f32x4 l11 = block(X, X, 16, Yh, Yh, 16, false);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = g * 4 + r;
-                        sL[(16 + row) * LDM + 16 + ln] = ln < row ? pbp[1][r] * l11[r] : 0.f;
+                        Tb[(16 + row) * LDM + 16 + ln] = ln < row ? pbp[1][r] * l11[r] : 0.f;
                     }
                     wave_lds_sync();
-                    invert16(sL + 16 * LDM + 16, Tb + 16 * LDM + 16, lane);
+                    invert16(Tb + 16 * LDM + 16, Tb + 16 * LDM + 16, lane);
                 } else if (role == 2) {
                     // -L10 (beta-scaled) goes where the consumers read it
                     const f32x4 v = block(X, X, 16, Yh, Yh, 0, false);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Tb[(16 + g * 4 + r) * LDM + ln] = -pbp[1][r] * v[r];
-                    store_m(Mb, block(QX, QXl, 16, Yh, Yl, 0, true), 16, 0, false);
+                    store_m(Mh, Ml, block(QX, QXl, 16, Yh, Yl, 0, true), 16, 0, false);
                 } else {
-                    store_m(Mb, block(QX, QXl, 16, Yh, Yl, 16, true), 16, 16, true);
-                    store_m(Mb, block(QX, QXl, 0, Yh, Yl, 0, true), 0, 0, true);
+                    store_m(Mh, Ml, block(QX, QXl, 16, Yh, Yl, 16, true), 16, 16, true);
+                    store_m(Mh, Ml, block(QX, QXl, 0, Yh, Yl, 0, true), 0, 0, true);
                 }
             }
 #pragma unroll

@@ -11,6 +11,10 @@ rounds ("plain": once; "split": hi + lo pair), and checks that
   * the kernel's plan stays well inside the 2e-3 max-norm budget, and
   * rounding every operand once would not (so the splits are needed).
 It models the kernel; it does not run it, and shares no code with it.
+
+The pipelined bf16 kernel rounds differently where the state meets a chunk's
+operands: K+ S = X (e^{E0} S) with the state's bf16 hi part only, and
+Q+ S = (q e^{g}) S with both operands rounded once to fp16 (`model_pipe`).
 """
 import numpy as np
 import pytest
@@ -61,6 +65,55 @@ def model(q, k, v, la, beta, S0, plan, C=32):
     return o, S
 
 
+def fp16(x):
+    return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
+
+
+def model_pipe(q, k, v, la, beta, S0, C=32):
+    """The pipelined kernel's plan: L from X, Y rounded once; M from split QX,
+    Y; the block substitution with T rounded once and its right-hand sides
+    split; K+ S with the scaled state's hi part; Q+ S in fp16; the update
+    Y^T U with both split."""
+    T_, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, np.float64)
+    o = np.zeros((T_, dv))
+    for c0 in range(0, T_, C):
+        n = min(C, T_ - c0)
+        pad = lambda a: np.concatenate([a[c0:c0 + n], np.zeros((C - n,) + a.shape[1:])])
+        Q, K, V, b, LA = pad(q), pad(k), pad(v), pad(beta), pad(la)
+        G = np.cumsum(LA, 0)
+        E0, E1 = G[15], G[31]
+        X, QX, Y = K * np.exp(G - E0), Q * np.exp(G - E0), K * np.exp(E0 - G)
+        L = np.tril(b[:, None] * (bf(X) @ bf(Y).T), -1)
+        M = np.tril(split(QX) @ split(Y).T)
+        IL = np.eye(C) + L
+        T00, T11 = np.linalg.inv(IL[:16, :16]), np.linalg.inv(IL[16:, 16:])
+        St = np.exp(E0)[:, None] * S
+        Rp = b[:, None] * (V - bf(X) @ bf(St))
+        U0 = bf(T00) @ split(Rp[:16])
+        U1 = bf(T11) @ split(Rp[16:] - bf(L[16:, :16]) @ split(U0))
+        U = np.concatenate([U0, U1])
+        O = fp16(Q * np.exp(G)) @ fp16(S) + split(M) @ split(U)
+        o[c0:c0 + n] = O[:n]
+        S = np.exp(E1 - E0)[:, None] * (St + split(Y).T @ split(U))
+    return o, S
+
+
+def worst_pipe(T=256, heads=3, wid=1):
+    w = W.workload(wid).shrink(T=T, H=heads, s0_std=0.02)
+    a = W.prefill_inputs(w)
+    ro, rs = oracle.forward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["S0"],
+                            a["cu_seqlens"])
+    eo = es = 0.0
+    for h in range(heads):
+        o, s = model_pipe(*(a[x][:, h].astype(np.float64) for x in ("q", "k", "v", "log_alpha", "beta")),
+                          a["S0"][0, h])
+        eo = max(eo, np.abs(o - ro[:, h]).max() / np.abs(ro[:, h]).max())
+        es = max(es, np.abs(s - rs[0, h]).max() / np.abs(rs[0, h]).max())
+    return eo, es
+
+
 def worst(plan, T=256, heads=3, wid=1):
     w = W.workload(wid).shrink(T=T, H=heads, s0_std=0.02)
     a = W.prefill_inputs(w)
@@ -94,3 +147,10 @@ def test_kernel_plan_within_budget():
 def test_single_rounding_everywhere_exceeds_budget():
     eo, es = worst(ALL_PLAIN)
     assert max(eo, es) > 2e-3, (eo, es)
+
+
+def test_pipelined_plan_within_budget():
+    eo, es = worst_pipe()
+    assert eo < 2e-4 and es < 2e-4, (eo, es)
+    ek, _ = worst(KERNEL_PLAN)
+    assert eo < ek, (eo, ek)   # fp16 Q+ S is the more accurate of the two
