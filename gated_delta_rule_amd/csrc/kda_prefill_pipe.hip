@@ -441,13 +441,19 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
         struct ScanSrc {
             __amdgpu_buffer_rsrc_t k, q, l;
         };
-        auto scan_src = [&](int64_t cidx) {
-            const int64_t c = t0 + cidx * CH;
-            const int nv = n_valid(c);
-            const size_t eoff = ((size_t)c * H + h) * DK;
-            return ScanSrc{make_rsrc((const __bf16*)p.k + eoff, span_bytes(nv, 2)),
-                           make_rsrc((const __bf16*)p.q + eoff, span_bytes(nv, 2)),
-                           make_rsrc(p.la + eoff, span_bytes(nv, 4))};
+        // chunk sources advance by one chunk of rows per step (no 64-bit
+        // multiplies in the loop)
+        const size_t step_el = (size_t)CH * rowel;
+        size_t src_el = ((size_t)t0 * H + h) * DK;   // first element of the next chunk to load
+        int64_t src_rem = t1 - t0;                     // its rows left in the sequence
+        auto scan_src = [&]() {
+            const int nv = src_rem <= 0 ? 0 : (src_rem < CH ? (int)src_rem : CH);
+            const ScanSrc r{make_rsrc((const __bf16*)p.k + src_el, span_bytes(nv, 2)),
+                            make_rsrc((const __bf16*)p.q + src_el, span_bytes(nv, 2)),
+                            make_rsrc(p.la + src_el, span_bytes(nv, 4))};
+            src_el += step_el;
+            src_rem -= CH;
+            return r;
         };
         auto load_kq = [&](const ScanSrc& r, int tau) {
             const int el = (part * TPL + tau) * rowel + sc;
@@ -473,18 +479,18 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
             pre = (upper ? plo : 0.f) + (odd ? lo : 0.f);
         };
         {
-            const ScanSrc r = scan_src(0);
+            const ScanSrc r = scan_src();
 #pragma unroll
             for (int tau = 0; tau < TPL; ++tau) {
                 load_kq(r, tau);
                 load_la(r, tau);
             }
         }
-        for (int64_t s = -2; s < nch; ++s) {
-            const int64_t c = s + 2;
+        int b3 = 0;   // chunk c % 3
+        for (int64_t c = 0; c < nch + 2; ++c) {   // step c - 2 scans chunk c
             if (c < nch) {
-                const int b3 = (int)(c % 3), b2 = (int)(c & 1);
-                const ScanSrc nx = scan_src(c + 1);
+                const int b2 = (int)(c & 1);
+                const ScanSrc nx = scan_src();
                 float cs0[TPL], cs1[TPL];
                 float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -537,6 +543,7 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                     // q e^{g} = QX e^{E0} in fp16 (at most |q|)
                     st(aQp + ro, pack_h2(Q0 * ee0, Q1 * ee1));
                 }
+                b3 = b3 == 2 ? 0 : b3 + 1;
             }
             __syncthreads();
         }
