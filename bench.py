@@ -49,7 +49,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
@@ -414,7 +414,7 @@ def main():
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": 128},
         "roofline": {"bound": "hbm", "achieved": pf_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": pf_gbps / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "chunk_fwd_kernel", "kernel_ms": pf_kernel_ms,
+                     "kernel": "chunk_fwd_pipe_kernel", "kernel_ms": pf_kernel_ms,
                      "algorithmic_bytes": pf_bytes, "algorithmic_flops": pf_flops,
                      "mfma_tflops_algorithmic": pf_tflops,
                      "mfma_frac_algorithmic": pf_tflops / PEAK_BF16_TFLOPS},

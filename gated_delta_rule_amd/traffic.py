@@ -37,8 +37,9 @@ LAUNCHES = {"copy": 6, "prefill": 6, "decode": 8}
 
 # Kernel symbol fragment, profile name, sources the kernel is built from.
 TARGETS = {
-    "prefill": ("chunk_fwd_kernel", "chunk_fwd_workload1",
-                ("kda_prefill.hip", "kda_device.h", "kda_launch.h", "kda_abi.hip")),
+    "prefill": ("chunk_fwd_pipe_kernel", "chunk_fwd_workload1",
+                ("kda_prefill_pipe.hip", "kda_prefill.hip", "kda_chunk.h", "kda_device.h", "kda_launch.h",
+                 "kda_abi.hip")),
     "decode": ("decode_step_kernel", "decode_step_workload4",
                ("kda_decode.hip", "kda_device.h", "kda_launch.h", "kda_abi.hip")),
 }
