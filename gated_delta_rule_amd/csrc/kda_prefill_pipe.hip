@@ -189,6 +189,31 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
         }
         return acc;
     };
+    // Two split blocks A B1^T and A B2^T that share the A rows (loaded once).
+    auto block2 = [&](const __bf16* A, const __bf16* Al, int arow0, const __bf16* B, const __bf16* Bl,
+                      int brow1, int brow2, f32x4& acc1, f32x4& acc2) {
+        acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ao = (arow0 + ln) * LDR + ks * 32 + g * 8;
+            const int bo1 = (brow1 + ln) * LDR + ks * 32 + g * 8;
+            const int bo2 = (brow2 + ln) * LDR + ks * 32 + g * 8;
+            Fr a, al, b1, b1l, b2, b2l;
+            load_contig(a, A + ao);
+            load_contig(al, Al + ao);
+            load_contig(b1, B + bo1);
+            load_contig(b1l, Bl + bo1);
+            load_contig(b2, B + bo2);
+            load_contig(b2l, Bl + bo2);
+            mma(acc1, al, b1);
+            mma(acc2, al, b2);
+            mma(acc1, a, b1l);
+            mma(acc2, a, b2l);
+            mma(acc1, a, b1);
+            mma(acc2, a, b2);
+        }
+    };
     // Store an M block (C layout) at rows r0, columns c0 as hi and lo bf16
     // tiles, keeping j <= t if diag.
     auto store_m = [&](__bf16* Mh, __bf16* Ml, const f32x4& m, int r0, int c0, bool diag) {
@@ -590,10 +615,12 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                     const f32x4 v = block(X, X, 16, Yh, Yh, 0, false);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Tb[(16 + g * 4 + r) * LDM + ln] = -pbp[1][r] * v[r];
-                    store_m(Mh, Ml, block(QX, QXl, 16, Yh, Yl, 0, true), 16, 0, false);
-                } else {
-                    store_m(Mh, Ml, block(QX, QXl, 16, Yh, Yl, 16, true), 16, 16, true);
                     store_m(Mh, Ml, block(QX, QXl, 0, Yh, Yl, 0, true), 0, 0, true);
+                } else {
+                    f32x4 m10, m11;
+                    block2(QX, QXl, 16, Yh, Yl, 0, 16, m10, m11);
+                    store_m(Mh, Ml, m10, 16, 0, false);
+                    store_m(Mh, Ml, m11, 16, 16, true);
                 }
             }
 #pragma unroll
