@@ -36,9 +36,9 @@ struct PrefillParams {
     float* u_out;
 };
 
-// The bf16 prefill with 16 value columns per consumer wave and no
-// per-chunk stores, as a three-stage pipeline (scan, tiles, chain) with one
-// workgroup barrier per chunk.  Same arguments, grid and results.
+// The bf16 prefill with 16 value columns per consumer wave as a three-stage
+// pipeline (scan, tiles, chain) with one workgroup barrier per chunk.  Same
+// arguments, grid and outputs (h_states, r_out, u_out included).
 hipError_t launch_chunk_fwd_pipe(const PrefillParams& p, hipStream_t stream);
 
 // Enqueue the prefill (and, when `sort`, the sequence-order pass first).

@@ -776,8 +776,7 @@ hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, b
     } while (0)
     if (bf16_in) {
         if (wcols == 32) KDA_FWD(__bf16, 32, 4);
-        else if (!hs) return launch_chunk_fwd_pipe(p, stream);
-        else KDA_FWD(__bf16, 16, 8);
+        else return launch_chunk_fwd_pipe(p, stream);
     } else {
         if (wcols == 32) KDA_FWD(float, 32, 4);
         else KDA_FWD(float, 16, 8);

@@ -82,7 +82,9 @@ __device__ __forceinline__ uint32_t lds_addr(const __bf16* p) {
 
 }  // namespace
 
-template <int NSCAN>
+// STORE_H: also store, per chunk, the state at its start (h_states), V - K+ S
+// (r_out) and U (u_out), as chunk_fwd_kernel does for the backward pass.
+template <int NSCAN, bool STORE_H>
 __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(PrefillParams p) {
     constexpr int WCOLS = 16;         // value columns per consumer wave
     constexpr int DVW = 4 * WCOLS;    // value columns per workgroup
@@ -267,6 +269,14 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 const int b3 = (int)(s % 3), b2 = (int)(s & 1);
                 const float* Tb = sT[b2];
                 float4 t00v, t11v, l10v;
+                if constexpr (STORE_H) {   // the state at this chunk's start -> slot t0 / 32 + n + s
+                    float* hb = p.h_states + ((size_t)(t0 / CH + n + s) * H + h) * (DK * DK);
+#pragma unroll
+                    for (int it = 0; it < 8; ++it)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            hb[(size_t)(it * 16 + g * 4 + r) * DK + col0 + ln] = S[it][r];
+                }
                 // K+ S = X (e^{E0} S) on bf16 matrix cores with the scaled
                 // state's hi part (the delta rule corrects that rounding), and
                 // Q+ S with both operands in fp16 (q e^{g} <= |q|, so in range):
@@ -339,12 +349,27 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 t00v = *reinterpret_cast<const float4*>(Tb + ln * LDM + g * 4);
                 t11v = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + 16 + g * 4);
                 l10v = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + g * 4);
-                // R' = B_beta (V - K+ S)
+                // R' = B_beta (V - K+ S)  (V - K+ S itself kept for the backward pass)
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        R[tb][r] = pb[tb][r] * (__uint_as_float((uint32_t)pv[tb][r] << 16) - R[tb][r]);
+                        R[tb][r] = __uint_as_float((uint32_t)pv[tb][r] << 16) - R[tb][r];
+                if constexpr (STORE_H) {
+                    const int64_t cs = t0 + s * CH;
+                    const auto rr = make_rsrc(p.r_out + ((size_t)cs * H + h) * DK, span_bytes(n_valid(cs), 4));
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int el = (tb * 16 + g * 4 + r) * rowel + col0 + ln;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(R[tb][r]), rr, el * 4, 0, 0);
+                        }
+                }
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) R[tb][r] *= pb[tb][r];
                 // next chunk's values and beta
                 load_v(s + 1);
                 load_beta(s + 1, pb);
@@ -374,6 +399,16 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
 #pragma unroll
                     for (int r = 0; r < 4; ++r) b[r] = rhs[r];
                     mma_k16<false, SPLITB>(U1, t11, b);
+                }
+                if constexpr (STORE_H) {
+                    const int64_t cs = t0 + s * CH;
+                    const auto ru = make_rsrc(p.u_out + ((size_t)cs * H + h) * DK, span_bytes(n_valid(cs), 4));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int el = (g * 4 + r) * rowel + col0 + ln;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(U0[r]), ru, el * 4, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(U1[r]), ru, (el + 16 * rowel) * 4, 0, 0);
+                    }
                 }
                 // U as the B operand of M U and Y^T U (tile order: U0 rows, U1 rows).
                 Fr bUh, bUl;
@@ -634,8 +669,11 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
 
 hipError_t launch_chunk_fwd_pipe(const PrefillParams& p, hipStream_t stream) {
     const int64_t groups = ((int64_t)p.n_units + 7) / 8;
-    hipLaunchKernelGGL(chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN>, dim3((unsigned)(groups * 8 * p.n_slices)),
-                       dim3(64 * (8 + KDA_PIPE_NSCAN)), 0, stream, p);
+    const dim3 grid((unsigned)(groups * 8 * p.n_slices)), block(64 * (8 + KDA_PIPE_NSCAN));
+    if (p.h_states)
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
