@@ -8,12 +8,18 @@
 //   O    = Q+ S + Tril(Q+ K-^T) U                                      (63)
 //   S   <- Diag(e^{g_C}) S + K_end^T U,  k_end = k e^{g_C - g}          (66)
 //
+// This kernel runs fp32 inputs, and bf16 inputs with 32 value columns per
+// consumer wave (one workgroup per head, used when there are 256 or more
+// (sequence, head) units); bf16 with two 64-column slices per head runs the
+// pipelined kernel of kda_prefill_pipe.hip instead.
+//
 // MI355X design (not the pages' two-kernel split):
-//   * One workgroup (4 waves) per (sequence, head, value-column slice)
-//     walks the sequence's chunks serially.  The recurrence acts on S from
-//     the left, so value columns evolve independently: each wave owns
-//     WCOLS columns of the 128 x 128 fp32 state and keeps them in MFMA
-//     accumulator registers for the whole sequence.
+//   * One workgroup (4 consumer waves and NPROD producer waves) per
+//     (sequence, head, value-column slice) walks the sequence's chunks
+//     serially.  The recurrence acts on S from the left, so value columns
+//     evolve independently: each consumer wave owns WCOLS columns of the
+//     128 x 128 fp32 state and keeps them in MFMA accumulator registers for
+//     the whole sequence.
 //   * C = 32 tokens per chunk.  Every decay product is factored about the
 //     cumulative decay E0 at the end of the chunk's first 16 tokens:
 //         X = k e^{g - E0},  QX = q e^{g - E0},  Y = k e^{E0 - g},
@@ -26,8 +32,8 @@
 //         K+ S = X (e^{E0} S),  Q+ S = QX (e^{E0} S),
 //         S_next = e^{E1 - E0} (e^{E0} S + Y^T U)   (E1 = g_C).
 //   * The decay scan and the operand tiles are produced once per chunk by
-//     all 256 threads (two key channels and 8 tokens each; the two halves
-//     of a 16-token sub-tile exchange partial sums across the wave) directly
+//     the producer waves (two key channels and 32 / NPROD tokens per lane;
+//     the parts of a 16-token sub-tile exchange partial sums across the wave) directly
 //     in the MFMA operand layouts (token-major rows for the products over
 //     channels, channel-major rows of Y for the product over tokens), so
 //     the matrix loops only load and issue.  Inputs arrive through buffer
