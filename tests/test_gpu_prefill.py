@@ -95,6 +95,28 @@ def test_varlen_packing_with_empty_and_ragged_sequences():
     check_full(w, arrs, cu=cu, label=f"varlen lens={lens}")
 
 
+@pytest.mark.parametrize("T", [64, 65, 96, 97, 128])
+def test_bf16_pipeline_fill_and_drain(T):
+    """Two to four chunks per sequence: the bf16 kernel overlaps the gate scan of
+    chunk n+2, the tiles of chunk n+1 and the state update of chunk n, so short
+    sequences end the pipeline before it is full."""
+    w, arrs = small(T, 2, 1, 0.02)
+    check_full(w, arrs, label=f"bf16 pipeline T={T}")
+
+
+def test_varlen_pipeline_lengths_mixed():
+    """Packed sequences of 1 to 4 chunks (and ragged tails) in one launch."""
+    lens = [1, 32, 33, 64, 65, 96, 97, 0, 2, 128]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    w = W.workload(2).shrink(n_varlen=0, B=1, T=T, H=2)
+    a = W.prefill_inputs(w)
+    rng = np.random.default_rng(1)
+    a["S0"] = (0.02 * rng.standard_normal((len(lens), 2, 128, 128))).astype(np.float32)
+    arrs = {n: a[n] for n in ("q", "k", "v", "log_alpha", "beta", "S0")}
+    check_full(w, arrs, cu=cu, label=f"varlen pipeline lens={lens}")
+
+
 def test_continuation_matches_single_run():
     """chunk_fwd(x[:T1]) then chunk_fwd(x[T1:], S0=S_T1) equals chunk_fwd(x)."""
     w, arrs = small(300, 2, 1, 0.02)
