@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix
 PEAK_F32_TFLOPS = 157.3         # MI355X dense fp32 matrix
+N_XCD = 8                       # MI355X accelerator complex dies
+N_SIMD = 1024                   # 256 compute units x 4 SIMDs
 # Backward pass, algorithmic flops per token and head: the forward pass it
 # repeats (131072) plus its own products per 32-token chunk (P, M: 2 x
 # 2*32*32*128; the state-gradient walk: K_end dS, Q+^T dO, Kb^T W at
@@ -269,7 +271,7 @@ def main():
     import torch
     import gated_delta_rule_amd as kda
     from gated_delta_rule_amd import workloads as W
-    from gated_delta_rule_amd.traffic import measured as measured_traffic
+    from gated_delta_rule_amd.traffic import measured as measured_traffic, measured_mfma
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -320,6 +322,21 @@ def main():
     pf_gbps = pf_bytes / (pf_kernel_ms * 1e-3) / 1e9
     pf_tflops = pf_flops / (pf_kernel_ms * 1e-3) / 1e12
     traffic = measured_traffic("prefill")
+    mfma = measured_mfma()
+    mfma_counters = None
+    if mfma is not None:
+        # matrix-core flops the counters saw per launch (MOPS x 512), over the
+        # live launch time; busy = MFMA busy cycles summed over the SIMDs over
+        # (GPU active cycles of one XCD x 1024 SIMDs)
+        hw = sum(mfma["hw_flops_per_launch_from_counters"].values())
+        c = mfma["counters"]
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"]["per_dispatch"] / (
+            c["GRBM_GUI_ACTIVE"]["per_dispatch"] / N_XCD * N_SIMD)
+        mfma_counters = {"hw_flops_per_launch": hw,
+                         "hw_tflops": hw / (pf_kernel_ms * 1e-3) / 1e12,
+                         "hw_frac_of_bf16_peak": hw / (pf_kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "mfma_busy_frac": busy,
+                         "source": "profiles/chunk_fwd_workload1_mfma.json"}
     del d, o, S_T
     torch.cuda.empty_cache()
     if args.only == "prefill":
@@ -417,7 +434,8 @@ def main():
                      "kernel": "chunk_fwd_pipe_kernel", "kernel_ms": pf_kernel_ms,
                      "algorithmic_bytes": pf_bytes, "algorithmic_flops": pf_flops,
                      "mfma_tflops_algorithmic": pf_tflops,
-                     "mfma_frac_algorithmic": pf_tflops / PEAK_BF16_TFLOPS},
+                     "mfma_frac_algorithmic": pf_tflops / PEAK_BF16_TFLOPS,
+                     "mfma_counters": mfma_counters},
         "decode": {
             "metric": "decode-step state GB/s", "value": state_gbps, "unit": "GB/s",
             "ms_per_step": dec_ms, "steps": steps_d,

@@ -1,4 +1,4 @@
-"""HBM traffic of the prefill and decode kernels from rocprofv3 counters.
+"""HBM traffic and matrix-core work of the kernels from rocprofv3 counters.
 
     python -m gated_delta_rule_amd.traffic collect [--out DIR]
 
@@ -15,8 +15,16 @@ is the profiled program: it prepares the resident inputs of one workload
 and launches its kernel a few times.  The orchestrating process never
 touches the GPU itself.
 
+    python -m gated_delta_rule_amd.traffic mfma [--out DIR]
+
+runs one rocprofv3 pass per matrix-core counter (MFMA operations per data
+type, MFMA busy cycles, SQ busy cycles, GPU active cycles) over the prefill
+target and writes `profiles/chunk_fwd_workload1_mfma.json`: the counters per
+launch, the hardware flops they imply (each MOPS count stands for 512 flops)
+and the flops the kernel's instruction mix implies (`prefill_mfma_flops`).
+
 The JSON records a hash of the kernel's sources; the benchmark reports the
-traffic only while that hash matches the sources it runs.
+counters only while that hash matches the sources it runs.
 """
 from __future__ import annotations
 
@@ -55,6 +63,47 @@ def sources_hash(kind):
 
 def profile_path(kind, profiles_dir=None):
     return os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), TARGETS[kind][1] + "_traffic.json")
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+MOPS_FLOPS = 512              # flops per count of an SQ_INSTS_VALU_MFMA_MOPS_* counter
+
+
+def prefill_mfma_flops(T=8192, H=96, chunk=32, slices=2):
+    """Matrix-core flops one launch of the pipelined bf16 prefill kernel issues,
+    counted from its instruction mix (16x16x32 = 16,384 flops, 16x16x16 = 8,192).
+
+    Per chunk and workgroup (64 value columns of one head):
+      consumer wave x4: K+S 8 bf16 and Q+S 8 fp16 16x16x32; block substitution
+        3 x (hi, lo) 16x16x16 bf16; O = M U 2 x 3 16x16x32; state update
+        8 x 3 16x16x32;
+      tile waves: L00 and L11 4 each, -L10 4, M00 12, M10 and M11 24 (16x16x32).
+    """
+    k32, k16 = 16384, 8192
+    consumer_bf16 = 8 * k32 + 6 * k16 + 6 * k32 + 24 * k32
+    consumer_f16 = 8 * k32
+    tiles_bf16 = (4 + 4 + 4 + 12 + 24) * k32
+    units = (T // chunk) * H * slices
+    return {"bf16": units * (4 * consumer_bf16 + tiles_bf16), "f16": units * 4 * consumer_f16}
+
+
+def mfma_profile_path(profiles_dir=None):
+    return os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), "chunk_fwd_workload1_mfma.json")
+
+
+def measured_mfma():
+    """The prefill kernel's stored matrix-core counters, or None when they were
+    taken on other sources (or never)."""
+    try:
+        with open(mfma_profile_path()) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_sha256_16") != sources_hash("prefill"):
+        return None
+    return rec
 
 
 def measured(kind):
@@ -109,16 +158,20 @@ def run_target(kind):
 
 
 # ------------------------------------------------------------ orchestration
-def counter_pass(kind, counter, out):
+def counter_pass(kind, counter, out, run=True):
+    """One rocprofv3 pass of `counter` over the target (skipped with run=False,
+    which re-reads a previous pass's output); returns its value per
+    (dispatch, kernel)."""
     d = os.path.join(out, f"{kind}_{counter}")
     cmd = ["timeout", "-s", "KILL", "120", "rocprofv3", "--pmc", counter, "-d", d, "-o", "run",
            "--output-format", "csv", "--", sys.executable, "-u", "-m", "gated_delta_rule_amd.traffic",
            "target", kind]
     env = dict(os.environ, TMPDIR="/tmp", PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
-    print("running:", " ".join(cmd), flush=True)
-    r = subprocess.run(cmd, cwd="/tmp", env=env)
-    if r.returncode != 0:
-        raise SystemExit(f"rocprofv3 pass {kind}/{counter} failed with status {r.returncode}")
+    if run:
+        print("running:", " ".join(cmd), flush=True)
+        r = subprocess.run(cmd, cwd="/tmp", env=env)
+        if r.returncode != 0:
+            raise SystemExit(f"rocprofv3 pass {kind}/{counter} failed with status {r.returncode}")
     files = []
     for dp, _, fs in os.walk(d):
         files += [os.path.join(dp, f) for f in fs if f.endswith("counter_collection.csv")]
@@ -186,6 +239,35 @@ def collect(out, profiles_dir):
         print(f"{kind}: {total / 1e9:.4f} GB per launch -> {path}", flush=True)
 
 
+def collect_mfma(out, profiles_dir, run=True):
+    os.makedirs(out, exist_ok=True)
+    os.makedirs(profiles_dir, exist_ok=True)
+    frag = TARGETS["prefill"][0]
+    rec = {}
+    for counter in MFMA_COUNTERS:
+        val, n = kib_per_dispatch(counter_pass("prefill", counter, out, run), frag)
+        rec[counter] = {"per_dispatch": val, "dispatches": n}
+        print(f"prefill {counter}: {val:.6g} per dispatch", flush=True)
+    hw = {t: rec[f"SQ_INSTS_VALU_MFMA_MOPS_{t.upper()}"]["per_dispatch"] * MOPS_FLOPS
+          for t in ("bf16", "f16", "f32")}
+    doc = {
+        "kernel": frag,
+        "workload": "prefill B=1 T=8192 H=96 d=128 bf16, S0=0, o and S_T fp32",
+        "command": "python -m gated_delta_rule_amd.traffic mfma (per pass: rocprofv3 --pmc <counter> "
+                   "-d <dir> -o run --output-format csv -- python -u -m gated_delta_rule_amd.traffic "
+                   "target prefill)",
+        "counters": rec,
+        "hw_flops_per_launch_from_counters": hw,
+        "hw_flops_per_launch_from_instruction_mix": prefill_mfma_flops(),
+        "kernel_sources_sha256_16": sources_hash("prefill"),
+    }
+    path = mfma_profile_path(profiles_dir)
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    print(f"prefill matrix-core counters -> {path}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -196,9 +278,16 @@ def main():
                    help="directory for the raw counter output")
     c.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"),
                    help="where the per-kernel JSON summaries go")
+    m = sub.add_parser("mfma")
+    m.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "mfma"))
+    m.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
+    m.add_argument("--parse-only", action="store_true",
+                   help="summarise the counter output already under --out")
     args = ap.parse_args()
     if args.cmd == "target":
         run_target(args.kind)
+    elif args.cmd == "mfma":
+        collect_mfma(os.path.abspath(args.out), os.path.abspath(args.profiles_dir), not args.parse_only)
     else:
         collect(os.path.abspath(args.out), os.path.abspath(args.profiles_dir))
 
