@@ -274,12 +274,12 @@ def main():
     t = sub.add_parser("target")
     t.add_argument("kind", choices=["copy", "prefill", "decode"])
     c = sub.add_parser("collect")
-    c.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "traffic"),
+    c.add_argument("--out", default=os.path.join(ROOT, "counters_out", "traffic"),
                    help="directory for the raw counter output")
     c.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"),
                    help="where the per-kernel JSON summaries go")
     m = sub.add_parser("mfma")
-    m.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "mfma"))
+    m.add_argument("--out", default=os.path.join(ROOT, "counters_out", "mfma"))
     m.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     m.add_argument("--parse-only", action="store_true",
                    help="summarise the counter output already under --out")
