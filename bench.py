@@ -443,7 +443,7 @@ def main():
                                    "fp32 state [256,96,128,128] ~N(0,0.02^2), chained steps"},
             "roofline": {"bound": "hbm", "achieved": dec_gbps_all, "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": dec_gbps_all / PEAK_HBM_GBPS,
-                         "traffic": dec_traffic, "kernel": "decode_step_kernel",
+                         "traffic": dec_traffic, "kernel": "recurrent_kernel",
                          "kernel_ms": dec_kernel_ms, "algorithmic_bytes": dec_bytes,
                          "algorithmic_flops": n_states * DECODE_FLOPS_PER_STATE},
         },

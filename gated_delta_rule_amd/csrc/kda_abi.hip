@@ -275,8 +275,10 @@ int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,
     for (const Range& r : ins)
         if (overlaps(ro, r) || overlaps(rs, r)) return KDA_ERR_ALIASING;
     if (overlaps(ro, rs)) return KDA_ERR_ALIASING;
-    hipError_t e = kda::launch_decode_step(q, k, v, in_dtype == KDA_BF16, log_alpha, beta, S,
-                                           states, o, stream);
+    // one token per request on the recurrent kernel: no replay, state committed
+    hipError_t e = kda::launch_recurrent(q, k, v, in_dtype == KDA_BF16, log_alpha, beta, nullptr,
+                                         nullptr, nullptr, nullptr, nullptr, nullptr, S, states, H,
+                                         1, 0, 1, o, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

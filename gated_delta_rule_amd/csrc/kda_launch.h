@@ -116,8 +116,4 @@ struct BwdParams {
 };
 hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream);
 
-hipError_t launch_decode_step(const void* q, const void* k, const void* v, bool bf16_in,
-                              const float* log_alpha, const float* beta, float* S,
-                              int64_t n_states, float* o, hipStream_t stream);
-
 }  // namespace kda

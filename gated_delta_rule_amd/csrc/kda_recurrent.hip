@@ -17,13 +17,17 @@
 //   u = beta (v - x),  x = k^T Diag(a) S,  o = y + (q . k) u,  y = q^T Diag(a) S,
 //   S <- Diag(a) S + k u^T.
 //
-// Work decomposition: one 1024-thread workgroup per state; wave w owns value
-// columns 8w..8w+7 for all 128 key rows, lane l holding column 8w + (l & 7)
-// of rows (l >> 3) + 8i, i < 16.  The sums over key rows then stay inside
-// the wave (three cross-lane butterflies, no LDS and no barrier per token);
-// waves only share the token data, staged in LDS 16 tokens at a time.  The
-// state moves between HBM and registers through LDS so that both transfers
-// are 1 KB-contiguous per wave instruction.
+// Work decomposition: one 1024-thread workgroup per state at a time; wave w
+// owns value columns 8w..8w+7 for all 128 key rows, lane l holding column
+// 8w + (l & 7) of rows (l >> 3) + 8i, i < 16.  The sums over key rows then
+// stay inside the wave (three cross-lane butterflies, no LDS and no barrier
+// per token); waves only share the token data, staged in LDS 16 tokens at a
+// time.  The state moves between HBM and registers through LDS so that both
+// transfers are 1 KB-contiguous per wave instruction.  On large batches a
+// workgroup walks up to eight states in turn and reads the next state from
+// HBM while it runs the current one's last tokens and writes it back, so
+// the state stream does not stop while a compute unit computes.  The
+// one-token decode step is this kernel with one token per request.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -32,6 +36,7 @@ namespace kda {
 constexpr int RC_THREADS = 1024;
 constexpr int RC_TOK = 16;       // tokens staged per pass
 constexpr int RC_LDS = 136;      // LDS row stride of the staged state (floats)
+constexpr int RC_MAX_PER_WG = 8;  // states per workgroup on large batches (measured: 8 ahead of 24, 96, 4, 2, 1)
 
 // x + (value of lane l ^ 8), within each 16-lane row (rotation by 8).
 __device__ __forceinline__ float add_xor8(float x) {
@@ -58,15 +63,17 @@ struct TokSrc {
 template <typename InT>
 __global__ __launch_bounds__(RC_THREADS) void recurrent_kernel(TokSrc rep, const int32_t* n_replay,
                                                                TokSrc out, float* S, float* o,
-                                                               int32_t H, int32_t commit) {
+                                                               int32_t H, int32_t commit,
+                                                               int64_t n_states, int32_t per_wg) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 7, rg = lane >> 3;
     const int col = wave * 8 + c;
-    const int64_t bh = blockIdx.x;
-    const int64_t b = bh / H;
-    const int h = (int)(bh - b * H);
+    const int64_t first = (int64_t)blockIdx.x * per_wg;
+    const int64_t last = first + per_wg < n_states ? first + per_wg : n_states;
+    int64_t bh = first, b = 0;
+    int h = 0;
 
     // One LDS area: the staged state while it moves to or from HBM, the token
     // data in between (barriers separate the two uses).  Token data: k, q and
@@ -81,18 +88,17 @@ __global__ __launch_bounds__(RC_THREADS) void recurrent_kernel(TokSrc rep, const
     float* sB = smem + 4 * RC_TOK * 128;
     float* sQK = sB + RC_TOK;
 
-    float4* Sg = reinterpret_cast<float4*>(S + bh * (128 * 128));
-    // state: HBM -> LDS (1 KB per wave instruction) -> registers
+    // The next state's HBM read is issued before this state's tokens run, so
+    // it overlaps them; a state is 1 KB per wave instruction both ways.
+    f32x4 pf[4];
+    auto fetch = [&](int64_t st) {
+        const f32x4* g = reinterpret_cast<const f32x4*>(S + st * (128 * 128));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = tid + RC_THREADS * j;
-        const float4 x = Sg[e];
-        *reinterpret_cast<float4*>(&sS[(e >> 5) * RC_LDS + 4 * (e & 31)]) = x;
-    }
-    __syncthreads();
+        for (int j = 0; j < 4; ++j) pf[j] = __builtin_nontemporal_load(&g[tid + RC_THREADS * j]);
+    };
     float s[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = sS[(rg + 8 * i) * RC_LDS + col];
+    bool fetched = false;
+    fetch(first);
 
     auto store_state = [&]() {
         __syncthreads();   // every lane is done reading sS
@@ -102,12 +108,13 @@ __global__ __launch_bounds__(RC_THREADS) void recurrent_kernel(TokSrc rep, const
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = tid + RC_THREADS * j;
-            Sg[e] = *reinterpret_cast<const float4*>(&sS[(e >> 5) * RC_LDS + 4 * (e & 31)]);
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sS[(e >> 5) * RC_LDS + 4 * (e & 31)]),
+                                        &reinterpret_cast<f32x4*>(S + bh * (128 * 128))[e]);
         }
     };
 
     // Run n tokens of one stream; outputs when `emit`.
-    auto run = [&](const TokSrc& src, int n, bool emit) {
+    auto run = [&](const TokSrc& src, int n, bool emit, bool prefetch) {
         for (int t0 = 0; t0 < n; t0 += RC_TOK) {
             const int nt = n - t0 < RC_TOK ? n - t0 : RC_TOK;
             __syncthreads();   // previous tokens consumed
@@ -138,6 +145,12 @@ __global__ __launch_bounds__(RC_THREADS) void recurrent_kernel(TokSrc rep, const
                 }
             }
             __syncthreads();
+            // the next state's read goes out after this pass's last token
+            // loads, so that waiting for those does not wait for it
+            if (prefetch && t0 + RC_TOK >= n && bh + 1 < last) {
+                fetch(bh + 1);
+                fetched = true;
+            }
             for (int tt = 0; tt < nt; ++tt) {
                 const float4* k4 = reinterpret_cast<const float4*>(&sK[tt][rg * 16]);
                 const float4* q4 = reinterpret_cast<const float4*>(&sQ[tt][rg * 16]);
@@ -178,15 +191,32 @@ __global__ __launch_bounds__(RC_THREADS) void recurrent_kernel(TokSrc rep, const
         }
     };
 
-    int nr = 0;
-    if (rep.T > 0) {
-        nr = n_replay ? n_replay[b] : rep.T;
-        nr = nr < 0 ? 0 : (nr > rep.T ? rep.T : nr);
-        run(rep, nr, false);
+    for (; bh < last; ++bh) {
+        b = bh / H;
+        h = (int)(bh - b * H);
+        // prefetched state -> LDS -> registers (the previous state's store has
+        // finished reading the staging area)
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = tid + RC_THREADS * j;
+            *reinterpret_cast<f32x4*>(&sS[(e >> 5) * RC_LDS + 4 * (e & 31)]) = pf[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = sS[(rg + 8 * i) * RC_LDS + col];
+        int nr = 0;
+        if (rep.T > 0) {
+            nr = n_replay ? n_replay[b] : rep.T;
+            nr = nr < 0 ? 0 : (nr > rep.T ? rep.T : nr);
+            run(rep, nr, false, false);
+        }
+        if (!commit && nr > 0) store_state();
+        fetched = false;
+        run(out, out.T, true, true);
+        if (!fetched && bh + 1 < last) fetch(bh + 1);
+        if (commit) store_state();
     }
-    if (!commit && nr > 0) store_state();
-    run(out, out.T, true);
-    if (commit) store_state();
 }
 
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, bool bf16_in,
@@ -197,13 +227,18 @@ hipError_t launch_recurrent(const void* q, const void* k, const void* v, bool bf
                             float* o, hipStream_t stream) {
     const TokSrc out{q, k, v, log_alpha, beta, T};
     const TokSrc rep{rq, rk, rv, rlog_alpha, rbeta, Tr};
-    dim3 grid((unsigned)n_states), block(RC_THREADS);
+    // several states per workgroup once there are enough to keep every
+    // compute unit busy (at least eight workgroups each), so that state
+    // reads overlap token work
+    const int64_t fill = n_states / 2048;
+    const int32_t per_wg = fill < 1 ? 1 : (fill > RC_MAX_PER_WG ? RC_MAX_PER_WG : (int32_t)fill);
+    dim3 grid((unsigned)((n_states + per_wg - 1) / per_wg)), block(RC_THREADS);
     if (bf16_in)
         hipLaunchKernelGGL(recurrent_kernel<__bf16>, grid, block, 0, stream, rep, n_replay, out, S,
-                           o, H, commit);
+                           o, H, commit, n_states, per_wg);
     else
         hipLaunchKernelGGL(recurrent_kernel<float>, grid, block, 0, stream, rep, n_replay, out, S,
-                           o, H, commit);
+                           o, H, commit, n_states, per_wg);
     return hipGetLastError();
 }
 

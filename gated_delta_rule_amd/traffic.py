@@ -48,8 +48,8 @@ TARGETS = {
     "prefill": ("chunk_fwd_pipe_kernel", "chunk_fwd_workload1",
                 ("kda_prefill_pipe.hip", "kda_prefill.hip", "kda_chunk.h", "kda_device.h", "kda_launch.h",
                  "kda_abi.hip")),
-    "decode": ("decode_step_kernel", "decode_step_workload4",
-               ("kda_decode.hip", "kda_device.h", "kda_launch.h", "kda_abi.hip")),
+    "decode": ("recurrent_kernel", "decode_step_workload4",
+               ("kda_recurrent.hip", "kda_device.h", "kda_launch.h", "kda_abi.hip")),
 }
 
 
