@@ -96,6 +96,30 @@ __global__ __launch_bounds__(RC_THREADS) void recurrent_kernel(TokSrc rep, const
 #pragma unroll
         for (int j = 0; j < 4; ++j) pf[j] = __builtin_nontemporal_load(&g[tid + RC_THREADS * j]);
     };
+    // Without a replay stream and with 2..16 tokens (one staging pass), the
+    // next state's token inputs are read ahead too (wave w < T: token w,
+    // channels lane and lane + 64), so a state's step starts with no HBM
+    // wait (8 tokens: 0.90 against 0.94 ms at B=256, H=96; with one token
+    // it measured slower, 0.540 against 0.511 ms, so it stays off there).
+    float tk[2], tq[2], tv[2], tl[2], tb = 0.f;
+    bool tok_ready = false;
+    const bool tok_ahead = rep.T == 0 && out.T >= 2 && out.T <= RC_TOK;
+    auto fetch_tokens = [&](int64_t st) {
+        if (wave < out.T) {
+            const int64_t sb = st / H;
+            const size_t row = ((size_t)sb * out.T + wave) * H + (st - sb * H);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int ch = lane + 64 * half;
+                tk[half] = to_f32(((const InT*)out.k)[row * 128 + ch]);
+                tq[half] = to_f32(((const InT*)out.q)[row * 128 + ch]);
+                tv[half] = to_f32(((const InT*)out.v)[row * 128 + ch]);
+                tl[half] = out.la[row * 128 + ch];
+            }
+            tb = out.beta[row];
+        }
+        tok_ready = true;
+    };
     float s[16];
     bool fetched = false;
     fetch(first);
@@ -120,35 +144,43 @@ __global__ __launch_bounds__(RC_THREADS) void recurrent_kernel(TokSrc rep, const
             __syncthreads();   // previous tokens consumed
             // stage nt tokens: thread (token tt = tid >> 6, channel pair) -- one wave per token
             if (wave < nt) {
-                const size_t row = ((size_t)b * src.T + t0 + wave) * H + h;
-                const InT* kp = (const InT*)src.k + row * 128;
-                const InT* qp = (const InT*)src.q + row * 128;
-                const InT* vp = (const InT*)src.v + row * 128;
-                const float* lp = src.la + row * 128;
+                if (!tok_ready) {   // not read ahead: this pass's tokens now
+                    const size_t row = ((size_t)b * src.T + t0 + wave) * H + h;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int ch = lane + 64 * half;
+                        tk[half] = to_f32(((const InT*)src.k)[row * 128 + ch]);
+                        tq[half] = to_f32(((const InT*)src.q)[row * 128 + ch]);
+                        tv[half] = to_f32(((const InT*)src.v)[row * 128 + ch]);
+                        tl[half] = src.la[row * 128 + ch];
+                    }
+                    tb = src.beta[row];
+                }
                 float qk = 0.f;
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int ch = lane + 64 * half;
-                    const float kk = to_f32(kp[ch]), qq = to_f32(qp[ch]);
                     const int slot = (ch & 7) * 16 + (ch >> 3);   // row ch = rg + 8 i
-                    sK[wave][slot] = kk;
-                    sQ[wave][slot] = qq;
-                    sA[wave][slot] = __expf(lp[ch]);
-                    sV[wave][ch] = to_f32(vp[ch]);
-                    qk += qq * kk;
+                    sK[wave][slot] = tk[half];
+                    sQ[wave][slot] = tq[half];
+                    sA[wave][slot] = __expf(tl[half]);
+                    sV[wave][ch] = tv[half];
+                    qk += tq[half] * tk[half];
                 }
 #pragma unroll
                 for (int off = 32; off > 0; off >>= 1) qk += __shfl_xor(qk, off);
                 if (lane == 0) {
                     sQK[wave] = qk;
-                    sB[wave] = src.beta[row];
+                    sB[wave] = tb;
                 }
             }
+            tok_ready = false;
             __syncthreads();
             // the next state's read goes out after this pass's last token
             // loads, so that waiting for those does not wait for it
             if (prefetch && t0 + RC_TOK >= n && bh + 1 < last) {
                 fetch(bh + 1);
+                if (tok_ahead) fetch_tokens(bh + 1);
                 fetched = true;
             }
             for (int tt = 0; tt < nt; ++tt) {

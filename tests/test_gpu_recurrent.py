@@ -148,3 +148,35 @@ def test_deterministic():
         torch.cuda.synchronize()
         outs.append((o.cpu(), S.cpu()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("B,H,T,replay", [(65, 67, 5, False), (65, 67, 17, False),
+                                          (67, 97, 1, False), (65, 67, 4, True)])
+def test_many_states_per_workgroup(B, H, T, replay):
+    """Batches of 4,096+ states, where a workgroup walks several states and
+    reads the next one (and, with 2..16 tokens and no replay, its tokens)
+    while the current one runs; state counts that leave a short last
+    workgroup."""
+    new, _ = tokens(B, T, H, seed=6)
+    S0 = state(B, H, seed=7)
+    dn = dev(new, "bf16")
+    S = torch.from_numpy(S0).cuda()
+    say(f"[recurrent] {B * H} states T={T} replay={replay}: GPU")
+    if replay:
+        rep, _ = tokens(B, 3, H, seed=8)
+        n = np.random.default_rng(9).integers(0, 4, B).astype(np.int32)
+        dr = dev(rep, "bf16")
+        o = kda.recurrent_fwd(dn["q"], dn["k"], dn["v"], dn["log_alpha"], dn["beta"], S,
+                              replay=tuple(dr[x] for x in NAMES),
+                              n_replay=torch.from_numpy(n).cuda(), commit=False)
+        torch.cuda.synchronize()
+        _, s_mid = oracle_run(rep, S0, n)
+        ro, _ = oracle_run(new, s_mid.astype(np.float64))
+        rs = s_mid
+    else:
+        o = kda.recurrent_fwd(dn["q"], dn["k"], dn["v"], dn["log_alpha"], dn["beta"], S)
+        torch.cuda.synchronize()
+        ro, rs = oracle_run(new, S0)
+    eo, es = rel_err(o.cpu().numpy(), ro), rel_err(S.cpu().numpy(), rs)
+    say(f"[recurrent] {B * H} states T={T} replay={replay}: rel err o {eo:.3e} S {es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
