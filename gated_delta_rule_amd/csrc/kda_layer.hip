@@ -13,10 +13,12 @@
 // section 1.4): out = o / sqrt(mean o^2 + 1e-6) * w * sigmoid(g).
 //
 // All three kernels move each element once and do a few flops on it, so they
-// are HBM-bound: a wave owns one head's 128 channels (two per lane) of one
-// row (epilogue) or of eight consecutive rows (prologue, with the conv
-// weights and the last three raw inputs kept in registers), sums over the
-// row by DPP wave reduction.  The prologue reads and writes through buffer
+// are HBM-bound.  Prologue: a wave owns one head's 128 channels (two per
+// lane) of eight consecutive rows, with the conv weights and the last three
+// raw inputs kept in registers, and sums over the row by DPP wave
+// reduction.  Epilogue: a lane owns four channels of one of two consecutive
+// rows, so every wave instruction moves 1 KB, and a wave reads the inputs
+// of four row pairs before it reduces the first (half-wave DPP sums).  The prologue reads and writes through buffer
 // resources with 32-bit offsets from its first row (rows past the end read
 // as zero, and the window before a sequence start takes the cache entry
 // through the same out-of-range trick instead of a branch).  The cache
@@ -248,20 +250,37 @@ __global__ __launch_bounds__(LY_THREADS) void conv_cache_kernel(LayerParams p) {
     for (int m = 0; m < 3; ++m) cp[m * HD] = nv[m];
 }
 
+// Epilogue: lane l holds channels 4 (l & 31)..+3 of item 2 j + (l >> 5), so a
+// wave instruction reads two consecutive items (1 KB); each wave runs
+// EP_IT such pairs with every load issued before the first reduction
+// (0.183 ms at T=8192 H=96 against 0.213 ms with one item per wave and two
+// channels per lane; 8 pairs per wave 0.200 ms).
+constexpr int EP_IT = 4;
 __global__ __launch_bounds__(LY_THREADS) void epilogue_kernel(const float* __restrict__ o,
                                                               const float* __restrict__ g,
                                                               const float* __restrict__ w,
                                                               float* __restrict__ out, int64_t items) {
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * (LY_THREADS / 64) + (threadIdx.x >> 6);
-    if (item >= items) return;
-    const int64_t base = item * 128 + 2 * lane;
-    const float2 x = *reinterpret_cast<const float2*>(o + base);
-    const float2 gg = *reinterpret_cast<const float2*>(g + base);
-    const float2 ww = *reinterpret_cast<const float2*>(w + 2 * lane);
-    const float r = rsqrtf(wave_sum(x.x * x.x + x.y * x.y) * (1.f / 128.f) + LY_EPS);
-    *reinterpret_cast<float2*>(out + base) =
-        make_float2(x.x * r * ww.x * sigm(gg.x), x.y * r * ww.y * sigm(gg.y));
+    const int64_t first = ((int64_t)blockIdx.x * (LY_THREADS / 64) + (threadIdx.x >> 6)) * (2 * EP_IT);
+    const int c = 4 * (lane & 31);
+    const float4 ww = *reinterpret_cast<const float4*>(w + c);
+    f32x4 x[EP_IT], gg[EP_IT];
+#pragma unroll
+    for (int j = 0; j < EP_IT; ++j) {
+        int64_t item = first + 2 * j + (lane >> 5);
+        item = item < items ? item : items - 1;   // a short tail re-reads the last item
+        x[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o + item * 128 + c));
+        gg[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + item * 128 + c));
+    }
+#pragma unroll
+    for (int j = 0; j < EP_IT; ++j) {
+        const int64_t item = first + 2 * j + (lane >> 5);
+        const f32x4 v = x[j];
+        const float r = rsqrtf(half_sum_dpp(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]) * (1.f / 128.f) + LY_EPS);
+        const f32x4 res = {v[0] * r * ww.x * sigm(gg[j][0]), v[1] * r * ww.y * sigm(gg[j][1]),
+                           v[2] * r * ww.z * sigm(gg[j][2]), v[3] * r * ww.w * sigm(gg[j][3])};
+        if (item < items) __builtin_nontemporal_store(res, reinterpret_cast<f32x4*>(out + item * 128 + c));
+    }
 }
 
 hipError_t launch_prologue(const LayerParams& p, bool bf16_in, hipStream_t stream) {
@@ -283,8 +302,8 @@ hipError_t launch_prologue(const LayerParams& p, bool bf16_in, hipStream_t strea
 hipError_t launch_epilogue(const float* o, const float* g, const float* w, float* out, int64_t items,
                            hipStream_t stream) {
     if (items > 0)
-        hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)((items + 3) / 4)), dim3(LY_THREADS), 0,
-                           stream, o, g, w, out, items);
+        hipLaunchKernelGGL(epilogue_kernel, dim3((unsigned)((items + 8 * EP_IT - 1) / (8 * EP_IT))),
+                           dim3(LY_THREADS), 0, stream, o, g, w, out, items);
     return hipGetLastError();
 }
 
