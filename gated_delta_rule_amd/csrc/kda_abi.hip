@@ -90,7 +90,7 @@ const char* kda_status_str(int status) {
         case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: tensors need 16-byte alignment (beta, cu_seqlens 4-byte)";
         case KDA_ERR_ALIASING: return "KDA_ERR_ALIASING: an output overlaps an input";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
-        case KDA_ERR_TOO_LARGE: return "KDA_ERR_TOO_LARGE: sizes exceed the launch limits";
+        case KDA_ERR_TOO_LARGE: return "KDA_ERR_TOO_LARGE: sizes exceed the launch limits (or H > KDA_MAX_HEADS)";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
         default: return "unknown kda_status";
     }
@@ -99,6 +99,7 @@ const char* kda_status_str(int status) {
 size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H, int32_t dk,
                                      int32_t dv, int varlen) {
     if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim || H < 1 || T < 0) return 0;
+    if (H > KDA_MAX_HEADS) return 0;
     if (varlen) return n_seqs > kOrderMax ? 0 : (size_t)n_seqs * sizeof(int32_t);
     const Split sp = split_for(n_seqs, T, H);
     if (sp.P < 2) return 0;
@@ -114,6 +115,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
     if (dk != kHeadDim || dv != kHeadDim || H < 1 || n_seqs < 0 || T < 0)
         return KDA_ERR_BAD_SHAPE;
+    if (H > KDA_MAX_HEADS) return KDA_ERR_TOO_LARGE;
     const bool varlen = cu_seqlens != nullptr;
     int64_t tokens = 0;  // rows of the token axis
     if (varlen) {
@@ -259,6 +261,7 @@ int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,
                     int32_t dk, int32_t dv, float* o, hipStream_t stream) {
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
     if (dk != kHeadDim || dv != kHeadDim || H < 1 || B < 0) return KDA_ERR_BAD_SHAPE;
+    if (H > KDA_MAX_HEADS) return KDA_ERR_TOO_LARGE;
     if (B == 0) return KDA_OK;
     const int64_t states = (int64_t)B * H;
     if (states > kMaxGrid) return KDA_ERR_TOO_LARGE;
@@ -292,6 +295,7 @@ int kda_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
     if (dk != kHeadDim || dv != kHeadDim || H < 1 || B < 0 || T < 0 || T > kMaxRecurrent ||
         Tr < 0 || Tr > kMaxRecurrent)
         return KDA_ERR_BAD_SHAPE;
+    if (H > KDA_MAX_HEADS) return KDA_ERR_TOO_LARGE;
     if (B == 0) return KDA_OK;
     const int64_t states = (int64_t)B * H;
     if (states > kMaxGrid) return KDA_ERR_TOO_LARGE;
@@ -334,6 +338,7 @@ int kda_prologue(const void* q_raw, const void* k_raw, const void* v_raw, int in
                  hipStream_t stream) {
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
     if (dk != kHeadDim || H < 1 || n_seqs < 0 || T < 0) return KDA_ERR_BAD_SHAPE;
+    if (H > KDA_MAX_HEADS) return KDA_ERR_TOO_LARGE;
     const bool varlen = cu_seqlens != nullptr;
     int64_t rows = 0, elems = 0, hrows = 0;
     if (varlen) rows = T;
@@ -393,6 +398,7 @@ int kda_prologue(const void* q_raw, const void* k_raw, const void* v_raw, int in
 int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, int32_t H,
                  int32_t dv, float* out, hipStream_t stream) {
     if (dv != kHeadDim || H < 1 || rows < 0) return KDA_ERR_BAD_SHAPE;
+    if (H > KDA_MAX_HEADS) return KDA_ERR_TOO_LARGE;
     int64_t items = 0, elems = 0;
     if (!mul_ok(rows, (int64_t)H, &items) || !mul_ok(items, kHeadDim, &elems) ||
         elems > INT64_MAX / 8 || (items + 3) / 4 > kMaxGrid)
@@ -435,6 +441,7 @@ static bool bwd_layout(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayout* L) 
 size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H, int32_t dk, int32_t dv,
                                      int varlen) {
     if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim || H < 1 || T < 0) return 0;
+    if (H > KDA_MAX_HEADS) return 0;
     int64_t tokens = T;
     if (!varlen && !mul_ok((int64_t)n_seqs, T, &tokens)) return 0;
     BwdLayout L;
@@ -451,6 +458,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     if (in_dtype != KDA_BF16 && in_dtype != KDA_F32) return KDA_ERR_BAD_DTYPE;
     if (dk != kHeadDim || dv != kHeadDim || H < 1 || n_seqs < 0 || T < 0)
         return KDA_ERR_BAD_SHAPE;
+    if (H > KDA_MAX_HEADS) return KDA_ERR_TOO_LARGE;
     const bool varlen = cu_seqlens != nullptr;
     int64_t tokens = 0;
     if (varlen) tokens = T;

@@ -88,7 +88,9 @@ hipError_t launch_epilogue(const float* o, const float* g, const float* w, float
 // Backward pass after a forward pass that stored the state at every chunk
 // start in h (see PrefillParams::h_states; chunk j of sequence n in slot
 // start_n / 32 + n + j).  Arrays: h, dsn [slots, H, 128, 128];
-// tmp [slots, H, 3, 32, 32] (T, M, P); w [tokens, H, 128].
+// tmp [slots, H, 15488] floats per (chunk, head): T^T, M^T, P [32][32],
+// K_end^T, Q+^T, -(B_beta K+)^T [128][32] and e^{g_C} [128];
+// w, r, u [tokens, H, 128].
 struct BwdParams {
     const void* q;
     const void* k;

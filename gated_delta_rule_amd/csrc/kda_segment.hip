@@ -26,8 +26,10 @@ constexpr int MG_COLS = 16;     // value columns per workgroup
 constexpr int MG_LDF = 132;     // LDS row stride of F (floats)
 
 __global__ __launch_bounds__(MG_THREADS) void segment_merge_kernel(
-    const float* __restrict__ F, const float* __restrict__ Sl, const float* __restrict__ S0,
-    float* __restrict__ S_in, float* __restrict__ S_T, int32_t P, int32_t H) {
+    const float* __restrict__ F, const float* __restrict__ Sl, const float* S0,
+    float* __restrict__ S_in, float* S_T, int32_t P, int32_t H) {
+    // S0 and S_T may be the same array (in-place carry): each thread reads
+    // its S0 elements before it writes the same elements of S_T.
     constexpr size_t ST = 128 * 128;
     const int cb = blockIdx.x & 7;
     const int bh = blockIdx.x >> 3;

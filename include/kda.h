@@ -50,6 +50,12 @@ extern "C" {
 
 #define KDA_ABI_VERSION 3
 
+/* Largest head count any entry point accepts: the kernels address a chunk's
+ * token rows (up to 32 rows of H * 128 fp32 values) with 32-bit byte
+ * offsets, which stay below 2^31 for H <= 65536.  Larger H ->
+ * KDA_ERR_TOO_LARGE (the workspace queries return 0). */
+#define KDA_MAX_HEADS 65536
+
 typedef enum kda_status {
     KDA_OK = 0,
     KDA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
@@ -58,7 +64,7 @@ typedef enum kda_status {
     KDA_ERR_MISALIGNED = 4,     /* pointer alignment contract violated */
     KDA_ERR_ALIASING = 5,       /* an output overlaps an input illegally */
     KDA_ERR_WORKSPACE = 6,      /* workspace missing or too small */
-    KDA_ERR_TOO_LARGE = 7,      /* sizes beyond the launch limits */
+    KDA_ERR_TOO_LARGE = 7,      /* sizes beyond the launch limits (or H > KDA_MAX_HEADS) */
     KDA_ERR_HIP = 8             /* the kernel launch itself failed */
 } kda_status;
 

@@ -263,3 +263,24 @@ def test_chunk_bwd_validation(lib):
     assert bwd(lib, ws=P["ws"] + 4) == ALIGN
     assert bwd(lib, n=2 ** 31 - 1, T=2 ** 40) == LARGE
     assert bwd(lib, n=0) == OK
+
+
+def test_head_count_upper_bound(lib):
+    """The kernels address a chunk's token rows with 32-bit byte offsets, so
+    H above KDA_MAX_HEADS is refused with KDA_ERR_TOO_LARGE by every entry
+    point (and the workspace queries report 0) before anything is enqueued."""
+    hmax = int(re.search(r"#define KDA_MAX_HEADS (\d+)", open(HEADER).read()).group(1))
+    assert hmax == 65536 and 32 * hmax * 128 * 4 <= 2 ** 31
+    big = hmax + 1
+    assert chunk(lib, H=big, n=1, T=1) == LARGE
+    assert chunk(lib, H=big, n=1, T=1, cu=P["cu"], ws=P["ws"], wsb=4) == LARGE
+    assert decode(lib, H=big, B=1) == LARGE
+    assert recurrent(lib, H=big, B=1) == LARGE
+    assert prologue(lib, H=big, n=1, T=1) == LARGE
+    assert epilogue(lib, H=big, rows=1) == LARGE
+    assert bwd(lib, H=big, n=1, T=1) == LARGE
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 1, big, 128, 128, 1) == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(1, 1, big, 128, 128, 0) == 0
+    # the bound itself is accepted (validation continues to later checks)
+    assert chunk(lib, H=hmax, n=1, T=1, q=None) == NULLP
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 1, hmax, 128, 128, 1) == 4

@@ -264,5 +264,6 @@ def test_workload2_full_size_sampled_units():
 @pytest.mark.timeout(900)
 def test_workload3_full_size_sampled_columns():
     """T=1,048,576, H=16: eight value columns of two heads, every token (the
-    sequence-parallel path: 8 segments per head)."""
+    sequence-parallel path: 16 segments per head, one 512-thread workgroup
+    per segment chain)."""
     _sampled_check(W.workload(3), [0, 9], "workload 3 (T=1M H=16)", cols=(40, 48))

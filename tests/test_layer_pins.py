@@ -100,3 +100,33 @@ def test_prologue_composition():
     assert np.allclose(v, y / (1 + np.exp(-y)), atol=1e-14)
     assert np.array_equal(c[1], raw[1][-3:])
     assert la.shape == (T, H, d) and be.shape == (T, H)
+
+
+def test_prologue_gate_outputs_pinned():
+    """log alpha = -5 sigmoid(a) and beta = sigmoid(b), read out of prologue()
+    itself at points where the values are fixed without the formula: a = 0
+    gives the midpoint -2.5, a -> +inf the lower bound -5, a -> -inf no
+    decay (0); b = 0 gives 1/2, b -> +inf full write (1), b -> -inf none (0).
+    ("Kimi K3 技术报告解读" section 3.3 class KDA and section 3.5: the decay's
+    log is bounded below by g_min = -5 through a sigmoid; the write gate is a
+    sigmoid.)  A sign error (sigmoid(-a) or sigmoid(-b)) swaps the limits."""
+    T, H, d = 3, 2, 128
+    raw = [np.zeros((T, H, d)) for _ in range(3)]
+    cw = np.zeros((3, H, d, 4))
+    a = np.zeros((T, H, d))
+    a[1] = 60.0
+    a[2] = -60.0
+    b = np.array([[0.0, 0.0], [60.0, 60.0], [-60.0, -60.0]])
+    _, _, _, la, be, _ = L.prologue(*raw, cw, a, b)
+    assert np.array_equal(la[0], np.full((H, d), -2.5))
+    assert np.allclose(la[1], -5.0, rtol=0, atol=1e-24)
+    assert np.all(la[2] <= 0) and np.all(la[2] > -1e-24)
+    assert np.array_equal(be[0], np.full(H, 0.5))
+    assert np.allclose(be[1], 1.0, rtol=0, atol=1e-24)
+    assert np.all(be[2] >= 0) and np.all(be[2] < 1e-24)
+    # strictly monotone in the same direction as the pre-activation
+    a = np.linspace(-8, 8, 17)[:, None, None] * np.ones((1, H, d))
+    b = np.linspace(-8, 8, 17)[:, None] * np.ones((1, H))
+    raw = [np.zeros((17, H, d)) for _ in range(3)]
+    _, _, _, la, be, _ = L.prologue(*raw, cw, a, b)
+    assert np.all(np.diff(la[:, 0, 0]) < 0) and np.all(np.diff(be[:, 0]) > 0)
