@@ -194,6 +194,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     p.h_states = nullptr;
     p.r_out = nullptr;
     p.u_out = nullptr;
+    p.S_T2 = nullptr;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -236,20 +237,31 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     const int swcols = 128 / (4 * ps.n_slices);
     if (((cunits + 7) / 8) * 8 * ps.n_slices > kMaxGrid) return KDA_ERR_TOO_LARGE;
 
-    kda::PrefillParams pa = ps;   // local final states
-    pa.S0 = nullptr;
-    pa.o = nullptr;
-    pa.S_T = wSl;
-    kda::PrefillParams pb = ps;   // transitions
-    pb.S0 = nullptr;
-    pb.o = nullptr;
-    pb.S_T = wF;
-    pb.s0_identity = 1;
     kda::PrefillParams pc = ps;   // outputs from the true incoming states
     pc.S0 = wSin;
     pc.S_T = nullptr;
-    hipError_t e = kda::launch_chunk_fwd(pa, bf16_in, swcols, false, stream);
-    if (e == hipSuccess) e = kda::launch_chunk_fwd(pb, bf16_in, swcols, false, stream);
+    hipError_t e;
+    if (ps.n_slices == 1) {
+        // one launch runs both chains of every segment on the same tiles
+        kda::PrefillParams pd = ps;
+        pd.S0 = nullptr;
+        pd.o = nullptr;
+        pd.S_T = wSl;
+        pd.S_T2 = wF;
+        e = kda::launch_chunk_fwd_dual(pd, bf16_in, stream);
+    } else {
+        kda::PrefillParams pa = ps;   // local final states
+        pa.S0 = nullptr;
+        pa.o = nullptr;
+        pa.S_T = wSl;
+        kda::PrefillParams pb = ps;   // transitions
+        pb.S0 = nullptr;
+        pb.o = nullptr;
+        pb.S_T = wF;
+        pb.s0_identity = 1;
+        e = kda::launch_chunk_fwd(pa, bf16_in, swcols, false, stream);
+        if (e == hipSuccess) e = kda::launch_chunk_fwd(pb, bf16_in, swcols, false, stream);
+    }
     if (e == hipSuccess)
         e = kda::launch_segment_merge(wF, wSl, S0, wSin, S_T, n_seqs, sp.P, H, stream);
     if (e == hipSuccess) e = kda::launch_chunk_fwd(pc, bf16_in, swcols, false, stream);
@@ -542,6 +554,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     p.h_states = ws + L.h;
     p.r_out = ws + L.r;
     p.u_out = ws + L.u;
+    p.S_T2 = nullptr;
     const bool bf16_in = in_dtype == KDA_BF16;
     hipError_t e = kda::launch_chunk_fwd(p, bf16_in, wcols, false, stream);
     if (e != hipSuccess) return KDA_ERR_HIP;

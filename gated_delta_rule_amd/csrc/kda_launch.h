@@ -34,6 +34,11 @@ struct PrefillParams {
     // With h_states: V - K+ S and U of every chunk, token-major like o.
     float* r_out;
     float* u_out;
+    // Two chains at once (launch_chunk_fwd_dual): the chain from S0 (or zero)
+    // with the values v, whose final state goes to S_T, and the chain from the
+    // identity with v read as zero, whose final state (the transition) goes
+    // to S_T2.  o is not written.  nullptr otherwise.
+    float* S_T2;
 };
 
 // The bf16 prefill with 16 value columns per consumer wave as a three-stage
@@ -44,6 +49,11 @@ hipError_t launch_chunk_fwd_pipe(const PrefillParams& p, hipStream_t stream);
 // Enqueue the prefill (and, when `sort`, the sequence-order pass first).
 hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, bool sort,
                             hipStream_t stream);
+
+// Both chains of a segment in one launch (one 32-column-per-wave workgroup
+// per (segment, head); n_slices must be 1): the local final state from S0 or
+// zero into S_T and the transition (identity start, v = 0) into S_T2.
+hipError_t launch_chunk_fwd_dual(const PrefillParams& prm, bool bf16_in, hipStream_t stream);
 
 // S_in[b, r] and S_T[b] of the segmented prefill: S_in[b, 0] = S0[b] (or 0),
 // S_in[b, r + 1] = F[b, r] S_in[b, r] + Sl[b, r]; S_T[b] = the state after

@@ -57,10 +57,15 @@
 
 namespace kda {
 
-// NPROD producer waves (4 or 8) follow the 4 consumer waves.
-template <typename InT, int WCOLS, int NPROD, bool STORE_H>
+// NPROD producer waves (4 or 8) follow the 4 consumer waves.  DUAL: every
+// consumer wave carries two chains over the same tiles, the one from S0 (or
+// zero) with the values v (final state -> S_T) and the one from the identity
+// with v read as zero (final state = the transition -> S_T2); o is not
+// formed.
+template <typename InT, int WCOLS, int NPROD, bool STORE_H, bool DUAL = false>
 __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillParams p) {
     constexpr bool F32 = std::is_same<InT, float>::value;
+    static_assert(!(DUAL && STORE_H), "the dual chain keeps no per-chunk states");
     constexpr int NCT = WCOLS / 16;   // 16-column tiles per consumer wave
     constexpr int DVW = 4 * WCOLS;    // value columns per workgroup
     constexpr int ES = (int)sizeof(InT);
@@ -145,6 +150,7 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
 
     // ======================================================== consumer state
     f32x4 S[8][NCT];
+    f32x4 S2[DUAL ? 8 : 1][DUAL ? NCT : 1];   // the identity-start chain
     const size_t sbase = ((size_t)n * H + h) * (DK * DK);
     float pv[2][NCT][4], pb[2][4];
     auto load_v = [&](int64_t cidx, float (&v)[2][NCT][4]) {
@@ -170,6 +176,7 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
     // Chain values carried from phase A to phase B of a step.
     f32x4 O[2][NCT], U0[NCT], U1[NCT];
     Frag<F32> bUh[NCT], bUl[NCT];
+    Frag<F32> bUh2[DUAL ? NCT : 1], bUl2[DUAL ? NCT : 1];
 
     // ======================================================== producer state
     // Scan role: a lane handles TPL consecutive tokens of the channel pair
@@ -387,6 +394,15 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                                    : p.S0 ? p.S0[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 +
                                                  ct * 16 + ln]
                                           : 0.f;
+        if constexpr (DUAL) {
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        S2[it][ct][r] = it * 16 + g * 4 + r == col0 + ct * 16 + ln ? 1.f : 0.f;
+        }
         // state at the start of chunk j -> slot hslot0 + j
         float* hbase = nullptr;
         if constexpr (STORE_H) hbase = p.h_states + ((size_t)(t0 / CH + n) * H + h) * (DK * DK);
@@ -422,51 +438,74 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                         S[it][ct][1] *= sc4.y;
                         S[it][ct][2] *= sc4.z;
                         S[it][ct][3] *= sc4.w;
+                        if constexpr (DUAL) {
+                            S2[it][ct][0] *= sc4.x;
+                            S2[it][ct][1] *= sc4.y;
+                            S2[it][ct][2] *= sc4.z;
+                            S2[it][ct][3] *= sc4.w;
+                        }
                     }
                 }
             }
-            // K+ S -> R and Q+ S -> O
-            f32x4 R[2][NCT];
+            // K+ S -> R and Q+ S -> O (DUAL: K+ S of both chains, no O)
+            f32x4 R[2][NCT], R2[2][DUAL ? NCT : 1];
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     R[tb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
                     O[tb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (DUAL) R2[tb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
+            // the k-slice ks of a chain's state as the B operand (hi, lo)
+            auto state_op = [&](const f32x4 (&St)[8][NCT], int ks, int ct, Frag<F32>& hi,
+                                Frag<F32>& lo) {
+                float f[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f[r] = St[2 * ks][ct][r];
+                    f[4 + r] = St[2 * ks + 1][ct][r];
+                }
+                if constexpr (F32) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hi.v[e] = f[e];
+                } else {
+                    SplitBF<8> s8 = split8(f);
+                    hi.v = s8.hi;
+                    lo.v = s8.lo;
+                }
+            };
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 Frag<F32> bS[NCT], bSl[NCT];
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    float f[8];
+                for (int ct = 0; ct < NCT; ++ct) state_op(S, ks, ct, bS[ct], bSl[ct]);
+                if constexpr (DUAL) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        f[r] = S[2 * ks][ct][r];
-                        f[4 + r] = S[2 * ks + 1][ct][r];
-                    }
-                    if constexpr (F32) {
+                    for (int tb = 0; tb < 2; ++tb) {
+                        Frag<F32> aK;
+                        load_tile(aK, sX[buf] + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) bS[ct].v[e] = f[e];
-                    } else {
-                        SplitBF<8> s8 = split8(f);
-                        bS[ct].v = s8.hi;
-                        bSl[ct].v = s8.lo;
-                    }
-                }
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    Frag<F32> aK, aQ;
-                    load_tile(aK, sX[buf] + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
-                    load_tile(aQ, sQX[buf] + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        if constexpr (!F32) {
-                            mma(R[tb][ct], aK, bSl[ct]);
-                            mma(O[tb][ct], aQ, bSl[ct]);
+                        for (int ct = 0; ct < NCT; ++ct) {
+                            if constexpr (!F32) mma(R[tb][ct], aK, bSl[ct]);
+                            mma(R[tb][ct], aK, bS[ct]);
                         }
-                        mma(R[tb][ct], aK, bS[ct]);
-                        mma(O[tb][ct], aQ, bS[ct]);
+                    }
+                } else {
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) {
+                        Frag<F32> aK, aQ;
+                        load_tile(aK, sX[buf] + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
+                        load_tile(aQ, sQX[buf] + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) {
+                            if constexpr (!F32) {
+                                mma(R[tb][ct], aK, bSl[ct]);
+                                mma(O[tb][ct], aQ, bSl[ct]);
+                            }
+                            mma(R[tb][ct], aK, bS[ct]);
+                            mma(O[tb][ct], aQ, bS[ct]);
+                        }
                     }
                 }
             }
@@ -490,8 +529,7 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        R[tb][ct][r] = pb[tb][r] * (pv[tb][ct][r] - R[tb][ct][r]);
+                    for (int r = 0; r < 4; ++r) R[tb][ct][r] = pb[tb][r] * (pv[tb][ct][r] - R[tb][ct][r]);
             // next chunk's values and beta (used one step later)
             load_v(cidx + 1, pv);
             load_beta(cidx + 1, pb);
@@ -506,21 +544,68 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                 t11[0] = a.x; t11[1] = a.y; t11[2] = a.z; t11[3] = a.w;
                 a = *reinterpret_cast<const float4*>(Tb + (16 + ln) * LDM + g * 4);
                 nl10[0] = a.x; nl10[1] = a.y; nl10[2] = a.z; nl10[3] = a.w;
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
+                auto subst = [&](const f32x4& r0, const f32x4& r1, f32x4& u0, f32x4& u1) {
                     float b[4];
-                    U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    u0 = f32x4{0.f, 0.f, 0.f, 0.f};
+                    u1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) b[r] = R[0][ct][r];
-                    mma_k16<F32, SPLITB>(U0[ct], t00, b);
-                    f32x4 rhs = R[1][ct];
+                    for (int r = 0; r < 4; ++r) b[r] = r0[r];
+                    mma_k16<F32, SPLITB>(u0, t00, b);
+                    f32x4 rhs = r1;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) b[r] = U0[ct][r];
+                    for (int r = 0; r < 4; ++r) b[r] = u0[r];
                     mma_k16<F32, SPLITB>(rhs, nl10, b);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) b[r] = rhs[r];
-                    mma_k16<F32, SPLITB>(U1[ct], t11, b);
+                    mma_k16<F32, SPLITB>(u1, t11, b);
+                };
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) subst(R[0][ct], R[1][ct], U0[ct], U1[ct]);
+                if constexpr (DUAL) {
+                    // the identity chain (v = 0), after the first one so that
+                    // its K+ S, R' and U reuse those registers; its U goes
+                    // straight into its B operands
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        Frag<F32> bS[NCT], bSl[NCT];
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) state_op(S2, ks, ct, bS[ct], bSl[ct]);
+#pragma unroll
+                        for (int tb = 0; tb < 2; ++tb) {
+                            Frag<F32> aK;
+                            load_tile(aK, sX[buf] + (tb * 16 + ln) * LDR + ks * 32 + g * 4);
+#pragma unroll
+                            for (int ct = 0; ct < NCT; ++ct) {
+                                if constexpr (!F32) mma(R2[tb][ct], aK, bSl[ct]);
+                                mma(R2[tb][ct], aK, bS[ct]);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) R2[tb][ct][r] = -pb[tb][r] * R2[tb][ct][r];
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        f32x4 u0, u1;
+                        subst(R2[0][ct], R2[1][ct], u0, u1);
+                        float f[8];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            f[r] = u0[r];
+                            f[4 + r] = u1[r];
+                        }
+                        if constexpr (F32) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) bUh2[ct].v[e] = f[e];
+                        } else {
+                            SplitBF<8> s8 = split8(f);
+                            bUh2[ct].v = s8.hi;
+                            bUl2[ct].v = s8.lo;
+                        }
+                    }
                 }
             }
             if constexpr (STORE_H) {
@@ -559,7 +644,7 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
             const int64_t c0 = t0 + cidx * CH;
             // O = Q+ S + M U (skipped when o is not wanted); rows past the
             // sequence end fall outside the store range.
-            if (p.o) {
+            if (!DUAL && p.o) {
                 const auto ro = make_rsrc(p.o + ((size_t)c0 * H + h) * DK, span_bytes(n_valid(c0), 4));
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
@@ -622,6 +707,17 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     S[it][ct][1] *= sc4.y;
                     S[it][ct][2] *= sc4.z;
                     S[it][ct][3] *= sc4.w;
+                    if constexpr (DUAL) {
+                        if constexpr (!F32) {
+                            mma(S2[it][ct], aYl, bUh2[ct]);
+                            mma(S2[it][ct], aY, bUl2[ct]);
+                        }
+                        mma(S2[it][ct], aY, bUh2[ct]);
+                        S2[it][ct][0] *= sc4.x;
+                        S2[it][ct][1] *= sc4.y;
+                        S2[it][ct][2] *= sc4.z;
+                        S2[it][ct][3] *= sc4.w;
+                    }
                 }
                 if constexpr (STORE_H) {
                     if (more) {
@@ -644,6 +740,12 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     S[it][ct][1] *= n4.y;
                     S[it][ct][2] *= n4.z;
                     S[it][ct][3] *= n4.w;
+                    if constexpr (DUAL) {
+                        S2[it][ct][0] *= n4.x;
+                        S2[it][ct][1] *= n4.y;
+                        S2[it][ct][2] *= n4.z;
+                        S2[it][ct][3] *= n4.w;
+                    }
                 }
             }
             __syncthreads();
@@ -657,6 +759,16 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
                     for (int r = 0; r < 4; ++r)
                         p.S_T[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 + ct * 16 + ln] =
                             S[it][ct][r];
+        }
+        if constexpr (DUAL) {
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        p.S_T2[sbase + (size_t)(it * 16 + g * 4 + r) * DK + col0 + ct * 16 + ln] =
+                            S2[it][ct][r];
         }
     } else {
         load_beta(0, pbp);
@@ -788,6 +900,21 @@ hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, b
         else KDA_FWD(float, 16, 8);
     }
 #undef KDA_FWD
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_fwd_dual(const PrefillParams& prm, bool bf16_in, hipStream_t stream) {
+    PrefillParams p = prm;
+    p.order = nullptr;
+    p.o = nullptr;
+    p.s0_identity = 0;
+    if (p.n_slices != 1 || !p.S_T || !p.S_T2) return hipErrorInvalidValue;
+    const int64_t groups = ((int64_t)p.n_units + 7) / 8;
+    const dim3 grid((unsigned)(groups * 8)), block(64 * 8);
+    if (bf16_in)
+        hipLaunchKernelGGL((chunk_fwd_kernel<__bf16, 32, 4, false, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((chunk_fwd_kernel<float, 32, 4, false, true>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -197,6 +197,18 @@ def test_sequence_parallel_matches_oracle(T, H, B, s0, dtype):
                label=f"sequence-parallel {dtype} T={T} H={H} B={B} s0={s0}")
 
 
+@pytest.mark.parametrize("T,H,B,dtype", [(8192, 64, 1, "bf16"),    # 4 segments x 64 heads
+                                         (8192, 32, 2, "f32")])    # 2 x 4 segments x 32 heads
+def test_sequence_parallel_fused_chains_match_oracle(T, H, B, dtype):
+    """With 256 segment chains (one workgroup each) the local final states and
+    the transitions come from one launch that carries both chains over the
+    same tiles; every output element against the oracle."""
+    assert kda.chunk_fwd_workspace_bytes(B, T, H, varlen=False) == 3 * 256 * 65536
+    w, arrs = small(T, H, B, 0.02, dtype=dtype, wid=0 if dtype == "f32" else 1)
+    check_full(w, arrs, tol=TOL_F32 if dtype == "f32" else TOL_BF16,
+               label=f"sequence-parallel fused chains {dtype} T={T} H={H} B={B}")
+
+
 def test_sequence_parallel_agrees_with_sequential_and_in_place():
     w, arrs = small(6000, 3, 2, 0.02)
     d = to_dev(arrs, w)
