@@ -13,7 +13,7 @@
 #include "kda_launch.h"
 
 namespace {
-int n_launch = 0, n_merge = 0, last_slices = 0, last_units = 0;
+int n_launch = 0, n_merge = 0, n_dual = 0, last_slices = 0, last_units = 0;
 int fails = 0;
 #define CHECK(c)                                                               \
     do {                                                                       \
@@ -32,6 +32,13 @@ hipError_t launch_chunk_fwd(const PrefillParams& p, bool, int wcols, bool, hipSt
     last_units = p.n_units;
     CHECK(wcols * 4 * p.n_slices == 128);
     CHECK(p.n_units == p.n_seqs * p.H);
+    return hipSuccess;
+}
+hipError_t launch_chunk_fwd_dual(const PrefillParams& p, bool, hipStream_t) {
+    ++n_launch;
+    ++n_dual;
+    CHECK(p.n_slices == 1 && p.S_T && p.S_T2 && !p.o);
+    CHECK(p.n_units == p.n_seqs * p.H && p.n_units >= 256);
     return hipSuccess;
 }
 hipError_t launch_segment_merge(const float*, const float*, const float*, float*, float*, int32_t B,
@@ -82,14 +89,25 @@ int main() {
     // packed batch with its order workspace
     CHECK(kda_chunk_fwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(8), 32,
                         270000, 96, 128, 128, F(5), nullptr, (void*)P(9), 128, nullptr) == KDA_OK);
-    // sequence-parallel path: three prefill launches and one merge
+    // sequence-parallel path with 256 segment chains: one launch for both
+    // chains of every segment, the merge, the rerun
     {
         const size_t ws = kda_chunk_fwd_workspace_bytes(1, 1 << 20, 16, 128, 128, 0);
         CHECK(ws == (size_t)3 * 16 * 16 * 65536);
-        const int before = n_launch, mb = n_merge;
+        const int before = n_launch, mb = n_merge, db = n_dual;
         CHECK(kda_chunk_fwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, nullptr, 1, 1 << 20, 16,
                             128, 128, F(5), F(6), (void*)P(9), ws, nullptr) == KDA_OK);
-        CHECK(n_launch - before == 3 && n_merge - mb == 1);
+        CHECK(n_launch - before == 2 && n_merge - mb == 1 && n_dual - db == 1);
+    }
+    // ... and with fewer chains (two workgroups per chain): the two chains
+    // as separate launches
+    {
+        const size_t ws = kda_chunk_fwd_workspace_bytes(2, 6000, 3, 128, 128, 0);
+        CHECK(ws == (size_t)3 * 2 * 2 * 3 * 65536);
+        const int before = n_launch, mb = n_merge, db = n_dual;
+        CHECK(kda_chunk_fwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, nullptr, 2, 6000, 3,
+                            128, 128, F(5), F(6), (void*)P(9), ws, nullptr) == KDA_OK);
+        CHECK(n_launch - before == 3 && n_merge - mb == 1 && n_dual == db);
     }
     // error paths
     CHECK(kda_chunk_fwd(P(0), P(1), P(2), 9, F(3), F(4), nullptr, nullptr, 1, 8, 4, 128, 128, F(5),
