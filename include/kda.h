@@ -132,10 +132,33 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  *         16-byte aligned, overlapping no other argument (required for
  *         packed batches when that size is not 0, optional otherwise; see
  *         above); contents need no initialisation and are clobbered.
- * Numerics: fp32 accumulation throughout; with KDA_BF16 inputs the matrix
- * products run on bf16 matrix cores with split (hi + lo) bf16 operands
- * where a single rounding would exceed 2e-3 relative error; with KDA_F32
- * inputs every product runs on fp32 matrix cores.
+ * Numerics: fp32 accumulation throughout.  With KDA_F32 inputs every
+ * product runs on fp32 matrix cores.  With KDA_BF16 inputs the products run
+ * on 16-bit matrix cores, with operands whose single rounding would exceed
+ * the 2e-3 budget split into hi + lo bf16 pairs; which operands are split
+ * depends on the kernel the call selects:
+ *   - n_seqs * H >= 256 (sequence, head) pairs: one workgroup per pair, every
+ *     product on bf16 (fp32's exponent range); the state is split in
+ *     K+ S and Q+ S.
+ *   - fewer pairs: two workgroups per pair (64 value columns each); the
+ *     scaled state enters K+ S rounded once to bf16, and Q+ S runs on fp16
+ *     matrix cores with q e^{g} and the (unscaled) state rounded once to
+ *     fp16, which is more precise (11-bit significands) but has fp16's
+ *     range: every element of q and every state entry must stay below 65504
+ *     in magnitude (larger ones give inf in o), and state entries below
+ *     about 6e-5 lose relative precision in that product (fp16 subnormals),
+ *     which matters only when the whole output is that small.  q normalised
+ *     by the caller meets the first condition; for the state it means |v|
+ *     and |S0| of ordinary size (the tests cover value scales from 1e-4 to
+ *     3e4 within 2e-3).
+ *   The two plans round differently, so the same sequence can give results
+ *   that differ in the last bits depending on how many (sequence, head)
+ *   pairs share the call; both stay within 2e-3 of the exact recurrence.
+ * The chunk form carries per-channel factors of up to e^{+-80}: in a key
+ * channel whose decay sits at the bound (log_alpha = -5 for 16 tokens) the
+ * state enters the products scaled by e^{-80}, so its entries below about
+ * 1e-3 become bf16 subnormals there; the terms they feed are below 5e-6 in
+ * absolute value whatever the scale of the rest of the state.
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
                   const float* log_alpha, const float* beta, const float* S0,

@@ -117,6 +117,19 @@ def test_varlen_pipeline_lengths_mixed():
     check_full(w, arrs, cu=cu, label=f"varlen pipeline lens={lens}")
 
 
+@pytest.mark.parametrize("scale", [1e-4, 3e4])
+@pytest.mark.parametrize("H,B", [(2, 2), (96, 3)])
+def test_value_scale_edges(scale, H, B):
+    """v and S0 scaled by 1e-4 and by 3e4 (states up to about 1.4e4): with
+    fewer than 256 (sequence, head) pairs Q+ S runs on fp16 matrix cores, whose
+    range these scales approach from both sides; with 256 or more on bf16.
+    Every element against the oracle."""
+    w, arrs = small(70, H, B, 0.02)
+    arrs["v"] = W.round_bf16((arrs["v"].astype(np.float64) * scale).astype(np.float32))
+    arrs["S0"] = (arrs["S0"].astype(np.float64) * scale).astype(np.float32)
+    check_full(w, arrs, label=f"value scale {scale:g}, H={H} B={B}")
+
+
 def test_continuation_matches_single_run():
     """chunk_fwd(x[:T1]) then chunk_fwd(x[T1:], S0=S_T1) equals chunk_fwd(x)."""
     w, arrs = small(300, 2, 1, 0.02)
