@@ -68,6 +68,9 @@ def load_library():
     lib.kda_prologue.restype = ctypes.c_int
     lib.kda_epilogue.argtypes = [fp, fp, fp, i64, i32, i32, fp, vp]
     lib.kda_epilogue.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, ip, i32, i64, i32,
+                                          i32, i32, fp, fp, vp]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, ip, i32, i64, i32, i32,

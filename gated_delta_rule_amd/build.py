@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_abi.hip", "kda_prefill.hip", "kda_prefill_pipe.hip", "kda_segment.hip", "kda_recurrent.hip",
+SOURCES = ["kda_abi.hip", "kda_noalloc.hip", "kda_prefill.hip", "kda_prefill_pipe.hip", "kda_segment.hip", "kda_recurrent.hip",
            "kda_layer.hip", "kda_backward.hip"]
 HEADERS = ["kda_device.h", "kda_launch.h", "kda_chunk.h"]
 ARCH = "gfx950"

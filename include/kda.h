@@ -27,8 +27,9 @@
  *     memory accesses.
  *   - All tensor pointers are DEVICE pointers owned by the caller, which
  *     allocates every buffer (including the workspace).  The library
- *     allocates nothing, keeps no mutable global state, never synchronises
- *     the host, and enqueues its kernels on `stream` (0 = the null stream).
+ *     allocates nothing, keeps no mutable global state (apart from the
+ *     scratch array of kda_chunk_fwd_noalloc), never synchronises the host,
+ *     and enqueues its kernels on `stream` (0 = the null stream).
  *   - Every argument is validated before anything is enqueued; on error the
  *     call returns a non-zero kda_status and has no effect.  Faults raised by
  *     the device asynchronously surface at the caller's next synchronisation.
@@ -165,6 +166,27 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
                   const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
                   int32_t H, int32_t dk, int32_t dv, float* o, float* S_T,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same kernels and results.
+ * The workspace comes from a scratch array of KDA_NOALLOC_SCRATCH_BYTES in
+ * the library's device memory (one per GPU, held until the process ends;
+ * its address is looked up on a device's first call).  That size covers
+ * every case kda_chunk_fwd_workspace_bytes can report (a longest-first
+ * order of up to 4096 sequences, or the sequence-parallel path's at most
+ * 3 x 256 segment states); a larger need returns KDA_ERR_TOO_LARGE.  The call
+ * allocates nothing.  All calls on one GPU share its scratch array and it
+ * keeps the last call's contents: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (48u * 1024u * 1024u)
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, int in_dtype,
+                          const float* log_alpha, const float* beta, const float* S0,
+                          const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
+                          int32_t H, int32_t dk, int32_t dv, float* o, float* S_T,
+                          hipStream_t stream);
 
 /*
  * One decode step for B independent requests, updating their states in

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_bytes",
                             "kda_chunk_fwd", "kda_decode_step", "kda_recurrent_fwd",
                             "kda_prologue", "kda_epilogue", "kda_chunk_bwd_workspace_bytes",
-                            "kda_chunk_bwd"])
+                            "kda_chunk_bwd", "kda_chunk_fwd_noalloc"])
     for n in names:
         assert hasattr(lib, n), n
 
