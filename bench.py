@@ -11,11 +11,13 @@ D steps and reports the state GB/s (state read + write per step / step
 time).  Inputs are seeded synthetic data resident in HBM before the timed
 regions; timing uses HIP events on the stream the kernels run on.
 
-Order of the run: the informational paths first (1M-token prefill, packed
-varlen prefill, multi-token decode, layer steps, backward), then the decode
-step, then the headline prefill (W untimed launches, then K timed ones), so
-that the headline is timed on a GPU that has been working for a few seconds
-and runs at its working clocks rather than the idle ones it starts from.
+Order of the run: W + K launches of the headline prefill on the idle GPU
+(reported as its cold launch time), the informational paths (1M-token
+prefill, packed varlen prefill, multi-token decode, layer steps, backward),
+the decode step, then the headline prefill: --settle-seconds (0.3) of
+untimed launches, W warm-up launches and K timed ones.  The GPU raises its
+clocks only after tens of milliseconds of sustained load, and a serving
+deployment runs at those clocks; the cold figure is reported beside it.
 
 Prints one JSON line (rank 0) with the metric, a roofline object for the
 prefill kernel (mean, median and minimum launch times; the roofline uses the
@@ -63,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one path only (for profiler runs); prints no JSON line")
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="untimed launches of the headline kernel before its warm-up steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the repeated oracle runs")
     ap.add_argument("--no-long", action="store_true",
@@ -353,6 +357,21 @@ def main():
     def prefill():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, None, o=o, S_T=S_T)
 
+    def launch_times(n):
+        ev = []
+        for _ in range(n):
+            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e_a.record(stream)
+            prefill()
+            e_b.record(stream)
+            ev.append((e_a, e_b))
+        torch.cuda.synchronize()
+        return [x.elapsed_time(y) for x, y in ev]
+
+    # The first launches of the process, on a GPU that has been idle (for
+    # information: its clocks are still low).
+    cold_ms = launch_times(args.warmup + args.steps)
+
     if args.only is None:   # the decode step's state and per-step inputs, likewise
         wd = W.workload(4)
         Bd, Hd = wd.B, wd.H
@@ -422,6 +441,16 @@ def main():
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ prefill
+    # Clock settle: the GPU raises its clocks only after tens of milliseconds
+    # of sustained load, so the headline kernel runs untimed for
+    # --settle-seconds first; then the W warm-up launches and the K timed ones.
+    n_settle, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(10):
+            prefill()
+        torch.cuda.synchronize()
+        n_settle += 10
+    t_settle = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         prefill()
     torch.cuda.synchronize()
@@ -514,6 +543,11 @@ def main():
                      "kernel": "chunk_fwd_pipe_kernel", "kernel_ms": pf_kernel_ms,
                      "kernel_ms_median": float(np.median(launch_ms)),
                      "kernel_ms_min": float(np.min(launch_ms)),
+                     "kernel_ms_cold_median": float(np.median(cold_ms[args.warmup:] or cold_ms)),
+                     "clock_settle": {"seconds": t_settle, "launches": n_settle,
+                                      "note": "untimed launches of the same kernel before the W "
+                                              "warm-up steps; kernel_ms_cold_median is the first "
+                                              "launches of the process on an idle GPU"},
                      "algorithmic_bytes": pf_bytes, "algorithmic_flops": pf_flops,
                      "mfma_tflops_algorithmic": pf_tflops,
                      "mfma_frac_algorithmic": pf_tflops / PEAK_BF16_TFLOPS,
