@@ -15,6 +15,17 @@ is the profiled program: it prepares the resident inputs of one workload
 and launches its kernel a few times.  The orchestrating process never
 touches the GPU itself.
 
+    python -m gated_delta_rule_amd.traffic phases [--out DIR]
+
+builds the contraction-phase probe (csrc/kda_phase_probe.hip, into its own
+libkda_probe.so), times it with HIP events and runs one rocprofv3 pass per
+matrix-core counter over it, and writes
+`profiles/contraction_phases_probe.json`: for the K+ S / Q+ S phase, the
+state-update phase and both, the matrix-core flops per launch, the rate
+against the 2.5 PFLOP/s 16-bit peak and the busy fraction of the matrix cores
+(SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), with
+one wave per SIMD and nothing else on the compute units.
+
     python -m gated_delta_rule_amd.traffic mfma [--out DIR]
 
 runs one rocprofv3 pass per matrix-core counter (MFMA operations per data
@@ -51,6 +62,137 @@ TARGETS = {
     "decode": ("recurrent_kernel", "decode_step_workload4",
                ("kda_recurrent.hip", "kda_device.h", "kda_launch.h", "kda_abi.hip")),
 }
+
+
+PROBE_SRC = "kda_phase_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libkda_probe.so")
+PROBE_MODES = {0: "K+S/Q+S", 1: "state update", 2: "K+S/Q+S then state update"}
+PROBE_WG, PROBE_ITERS, PROBE_LAUNCHES = 256, 2048, 6
+PEAK_16BIT_TFLOPS = 2500.0
+
+
+def build_probe(verbose=False):
+    """Compile the contraction-phase probe into libkda_probe.so (hipcc, gfx950)."""
+    from gated_delta_rule_amd import build as B
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [B.hipcc(), *B.FLAGS, f"-I{os.path.join(ROOT, 'include')}", "-o", tmp,
+           os.path.join(CSRC, PROBE_SRC)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
+def run_probe_target():
+    """The profiled program of `phases`: PROBE_LAUNCHES launches of each mode
+    (the first untimed), timed with HIP events; prints one JSON line."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.kda_probe_contraction.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.kda_probe_contraction.restype = ctypes.c_int
+    lib.kda_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.kda_probe_flops.restype = ctypes.c_double
+    dev = torch.device("cuda:0")
+    out = torch.empty(PROBE_WG * 256 * 48, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for mode in PROBE_MODES:
+        def launch():
+            rc = lib.kda_probe_contraction(ctypes.c_void_p(out.data_ptr()), PROBE_WG, PROBE_ITERS, mode,
+                                           ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: {rc}")
+        launch()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(PROBE_LAUNCHES - 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        flops = lib.kda_probe_flops(PROBE_WG, PROBE_ITERS, mode)
+        med = ms[len(ms) // 2]
+        res[mode] = {"ms_median": med, "flops_per_launch": flops,
+                     "tflops": flops / (med * 1e-3) / 1e12}
+    print("PROBE " + json.dumps(res), flush=True)
+
+
+def probe_hash():
+    h = hashlib.sha256()
+    for name in (PROBE_SRC, "kda_chunk.h", "kda_device.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def collect_phases(out, profiles_dir, run=True):
+    os.makedirs(out, exist_ok=True)
+    os.makedirs(profiles_dir, exist_ok=True)
+    if run:
+        build_probe(verbose=True)
+    env = dict(os.environ, TMPDIR="/tmp", PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    if run:
+        r = subprocess.run(["timeout", "-s", "KILL", "120", sys.executable, "-u", "-m",
+                            "gated_delta_rule_amd.traffic", "target", "probe"],
+                           cwd="/tmp", env=env, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise SystemExit(f"probe timing run failed ({r.returncode}): {r.stderr[-2000:]}")
+        timing = None
+        for line in r.stdout.splitlines():
+            if line.startswith("PROBE "):
+                timing = json.loads(line[6:])
+        with open(os.path.join(out, "probe_timing.json"), "w") as f:
+            json.dump(timing, f)
+    with open(os.path.join(out, "probe_timing.json")) as f:
+        timing = json.load(f)
+    counters = {}
+    for counter in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                    "SQ_INSTS_VALU_MFMA_MOPS_F16"):
+        per = counter_pass("probe", counter, out, run)
+        disp = sorted((int(k[0]), v) for k, v in per.items() if "contraction_probe" in k[1])
+        if len(disp) != PROBE_LAUNCHES * len(PROBE_MODES):
+            raise SystemExit(f"{counter}: {len(disp)} probe dispatches, expected "
+                             f"{PROBE_LAUNCHES * len(PROBE_MODES)}")
+        for i, mode in enumerate(PROBE_MODES):
+            vals = [v for _, v in disp[i * PROBE_LAUNCHES + 1:(i + 1) * PROBE_LAUNCHES]]
+            counters.setdefault(str(mode), {})[counter] = sum(vals) / len(vals)
+    modes = {}
+    for mode, name in PROBE_MODES.items():
+        c = counters[str(mode)]
+        t = timing[str(mode)]
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        hw = (c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + c["SQ_INSTS_VALU_MFMA_MOPS_F16"]) * MOPS_FLOPS
+        modes[name] = {"counters_per_launch": c, "ms_median": t["ms_median"],
+                       "flops_per_launch_instruction_mix": t["flops_per_launch"],
+                       "flops_per_launch_counters": hw,
+                       "tflops": t["tflops"], "frac_of_16bit_peak": t["tflops"] / PEAK_16BIT_TFLOPS,
+                       "mfma_busy_frac": busy}
+        print(f"{name}: {t['tflops']:.0f} TFLOP/s = {t['tflops'] / PEAK_16BIT_TFLOPS:.3f} of peak, "
+              f"matrix cores busy {busy:.3f}", flush=True)
+    doc = {
+        "probe": "csrc/kda_phase_probe.hip: the prefill consumer's K+S/Q+S and state-update instruction "
+                 "sequences on LDS-resident operands, one wave per SIMD, 256 workgroups x "
+                 f"{PROBE_ITERS} iterations, nothing else on the compute units",
+        "command": "python -m gated_delta_rule_amd.traffic phases (timing: python -u -m "
+                   "gated_delta_rule_amd.traffic target probe; per counter: rocprofv3 --pmc <counter> -d "
+                   "<dir> -o run --output-format csv -- python -u -m gated_delta_rule_amd.traffic target probe)",
+        "peak_tflops_16bit": PEAK_16BIT_TFLOPS,
+        "modes": modes,
+        "probe_source_sha256_16": probe_hash(),
+    }
+    path = os.path.join(profiles_dir, "contraction_phases_probe.json")
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    print(f"contraction phases -> {path}", flush=True)
 
 
 def sources_hash(kind):
@@ -121,6 +263,9 @@ def measured(kind):
 
 # ------------------------------------------------------------------ targets
 def run_target(kind):
+    if kind == "probe":
+        run_probe_target()
+        return
     import torch
     import gated_delta_rule_amd as kda
     from gated_delta_rule_amd import workloads as W
@@ -272,7 +417,7 @@ def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("target")
-    t.add_argument("kind", choices=["copy", "prefill", "decode"])
+    t.add_argument("kind", choices=["copy", "prefill", "decode", "probe"])
     c = sub.add_parser("collect")
     c.add_argument("--out", default=os.path.join(ROOT, "counters_out", "traffic"),
                    help="directory for the raw counter output")
@@ -283,7 +428,14 @@ def main():
     m.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     m.add_argument("--parse-only", action="store_true",
                    help="summarise the counter output already under --out")
+    ph = sub.add_parser("phases")
+    ph.add_argument("--out", default=os.path.join(ROOT, "counters_out", "phases"))
+    ph.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
+    ph.add_argument("--parse-only", action="store_true")
     args = ap.parse_args()
+    if args.cmd == "phases":
+        collect_phases(os.path.abspath(args.out), os.path.abspath(args.profiles_dir), not args.parse_only)
+        return
     if args.cmd == "target":
         run_target(args.kind)
     elif args.cmd == "mfma":
