@@ -22,17 +22,21 @@ libkda_probe.so), times it with HIP events and runs one rocprofv3 pass per
 matrix-core counter over it, and writes
 `profiles/contraction_phases_probe.json`: for the K+ S / Q+ S phase, the
 state-update phase and both, the matrix-core flops per launch, the rate
-against the 2.5 PFLOP/s 16-bit peak and the busy fraction of the matrix cores
-(SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), with
-one wave per SIMD and nothing else on the compute units.
+against the 2.5 PFLOP/s 16-bit peak, the busy fraction of the matrix cores
+(SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) and the
+share of LDS active cycles lost to bank conflicts (SQ_LDS_BANK_CONFLICT over
+SQ_LDS_IDX_ACTIVE), with one wave per SIMD and nothing else on the compute
+units.
 
     python -m gated_delta_rule_amd.traffic mfma [--out DIR]
 
-runs one rocprofv3 pass per matrix-core counter (MFMA operations per data
-type, MFMA busy cycles, SQ busy cycles, GPU active cycles) over the prefill
-target and writes `profiles/chunk_fwd_workload1_mfma.json`: the counters per
-launch, the hardware flops they imply (each MOPS count stands for 512 flops)
-and the flops the kernel's instruction mix implies (`prefill_mfma_flops`).
+runs one rocprofv3 pass per counter (MFMA operations per data type, MFMA
+busy cycles, SQ busy cycles, GPU active cycles, VALU / MFMA / LDS
+instructions issued, LDS bank-conflict and LDS active cycles) over the
+prefill target and writes `profiles/chunk_fwd_workload1_mfma.json`: the
+counters per launch, the hardware flops they imply (each MOPS count stands
+for 512 flops) and the flops the kernel's instruction mix implies
+(`prefill_mfma_flops`).
 
 The JSON records a hash of the kernel's sources; the benchmark reports the
 counters only while that hash matches the sources it runs.
@@ -155,7 +159,7 @@ def collect_phases(out, profiles_dir, run=True):
         timing = json.load(f)
     counters = {}
     for counter in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-                    "SQ_INSTS_VALU_MFMA_MOPS_F16"):
+                    "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"):
         per = counter_pass("probe", counter, out, run)
         disp = sorted((int(k[0]), v) for k, v in per.items() if "contraction_probe" in k[1])
         if len(disp) != PROBE_LAUNCHES * len(PROBE_MODES):
@@ -174,9 +178,11 @@ def collect_phases(out, profiles_dir, run=True):
                        "flops_per_launch_instruction_mix": t["flops_per_launch"],
                        "flops_per_launch_counters": hw,
                        "tflops": t["tflops"], "frac_of_16bit_peak": t["tflops"] / PEAK_16BIT_TFLOPS,
-                       "mfma_busy_frac": busy}
+                       "mfma_busy_frac": busy,
+                       "lds_bank_conflict_frac": c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]}
         print(f"{name}: {t['tflops']:.0f} TFLOP/s = {t['tflops'] / PEAK_16BIT_TFLOPS:.3f} of peak, "
-              f"matrix cores busy {busy:.3f}", flush=True)
+              f"matrix cores busy {busy:.3f}, LDS bank conflicts "
+              f"{modes[name]['lds_bank_conflict_frac']:.3f} of LDS active cycles", flush=True)
     doc = {
         "probe": "csrc/kda_phase_probe.hip: the prefill consumer's K+S/Q+S and state-update instruction "
                  "sequences on LDS-resident operands, one wave per SIMD, 256 workgroups x "
@@ -209,7 +215,8 @@ def profile_path(kind, profiles_dir=None):
 
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
                  "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
-                 "GRBM_GUI_ACTIVE")
+                 "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")
 MOPS_FLOPS = 512              # flops per count of an SQ_INSTS_VALU_MFMA_MOPS_* counter
 
 
@@ -404,6 +411,8 @@ def collect_mfma(out, profiles_dir, run=True):
         "counters": rec,
         "hw_flops_per_launch_from_counters": hw,
         "hw_flops_per_launch_from_instruction_mix": prefill_mfma_flops(),
+        "lds_bank_conflict_frac": rec["SQ_LDS_BANK_CONFLICT"]["per_dispatch"]
+        / rec["SQ_LDS_IDX_ACTIVE"]["per_dispatch"],
         "kernel_sources_sha256_16": sources_hash("prefill"),
     }
     path = mfma_profile_path(profiles_dir)
