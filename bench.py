@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+KDA_BWD_WINDOW = 2048           # the backward's default window (include/kda.h)
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix
 PEAK_F32_TFLOPS = 157.3         # MI355X dense fp32 matrix
 N_XCD = 8                       # MI355X accelerator complex dies
@@ -232,29 +233,42 @@ def backward_step(torch, kda, W, dev, reps=5):
     beta = torch.sigmoid(torch.randn((1, T, H), device=dev, generator=g))
     go = torch.randn(shp, device=dev, generator=g)
     gst = torch.randn((1, H, 128, 128), device=dev, generator=g)
-    ws = torch.empty(kda.load_library().kda_chunk_bwd_workspace_bytes(1, T, H, 128, 128, 0),
-                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    kda.chunk_bwd(q, k, v, la, beta, None, go, gst, workspace=ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
+
+    def timed(ws):
         kda.chunk_bwd(q, k, v, la, beta, None, go, gst, workspace=ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            kda.chunk_bwd(q, k, v, la, beta, None, go, gst, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    # the default workspace (2048-token windows), then one window per sequence
+    ws_default = kda.chunk_bwd_workspace_bytes(1, T, H)
+    ws_one = kda.chunk_bwd_workspace_bytes(1, T, H, window_tokens=T)
+    ws = torch.empty(ws_default, dtype=torch.uint8, device=dev)
+    ms = timed(ws)
+    del ws
+    ws = torch.empty(ws_one, dtype=torch.uint8, device=dev)
+    ms_one = timed(ws)
     flops = BWD_FLOPS_PER_TOKEN_HEAD * T * H
     del q, k, v, la, beta, go, gst, ws
     torch.cuda.empty_cache()
     return {"workload": f"KDA backward B=1 T={T} H={H} d=128, bf16 q/k/v, fp32 gates, "
                         "dL/do and dL/dS_T ~ N(0,1) (device-drawn)",
             "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+            "workspace_bytes": ws_default,
             "algorithmic_flops": flops, "tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
             "mfma_f32_peak_tflops": PEAK_F32_TFLOPS,
             "frac_f32_peak": flops / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
+            "single_window": {"ms": ms_one, "workspace_bytes": ws_one},
             "passes": "forward keeping chunk states, V - K+S and U; chunk matrices; "
-                      "reverse state-gradient walk; per-chunk gradients"}
+                      "reverse state-gradient walk; per-chunk gradients; equal lengths run in "
+                      f"windows of {KDA_BWD_WINDOW} tokens, last first (the states at window starts "
+                      "from a forward pass without per-chunk outputs)"}
 
 
 def varlen_prefill(torch, kda, W, dev, reps=3):

@@ -73,6 +73,8 @@ def load_library():
     lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.c_int]
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd_workspace_bytes_window.argtypes = [i32, i64, i32, i32, i32, i64]
+    lib.kda_chunk_bwd_workspace_bytes_window.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp, vp, vp, ctypes.c_int, fp, fp, fp, ip, i32, i64, i32, i32,
                                   i32, fp, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
     lib.kda_chunk_bwd.restype = ctypes.c_int
@@ -182,14 +184,27 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
     return o, S_T
 
 
+def chunk_bwd_workspace_bytes(n_seqs, T, H, varlen=False, window_tokens=None):
+    """kda_chunk_bwd_workspace_bytes, or with window_tokens (equal lengths)
+    kda_chunk_bwd_workspace_bytes_window."""
+    lib = load_library()
+    if window_tokens is None:
+        return int(lib.kda_chunk_bwd_workspace_bytes(n_seqs, T, H, 128, 128, int(varlen)))
+    if varlen:
+        raise KDAError("window_tokens applies to equal-length batches only")
+    return int(lib.kda_chunk_bwd_workspace_bytes_window(n_seqs, T, H, 128, 128, int(window_tokens)))
+
+
 def chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T=None, cu_seqlens=None, *,
-              want_grad_S0: bool = True, workspace=None):
+              want_grad_S0: bool = True, workspace=None, window_tokens=None):
     """Backward pass of chunk_fwd (see kda_chunk_bwd in include/kda.h).
 
     Inputs as for chunk_fwd; grad_o float32 like o; grad_S_T [N, H, 128, 128]
     float32 or None (zero).  Returns (grad_q, grad_k, grad_v, grad_log_alpha,
     grad_beta, grad_S0), all float32 with the shapes of q, k, v, log_alpha,
     beta and S0 ([N, H, 128, 128], or None when want_grad_S0 is False).
+    window_tokens (equal lengths, no workspace given): size the workspace for
+    that window length instead of the default one.
     """
     import torch
     lib = load_library()
@@ -226,8 +241,12 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, grad_o, grad_S_T=None, cu_seqlens=No
     gv, gla = torch.empty(v.shape, **f32), torch.empty(q.shape, **f32)
     gb = torch.empty(beta.shape, **f32)
     gS0 = torch.empty(st_shape, **f32) if want_grad_S0 else None
-    ws_bytes = int(lib.kda_chunk_bwd_workspace_bytes(n_seqs, T, H, dk, dv,
-                                                     int(cu_seqlens is not None)))
+    if window_tokens is not None and cu_seqlens is None:
+        ws_bytes = int(lib.kda_chunk_bwd_workspace_bytes_window(n_seqs, T, H, dk, dv,
+                                                                int(window_tokens)))
+    else:
+        ws_bytes = int(lib.kda_chunk_bwd_workspace_bytes(n_seqs, T, H, dk, dv,
+                                                         int(cu_seqlens is not None)))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream

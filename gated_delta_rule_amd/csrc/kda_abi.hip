@@ -187,9 +187,10 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     const int64_t grid = ((units + 7) / 8) * 8 * n_slices;
     if (grid > kMaxGrid) return KDA_ERR_TOO_LARGE;
 
-    kda::PrefillParams p;
+    kda::PrefillParams p{};
     p.seg_len = T;
     p.seg_per_seq = 1;
+    p.seg_sel = -1;
     p.s0_identity = 0;
     p.h_states = nullptr;
     p.r_out = nullptr;
@@ -430,15 +431,25 @@ int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, i
 // Backward workspace layout (floats): states at chunk starts and gradients
 // at chunk ends [slots, H, 128, 128] each, the chunk matrices of the first
 // backward pass [slots, H, kBwdChunkElems], and W, V - K+ S and U of every
-// token [tokens, H, 128] each; slots = tokens / 32 + n_seqs.
+// token [rows, H, 128] each.  Packed batches: slots = tokens / 32 + n_seqs,
+// rows = tokens.  Equal lengths run in windows of W chunks (the last window
+// first): slots = n_seqs * W, rows = n_seqs * 32 W, plus the state at the
+// start of every window after the first and one state gradient per
+// (sequence, head) carried from window to window.
 struct BwdLayout {
-    int64_t slots, h, dsn, tmp, w, r, u, total;   // offsets and total in floats
+    int64_t slots, rows, n_win, win_chunks;
+    int64_t h, dsn, tmp, w, r, u, ckpt, carry, total;   // offsets and total in floats
 };
-static bool bwd_layout(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayout* L) {
-    L->slots = tokens / kChunk + n_seqs;
-    int64_t sh = 0, st = 0, tmp = 0, wv = 0;
-    if (!mul_ok(L->slots, H, &sh) || !mul_ok(sh, kHeadDim * kHeadDim, &st) ||
-        !mul_ok(sh, kBwdChunkElems, &tmp) || !mul_ok(tokens, H * kHeadDim, &wv))
+static bool bwd_layout(int64_t n_seqs, int64_t slots, int64_t rows, int64_t n_win, int64_t H,
+                       BwdLayout* L) {
+    L->slots = slots;
+    L->rows = rows;
+    L->n_win = n_win;
+    int64_t sh = 0, st = 0, tmp = 0, wv = 0, units = 0, ust = 0, ck = 0;
+    if (!mul_ok(slots, H, &sh) || !mul_ok(sh, kHeadDim * kHeadDim, &st) ||
+        !mul_ok(sh, kBwdChunkElems, &tmp) || !mul_ok(rows, H * kHeadDim, &wv) ||
+        !mul_ok(n_seqs, H, &units) || !mul_ok(units, kHeadDim * kHeadDim, &ust) ||
+        !mul_ok(ust, n_win - 1, &ck))
         return false;
     L->h = 0;
     L->dsn = st;
@@ -446,18 +457,68 @@ static bool bwd_layout(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayout* L) 
     L->w = 2 * st + tmp;
     L->r = L->w + wv;
     L->u = L->r + wv;
-    L->total = 2 * st + tmp + 3 * wv;
-    return L->total >= 0 && L->total <= INT64_MAX / 8;
+    L->ckpt = L->u + wv;
+    L->carry = L->ckpt + ck;
+    L->total = L->carry + (n_win > 1 ? ust : 0);
+    return st <= INT64_MAX / 16 && tmp <= INT64_MAX / 16 && wv <= INT64_MAX / 16 &&
+           ck <= INT64_MAX / 16 && L->total >= 0 && L->total <= INT64_MAX / 8;
+}
+static bool bwd_layout_packed(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayout* L) {
+    L->win_chunks = 0;
+    return bwd_layout(n_seqs, tokens / kChunk + n_seqs, tokens, 1, H, L);
+}
+// Equal lengths with windows of W chunks (W >= 1; W >= the chunks of a
+// sequence: one window).
+static bool bwd_layout_windowed(int64_t n_seqs, int64_t T, int64_t H, int64_t W, BwdLayout* L) {
+    const int64_t C = (T + kChunk - 1) / kChunk;
+    if (W < 1) return false;
+    if (W > C) W = C < 1 ? 1 : C;
+    const int64_t n_win = C == 0 ? 1 : (C + W - 1) / W;
+    int64_t slots = 0, rows = 0;
+    if (!mul_ok(n_seqs, W, &slots) || !mul_ok(slots, kChunk, &rows)) return false;
+    L->win_chunks = W;
+    return bwd_layout(n_seqs, slots, rows, n_win, H, L);
+}
+// The window the backward uses for a workspace of `bytes`: one window if it
+// fits, else the longest power-of-two number of chunks that fits.
+static bool bwd_pick_window(int64_t n_seqs, int64_t T, int64_t H, size_t bytes, BwdLayout* L) {
+    const int64_t C = (T + kChunk - 1) / kChunk;
+    if (bwd_layout_windowed(n_seqs, T, H, C < 1 ? 1 : C, L) && (size_t)L->total * 4 <= bytes)
+        return true;
+    int64_t W = 1;
+    while (W * 2 < C) W *= 2;
+    for (; W >= 1; W /= 2)
+        if (bwd_layout_windowed(n_seqs, T, H, W, L) && (size_t)L->total * 4 <= bytes) return true;
+    return false;
+}
+static int64_t bwd_round_window(int64_t T, int64_t window_tokens) {
+    const int64_t C = (T + kChunk - 1) / kChunk;
+    const int64_t want = (window_tokens + kChunk - 1) / kChunk;
+    if (want >= C) return C < 1 ? 1 : C;
+    int64_t W = 1;
+    while (W < want) W *= 2;
+    return W >= C ? (C < 1 ? 1 : C) : W;
+}
+
+size_t kda_chunk_bwd_workspace_bytes_window(int32_t n_seqs, int64_t T, int32_t H, int32_t dk,
+                                            int32_t dv, int64_t window_tokens) {
+    if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim || H < 1 || T < 0 || window_tokens < 1)
+        return 0;
+    if (H > KDA_MAX_HEADS) return 0;
+    int64_t tokens = 0;
+    if (!mul_ok((int64_t)n_seqs, T, &tokens)) return 0;
+    BwdLayout L;
+    if (!bwd_layout_windowed(n_seqs, T, H, bwd_round_window(T, window_tokens), &L)) return 0;
+    return (size_t)L.total * 4;
 }
 
 size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H, int32_t dk, int32_t dv,
                                      int varlen) {
     if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim || H < 1 || T < 0) return 0;
     if (H > KDA_MAX_HEADS) return 0;
-    int64_t tokens = T;
-    if (!varlen && !mul_ok((int64_t)n_seqs, T, &tokens)) return 0;
+    if (!varlen) return kda_chunk_bwd_workspace_bytes_window(n_seqs, T, H, dk, dv, KDA_BWD_WINDOW);
     BwdLayout L;
-    if (!bwd_layout(n_seqs, tokens, H, &L)) return 0;
+    if (!bwd_layout_packed(n_seqs, T, H, &L)) return 0;
     return (size_t)L.total * 4;
 }
 
@@ -481,16 +542,21 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
         elems > INT64_MAX / 8 || !mul_ok((int64_t)n_seqs, (int64_t)H, &units) ||
         !mul_ok(units, kHeadDim * kHeadDim, &st_elems))
         return KDA_ERR_TOO_LARGE;
+    // The largest layout (packed, or one window per sequence) bounds the
+    // grids of every layout this call can pick.
     BwdLayout L;
-    if (!bwd_layout(n_seqs, tokens, H, &L)) return KDA_ERR_TOO_LARGE;
-    const int64_t chunks = L.slots * H;
-    if (units > INT32_MAX / 32 || chunks > INT32_MAX) return KDA_ERR_TOO_LARGE;
+    const bool sizes_ok = varlen ? bwd_layout_packed(n_seqs, tokens, H, &L)
+                                 : bwd_layout_windowed(n_seqs, T, H, (T + kChunk - 1) / kChunk + 1, &L);
+    if (!sizes_ok) return KDA_ERR_TOO_LARGE;
+    if (units > INT32_MAX / 32 || L.slots * H > INT32_MAX) return KDA_ERR_TOO_LARGE;
 
     if (tokens > 0 && (!q || !k || !v || !log_alpha || !beta || !grad_o || !grad_q || !grad_k ||
                        !grad_v || !grad_log_alpha || !grad_beta))
         return KDA_ERR_NULL_POINTER;
     if (!workspace) return KDA_ERR_WORKSPACE;
-    if ((size_t)L.total * 4 > workspace_bytes) return KDA_ERR_WORKSPACE;
+    if (varlen ? (size_t)L.total * 4 > workspace_bytes
+               : !bwd_pick_window(n_seqs, T, H, workspace_bytes, &L))
+        return KDA_ERR_WORKSPACE;
     if (tokens > 0) {
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) ||
             !aligned(grad_o, 16) || !aligned(grad_q, 16) || !aligned(grad_k, 16) ||
@@ -528,11 +594,11 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     }
 
     float* ws = (float*)workspace;
-    // 1. forward pass storing the state at every chunk start
+    const bool bf16_in = in_dtype == KDA_BF16;
     const int n_slices = units < 256 ? 2 : 1;
     const int wcols = 128 / (4 * n_slices);
     if (((units + 7) / 8) * 8 * n_slices > kMaxGrid) return KDA_ERR_TOO_LARGE;
-    kda::PrefillParams p;
+    kda::PrefillParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -546,20 +612,17 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     p.T = T;
     p.seg_len = T;
     p.seg_per_seq = 1;
+    p.seg_sel = -1;
     p.s0_identity = 0;
     p.n_seqs = n_seqs;
     p.H = H;
     p.n_slices = n_slices;
     p.n_units = (int32_t)units;
-    p.h_states = ws + L.h;
-    p.r_out = ws + L.r;
-    p.u_out = ws + L.u;
+    p.h_states = nullptr;
+    p.r_out = nullptr;
+    p.u_out = nullptr;
     p.S_T2 = nullptr;
-    const bool bf16_in = in_dtype == KDA_BF16;
-    hipError_t e = kda::launch_chunk_fwd(p, bf16_in, wcols, false, stream);
-    if (e != hipSuccess) return KDA_ERR_HIP;
-    // 2. chunk matrices, reverse state-gradient scan, chunk gradients
-    kda::BwdParams b;
+    kda::BwdParams b{};
     b.q = q;
     b.k = k;
     b.v = v;
@@ -582,10 +645,54 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     b.w = ws + L.w;
     b.T = T;
     b.slots = L.slots;
+    b.win_len = 0;
+    b.win_idx = 0;
     b.n_seqs = n_seqs;
     b.H = H;
-    e = kda::launch_chunk_bwd(b, bf16_in, stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (varlen) {
+        // 1. forward pass storing the state at every chunk start, V - K+ S
+        //    and U; 2. chunk matrices, reverse state-gradient walk, chunk
+        //    gradients
+        p.h_states = ws + L.h;
+        p.r_out = ws + L.r;
+        p.u_out = ws + L.u;
+        if (kda::launch_chunk_fwd(p, bf16_in, wcols, false, stream) != hipSuccess) return KDA_ERR_HIP;
+        return kda::launch_chunk_bwd(b, bf16_in, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    // Equal lengths, windows of W chunks.  The states at the window starts
+    // come first (forward passes without per-chunk outputs, window by
+    // window); then, from the last window to the first, the forward pass
+    // over the window keeping its per-chunk values and the three backward
+    // passes, with dL/dS carried from each window to the one before it.
+    const int64_t win_len = L.win_chunks * kChunk;
+    const int64_t st_el = units * kHeadDim * kHeadDim;
+    const int nw = (int)L.n_win;
+    auto ckpt = [&](int w) -> float* { return w == 0 ? nullptr : ws + L.ckpt + (int64_t)(w - 1) * st_el; };
+    p.seg_len = win_len;
+    for (int w = 0; w + 1 < nw; ++w) {
+        kda::PrefillParams pw = p;
+        pw.seg_sel = w;
+        pw.S0 = w == 0 ? S0 : ckpt(w);
+        pw.S_T = ckpt(w + 1);
+        if (kda::launch_chunk_fwd(pw, bf16_in, wcols, false, stream) != hipSuccess) return KDA_ERR_HIP;
+    }
+    float* carry = nw > 1 ? ws + L.carry : nullptr;
+    b.win_len = win_len;
+    for (int w = nw - 1; w >= 0; --w) {
+        kda::PrefillParams pw = p;
+        pw.seg_sel = w;
+        pw.S0 = w == 0 ? S0 : ckpt(w);
+        pw.h_states = ws + L.h;
+        pw.r_out = ws + L.r;
+        pw.u_out = ws + L.u;
+        if (kda::launch_chunk_fwd(pw, bf16_in, wcols, false, stream) != hipSuccess) return KDA_ERR_HIP;
+        kda::BwdParams bw = b;
+        bw.win_idx = w;
+        bw.dS_T = w == nw - 1 ? grad_S_T : carry;
+        bw.dS0 = w == 0 ? grad_S0 : carry;
+        if (kda::launch_chunk_bwd(bw, bf16_in, stream) != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
 }
 
 }  // extern "C"

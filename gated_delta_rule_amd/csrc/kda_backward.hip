@@ -131,34 +131,66 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ int crow(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 
-// First token of sequence n (clamped into [0, T] like the forward).
+// First token of sequence n (clamped into [0, T] like the forward), or of
+// its window in window mode.
 __device__ __forceinline__ int64_t seq_start(const BwdParams& p, int n) {
+    if (p.win_len > 0) {
+        const int64_t s = (int64_t)n * p.T + (int64_t)p.win_idx * p.win_len, e = (int64_t)(n + 1) * p.T;
+        return s < e ? s : e;
+    }
     if (!p.cu) return (int64_t)n * p.T;
     const int64_t a = p.cu[n];
     return a < 0 ? 0 : (a > p.T ? p.T : a);
 }
 __device__ __forceinline__ int64_t seq_end(const BwdParams& p, int n, int64_t start) {
+    if (p.win_len > 0) {
+        const int64_t e = (int64_t)(n + 1) * p.T;
+        return e - start > p.win_len ? start + p.win_len : e;
+    }
     if (!p.cu) return (int64_t)(n + 1) * p.T;
     const int64_t b = p.cu[n + 1];
     return b < start ? start : (b > p.T ? p.T : b);
 }
+// First slot of sequence n and the offset added to its token rows in w, r, u
+// (window mode: the compact layout, slot n * win_len / 32 + j and row
+// n * win_len + (t - start); otherwise slot start / 32 + n + j and row t).
+__device__ __forceinline__ int64_t slot_base(const BwdParams& p, int n, int64_t start) {
+    return p.win_len > 0 ? (int64_t)n * (p.win_len / BC) : start / BC + n;
+}
+__device__ __forceinline__ int64_t row_shift(const BwdParams& p, int n, int64_t start) {
+    return p.win_len > 0 ? (int64_t)n * p.win_len - start : 0;
+}
 
 // Chunk held by slot m: chunk j of sequence n uses slot start_n / 32 + n + j
-// (strictly increasing in n, so a binary search finds n).  nv = 0: no chunk.
+// (strictly increasing in n, so a binary search finds n), or n * W + j in
+// window mode (W = win_len / 32).  nv = 0: no chunk.  rs: row_shift of n.
 struct Chunk {
     int64_t c0;
+    int64_t rs;
     int nv;
 };
 __device__ Chunk slot_chunk(const BwdParams& p, int64_t m) {
-    int lo = 0, hi = p.n_seqs;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (seq_start(p, mid) / BC + mid <= m) lo = mid;
-        else hi = mid;
+    int n;
+    int64_t j;
+    if (p.win_len > 0) {
+        const int64_t W = p.win_len / BC;
+        n = (int)(m / W);
+        j = m - (int64_t)n * W;
+    } else {
+        int lo = 0, hi = p.n_seqs;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (seq_start(p, mid) / BC + mid <= m) lo = mid;
+            else hi = mid;
+        }
+        n = lo;
+        j = m - (seq_start(p, lo) / BC + lo);
     }
-    const int64_t s = seq_start(p, lo), e = seq_end(p, lo, s);
-    const int64_t j = m - (s / BC + lo);
-    Chunk c{s + j * BC, 0};
+    Chunk c{0, 0, 0};
+    if (n >= p.n_seqs) return c;
+    const int64_t s = seq_start(p, n), e = seq_end(p, n, s);
+    c.c0 = s + j * BC;
+    c.rs = row_shift(p, n, s);
     if (j >= 0 && c.c0 < e) c.nv = (int)(e - c.c0 < BC ? e - c.c0 : BC);
     return c;
 }
@@ -318,7 +350,8 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
     const int H = p.H;
     const int64_t t0 = seq_start(p, n), t1 = seq_end(p, n, t0);
     const int64_t nch = (t1 - t0 + BC - 1) / BC;
-    const int64_t slot0 = t0 / BC + n;
+    const int64_t slot0 = slot_base(p, n, t0);
+    const int64_t wrs = row_shift(p, n, t0);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -444,7 +477,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
             for (int r = 0; r < 16; ++r) {
                 const int t = crow(r, lane);
                 sW[sw][t * LC + i0] = W[r];
-                if (t < nv) p.w[((size_t)(c0 + t) * H + h) * BD + col] = W[r];
+                if (t < nv) p.w[((size_t)(c0 + wrs + t) * H + h) * BD + col] = W[r];
             }
             if (j > 0) load_t(j - 1);
         }
@@ -512,9 +545,10 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
     auto f4 = [](const float4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; };
     // token-major tiles of this chunk (rows past the sequence end read 0)
     const auto rdo = make_rsrc(p.dO + e0i, span);
-    const auto rw = make_rsrc(p.w + e0i, span);
-    const auto ru = make_rsrc(p.u + e0i, span);
-    const auto rr = make_rsrc(p.r + e0i, span);
+    const int64_t e0s = ((c0 + ch.rs) * H + h) * BD;   // same rows in w, u, r
+    const auto rw = make_rsrc(p.w + e0s, span);
+    const auto ru = make_rsrc(p.u + e0s, span);
+    const auto rr = make_rsrc(p.r + e0s, span);
     const auto rla = make_rsrc(p.la + e0i, span);
     const auto rk = make_rsrc((const InT*)p.k + e0i, span / (4 / ES));
     const auto rq = make_rsrc((const InT*)p.q + e0i, span / (4 / ES));

@@ -23,13 +23,20 @@ struct PrefillParams {
     // numbered b * seg_per_seq + r.  seg_per_seq = 1, seg_len = T: no split.
     int64_t seg_len;
     int32_t seg_per_seq;
+    // Window mode (equal lengths, backward pass): seg_sel >= 0 runs only
+    // segment seg_sel of each of the n_seqs sequences (chain n = sequence n),
+    // and h_states / r_out / u_out use the window's compact layout: chunk j
+    // of the window in slot n * (seg_len / 32) + j, token t of the window in
+    // row n * seg_len + (t - window start).  -1 otherwise.
+    int32_t seg_sel;
     // Transition pass: every chain starts from the identity state and reads
     // v as zero, so its final state is the chain's linear map S_in -> S_out.
     int32_t s0_identity;
     int32_t n_seqs, H, n_slices, n_units;   // n_seqs counts chains (segments)
     // Optional [slots, H, 128, 128]: the state at the start of every chunk
-    // (unsplit sequences only); chunk j of sequence n starting at token t0
-    // goes to slot t0 / 32 + n + j, which no other chunk uses.
+    // (unsplit sequences or window mode); chunk j of sequence n starting at
+    // token t0 goes to slot t0 / 32 + n + j, which no other chunk uses (in
+    // window mode: see seg_sel).
     float* h_states;
     // With h_states: V - K+ S and U of every chunk, token-major like o.
     float* r_out;
@@ -100,7 +107,13 @@ hipError_t launch_epilogue(const float* o, const float* g, const float* w, float
 // start_n / 32 + n + j).  Arrays: h, dsn [slots, H, 128, 128];
 // tmp [slots, H, 15488] floats per (chunk, head): T^T, M^T, P [32][32],
 // K_end^T, Q+^T, -(B_beta K+)^T [128][32] and e^{g_C} [128];
-// w, r, u [tokens, H, 128].
+// w, r, u [tokens, H, 128].  Window mode (win_len > 0, equal lengths only):
+// the pass covers tokens [win_idx * win_len, (win_idx + 1) * win_len) of
+// every sequence, with the compact slots and rows of PrefillParams::seg_sel
+// (slots = n_seqs * win_len / 32, rows = n_seqs * win_len); dS_T is the
+// gradient at the window's end and dS0 receives the one at its start (the
+// same array is allowed: each element is read before it is written, by the
+// same thread).
 struct BwdParams {
     const void* q;
     const void* k;
@@ -124,6 +137,8 @@ struct BwdParams {
     float* w;
     int64_t T;              // tokens per sequence (equal lengths) or total (packed)
     int64_t slots;
+    int64_t win_len;        // window mode: tokens per window (a multiple of 32), else 0
+    int32_t win_idx;        // window mode: which window
     int32_t n_seqs, H;
 };
 hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream);

@@ -90,13 +90,18 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
         t0 = a < 0 ? 0 : (a > Tt ? Tt : a);
         t1 = b < t0 ? t0 : (b > Tt ? Tt : b);
     } else {
-        const int64_t b = n / p.seg_per_seq, r = n - b * p.seg_per_seq;
+        const int64_t b = p.seg_sel >= 0 ? n : n / p.seg_per_seq;
+        const int64_t r = p.seg_sel >= 0 ? p.seg_sel : n - b * p.seg_per_seq;
         const int64_t e = (b + 1) * Tt;
         t0 = b * Tt + r * p.seg_len;
         t0 = t0 < e ? t0 : e;
         t1 = e - t0 > p.seg_len ? t0 + p.seg_len : e;
     }
     const int64_t nch = (t1 - t0 + CH - 1) / CH;
+    // STORE_H outputs: first state slot of this chain and the offset added to
+    // its token rows (window mode: the compact layout described at seg_sel)
+    const int64_t hslot0 = p.seg_sel >= 0 ? (int64_t)n * (p.seg_len / CH) : t0 / CH + n;
+    const int64_t srow = p.seg_sel >= 0 ? (int64_t)n * p.seg_len - t0 : 0;
     const int H = p.H;
     const int rowel = H * DK;   // elements between consecutive tokens
 
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
         }
         // state at the start of chunk j -> slot hslot0 + j
         float* hbase = nullptr;
-        if constexpr (STORE_H) hbase = p.h_states + ((size_t)(t0 / CH + n) * H + h) * (DK * DK);
+        if constexpr (STORE_H) hbase = p.h_states + ((size_t)hslot0 * H + h) * (DK * DK);
         auto store_h = [&](float* dst, int it, int ct) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
             // R' = B_beta (V - K+ S)  (V - K+ S itself kept for the backward pass)
             if constexpr (STORE_H) {
                 const int64_t cs = t0 + cidx * CH;
-                const auto rr = make_rsrc(p.r_out + ((size_t)cs * H + h) * DK, span_bytes(n_valid(cs), 4));
+                const auto rr = make_rsrc(p.r_out + ((size_t)(cs + srow) * H + h) * DK, span_bytes(n_valid(cs), 4));
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -610,7 +615,7 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
             }
             if constexpr (STORE_H) {
                 const int64_t cs = t0 + cidx * CH;
-                const auto ru = make_rsrc(p.u_out + ((size_t)cs * H + h) * DK, span_bytes(n_valid(cs), 4));
+                const auto ru = make_rsrc(p.u_out + ((size_t)(cs + srow) * H + h) * DK, span_bytes(n_valid(cs), 4));
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll

@@ -108,13 +108,18 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
         t0 = a < 0 ? 0 : (a > Tt ? Tt : a);
         t1 = b < t0 ? t0 : (b > Tt ? Tt : b);
     } else {
-        const int64_t b = n / p.seg_per_seq, r = n - b * p.seg_per_seq;
+        const int64_t b = p.seg_sel >= 0 ? n : n / p.seg_per_seq;
+        const int64_t r = p.seg_sel >= 0 ? p.seg_sel : n - b * p.seg_per_seq;
         const int64_t e = (b + 1) * Tt;
         t0 = b * Tt + r * p.seg_len;
         t0 = t0 < e ? t0 : e;
         t1 = e - t0 > p.seg_len ? t0 + p.seg_len : e;
     }
     const int64_t nch = (t1 - t0 + CH - 1) / CH;
+    // STORE_H outputs: first state slot of this chain and the offset added to
+    // its token rows (window mode: the compact layout described at seg_sel)
+    const int64_t hslot0 = p.seg_sel >= 0 ? (int64_t)n * (p.seg_len / CH) : t0 / CH + n;
+    const int64_t srow = p.seg_sel >= 0 ? (int64_t)n * p.seg_len - t0 : 0;
     const int H = p.H;
     const int rowel = H * DK;   // elements between consecutive tokens
 
@@ -269,8 +274,8 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 const int b3 = (int)(s % 3), b2 = (int)(s & 1);
                 const float* Tb = sT[b2];
                 float4 t00v, t11v, l10v;
-                if constexpr (STORE_H) {   // the state at this chunk's start -> slot t0 / 32 + n + s
-                    float* hb = p.h_states + ((size_t)(t0 / CH + n + s) * H + h) * (DK * DK);
+                if constexpr (STORE_H) {   // the state at this chunk's start -> slot hslot0 + s
+                    float* hb = p.h_states + ((size_t)(hslot0 + s) * H + h) * (DK * DK);
 #pragma unroll
                     for (int it = 0; it < 8; ++it)
 #pragma unroll
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                         R[tb][r] = __uint_as_float((uint32_t)pv[tb][r] << 16) - R[tb][r];
                 if constexpr (STORE_H) {
                     const int64_t cs = t0 + s * CH;
-                    const auto rr = make_rsrc(p.r_out + ((size_t)cs * H + h) * DK, span_bytes(n_valid(cs), 4));
+                    const auto rr = make_rsrc(p.r_out + ((size_t)(cs + srow) * H + h) * DK, span_bytes(n_valid(cs), 4));
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 }
                 if constexpr (STORE_H) {
                     const int64_t cs = t0 + s * CH;
-                    const auto ru = make_rsrc(p.u_out + ((size_t)cs * H + h) * DK, span_bytes(n_valid(cs), 4));
+                    const auto ru = make_rsrc(p.u_out + ((size_t)(cs + srow) * H + h) * DK, span_bytes(n_valid(cs), 4));
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int el = (g * 4 + r) * rowel + col0 + ln;

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /* Largest head count any entry point accepts: the kernels address a chunk's
  * token rows (up to 32 rows of H * 128 fp32 values) with 32-bit byte
@@ -278,16 +278,35 @@ int kda_epilogue(const float* o, const float* g, const float* w, int64_t rows, i
                  int32_t dv, float* out, hipStream_t stream);
 
 /*
- * Workspace size in bytes for kda_chunk_bwd (always required): with
- * tokens = n_seqs * T (equal lengths) or T (varlen != 0) and
- * slots = tokens / 32 + n_seqs, it holds the state at the start and the
- * state gradient at the end of every 32-token chunk (2 * slots * H * 64 KiB),
- * the chunk's matrices (three 32 x 32, three 128 x 32 and one 128-vector of
- * fp32: slots * H * 61952 bytes) and three fp32 value rows per token and
- * head (tokens * H * 1536 bytes).  0 for invalid sizes.
+ * Workspace size in bytes for kda_chunk_bwd (always required).  It holds,
+ * per 32-token chunk and head, the state at the chunk's start and the state
+ * gradient at its end (2 * 64 KiB) and the chunk's matrices (three 32 x 32,
+ * three 128 x 32 and one 128-vector of fp32: 61952 bytes), and per token and
+ * head three fp32 value rows (1536 bytes), for:
+ *   packed batches (varlen != 0): every chunk, slots = T / 32 + n_seqs
+ *     chunk slots and T tokens;
+ *   equal lengths (varlen == 0): one window of every sequence.  The backward
+ *     runs each sequence in windows of W chunks, the last window first
+ *     (W = KDA_BWD_WINDOW / 32, or all chunks when T is no longer): n_seqs * W
+ *     slots and n_seqs * 32 W tokens, plus the state at the start of every
+ *     window after the first and one state gradient per (sequence, head)
+ *     carried between windows (n_seqs * H * 64 KiB each).
+ * 0 for invalid sizes.
  */
+#define KDA_BWD_WINDOW 2048
 size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
                                      int32_t dk, int32_t dv, int varlen);
+
+/*
+ * Workspace size in bytes for kda_chunk_bwd on an equal-length batch with
+ * windows of window_tokens tokens, rounded up to 32 times a power of two (a
+ * window at least as long as T: one window, the largest and fastest
+ * layout).  kda_chunk_bwd uses the longest window whose layout fits in the
+ * workspace it is given: one window if it fits, else the longest
+ * power-of-two number of chunks.  0 for invalid sizes.
+ */
+size_t kda_chunk_bwd_workspace_bytes_window(int32_t n_seqs, int64_t T, int32_t H,
+                                            int32_t dk, int32_t dv, int64_t window_tokens);
 
 /*
  * Backward pass of kda_chunk_fwd: the gradients of a scalar loss L with
@@ -308,8 +327,17 @@ size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  *   beta; grad_S0 [n_seqs, H, dk, dv] or NULL to skip (it may be the same
  *   pointer as grad_S_T; any other overlap between an output, an input or
  *   the workspace is rejected).
- *   workspace: kda_chunk_bwd_workspace_bytes(...) bytes, 16-byte aligned,
- *   contents clobbered.
+ *   workspace: kda_chunk_bwd_workspace_bytes(...) bytes or more (equal
+ *   lengths: any size kda_chunk_bwd_workspace_bytes_window reports),
+ *   16-byte aligned, contents clobbered.
+ * Equal-length batches run window by window (see the workspace queries):
+ * the forward pass first walks the windows to store the state at each
+ * window's start, then each window, last first, recomputes its chunk
+ * states and runs the backward passes over it.  Every window after the
+ * first costs one more launch of the forward chain over the window before
+ * it.  Every window length evaluates the same chunk arithmetic in the same
+ * order (the carried state and state gradient pass through memory in fp32
+ * unchanged), so the gradients do not depend on it.
  * Numerics: fp32 accumulation throughout.  With KDA_F32 inputs every
  * product runs on fp32 matrix cores; with KDA_BF16 inputs the products of
  * the state-gradient walk and of the per-chunk gradients use split (hi + lo)

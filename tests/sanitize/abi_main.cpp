@@ -15,6 +15,17 @@
 namespace {
 int n_launch = 0, n_merge = 0, n_dual = 0, last_slices = 0, last_units = 0;
 int fails = 0;
+// forward and backward launches in order, for the backward's window plan
+struct Rec {
+    char kind;                 // 'f' forward, 'b' backward passes
+    int seg_sel, win_idx;
+    bool stores;               // forward keeps per-chunk values
+    const float *S0, *S_T, *dS_T;
+    float* dS0;
+    int64_t seg_len, win_len, slots;
+};
+Rec recs[256];
+int n_recs = 0;
 #define CHECK(c)                                                               \
     do {                                                                       \
         if (!(c)) {                                                            \
@@ -28,6 +39,11 @@ namespace kda {
 hipError_t launch_chunk_fwd_pipe(const PrefillParams&, hipStream_t) { return hipSuccess; }
 hipError_t launch_chunk_fwd(const PrefillParams& p, bool, int wcols, bool, hipStream_t) {
     ++n_launch;
+    if (n_recs < 256)
+        recs[n_recs++] = Rec{'f', p.seg_sel, 0, p.h_states != nullptr, p.S0, p.S_T, nullptr, nullptr,
+                             p.seg_len, 0, 0};
+    CHECK(p.seg_sel < 0 || (!p.cu && p.seg_len % 32 == 0 && p.seg_len > 0));
+    CHECK(!p.h_states || (p.r_out && p.u_out && !p.o));
     last_slices = p.n_slices;
     last_units = p.n_units;
     CHECK(wcols * 4 * p.n_slices == 128);
@@ -69,6 +85,10 @@ hipError_t launch_epilogue(const float*, const float*, const float*, float*, int
 hipError_t launch_chunk_bwd(const BwdParams& p, bool, hipStream_t) {
     ++n_launch;
     CHECK(p.slots >= 1);
+    CHECK(p.win_len == 0 || (!p.cu && p.win_len % 32 == 0 && p.slots * 32 == p.n_seqs * p.win_len));
+    if (n_recs < 256)
+        recs[n_recs++] = Rec{'b', -1, p.win_idx, false, nullptr, nullptr, p.dS_T, p.dS0, 0,
+                             p.win_len, p.slots};
     return hipSuccess;
 }
 }  // namespace kda
@@ -139,16 +159,70 @@ int main() {
                        nullptr) == KDA_OK);
     CHECK(kda_epilogue(F(0), F(1), F(2), 64, 4, 128, F(0), nullptr) == KDA_OK);
     CHECK(kda_epilogue(F(0), F(1), F(2), 64, 4, 128, F(1), nullptr) == KDA_ERR_ALIASING);
-    // backward
+    // backward: equal lengths run in windows, the last first
+    auto bwd_plan = [&](int n_seqs, int64_t T, size_t ws, const float* S0, const float* gST,
+                        float* gS0, int expect_windows, int64_t expect_win_len) {
+        n_recs = 0;
+        CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), S0, nullptr, n_seqs, T, 96, 128,
+                            128, F(20), gST, F(21), F(22), F(23), F(24), F(25), gS0, (void*)P(27), ws,
+                            nullptr) == KDA_OK);
+        const int K = expect_windows;
+        CHECK(n_recs == (K - 1) + 2 * K);
+        if (n_recs != (K - 1) + 2 * K) return;
+        // the states at the window starts: forward over windows 0 .. K-2
+        const float* prev_end = nullptr;
+        for (int w = 0; w + 1 < K; ++w) {
+            const Rec& r = recs[w];
+            CHECK(r.kind == 'f' && r.seg_sel == w && !r.stores && r.S_T && r.seg_len == expect_win_len);
+            CHECK(w == 0 ? r.S0 == S0 : r.S0 == prev_end);
+            prev_end = r.S_T;
+        }
+        // then per window, last first: forward keeping values, backward passes
+        const float* carry = nullptr;
+        for (int i = 0; i < K; ++i) {
+            const int w = K - 1 - i;
+            const Rec& f = recs[K - 1 + 2 * i];
+            const Rec& b = recs[K + 2 * i];
+            CHECK(f.kind == 'f' && f.seg_sel == w && f.stores && f.seg_len == expect_win_len);
+            CHECK(w == 0 ? f.S0 == S0 : f.S0 == recs[w - 1].S_T);
+            CHECK(b.kind == 'b' && b.win_idx == w && b.win_len == expect_win_len);
+            CHECK(b.slots == n_seqs * expect_win_len / 32);
+            CHECK(w == K - 1 ? b.dS_T == gST : b.dS_T == carry);
+            if (w == 0) CHECK(b.dS0 == gS0);
+            else CHECK(b.dS0 != nullptr && (w == K - 1 || b.dS0 == carry));
+            carry = b.dS0;
+        }
+    };
     {
         const size_t ws = kda_chunk_bwd_workspace_bytes(1, 8192, 96, 128, 128, 0);
-        CHECK(ws > 0);
+        CHECK(ws > 0 && ws == kda_chunk_bwd_workspace_bytes_window(1, 8192, 96, 128, 128, KDA_BWD_WINDOW));
+        bwd_plan(1, 8192, ws, nullptr, nullptr, F(26), 4, 2048);
+        bwd_plan(1, 8192, ws, F(7), F(8), F(26), 4, 2048);
+        // a little less workspace: the next shorter window
+        bwd_plan(1, 8192, ws - 1, nullptr, nullptr, F(26), 8, 1024);
+        // one window, as large as the sequence
+        const size_t one = kda_chunk_bwd_workspace_bytes_window(1, 8192, 96, 128, 128, 8192);
+        CHECK(one > ws && one == kda_chunk_bwd_workspace_bytes_window(1, 8192, 96, 128, 128, 1 << 30));
+        bwd_plan(1, 8192, one, F(7), F(8), F(8), 1, 8192);
+        // a ragged last window, three sequences
+        const size_t w3 = kda_chunk_bwd_workspace_bytes_window(3, 300, 96, 128, 128, 64);
+        bwd_plan(3, 300, w3, F(7), F(8), F(26), 5, 64);
+        // nothing to run but the gradient hand-through
+        bwd_plan(2, 0, kda_chunk_bwd_workspace_bytes(2, 0, 96, 128, 128, 0), F(7), F(8), F(26), 1, 32);
         CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, nullptr, 1, 8192, 96, 128,
                             128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26), (void*)P(27),
-                            ws, nullptr) == KDA_OK);
-        CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, nullptr, 1, 8192, 96, 128,
-                            128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26), (void*)P(27),
-                            ws - 1, nullptr) == KDA_ERR_WORKSPACE);
+                            1000, nullptr) == KDA_ERR_WORKSPACE);
+        // packed batches: one forward, one backward over every chunk
+        n_recs = 0;
+        const size_t wp = kda_chunk_bwd_workspace_bytes(4, 5000, 96, 128, 128, 1);
+        CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(28), 4,
+                            5000, 96, 128, 128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26),
+                            (void*)P(27), wp, nullptr) == KDA_OK);
+        CHECK(n_recs == 2 && recs[0].kind == 'f' && recs[0].seg_sel < 0 && recs[0].stores &&
+              recs[1].kind == 'b' && recs[1].win_len == 0 && recs[1].slots == 5000 / 32 + 4);
+        CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(28), 4,
+                            5000, 96, 128, 128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26),
+                            (void*)P(27), wp - 1, nullptr) == KDA_ERR_WORKSPACE);
     }
     for (int s = -1; s <= 9; ++s) CHECK(kda_status_str(s) != nullptr);
     CHECK(kda_abi_version() == KDA_ABI_VERSION);

@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(lib):
     assert names == sorted(["kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_bytes",
                             "kda_chunk_fwd", "kda_decode_step", "kda_recurrent_fwd",
                             "kda_prologue", "kda_epilogue", "kda_chunk_bwd_workspace_bytes",
-                            "kda_chunk_bwd", "kda_chunk_fwd_noalloc"])
+                            "kda_chunk_bwd", "kda_chunk_fwd_noalloc",
+                            "kda_chunk_bwd_workspace_bytes_window"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -218,15 +219,35 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def test_bwd_workspace_query(lib):
     ws = lib.kda_chunk_bwd_workspace_bytes
-    # slots = tokens / 32 + n_seqs; per slot and head 2 states + 3 [32, 32]
-    # matrices, plus one fp32 row per token and head
-    def expect(tokens, n, H):
+    wsw = lib.kda_chunk_bwd_workspace_bytes_window
+    per_slot = 2 * 128 * 128 + 3 * 32 * 32 + 3 * 128 * 32 + 128     # floats per chunk and head
+    state = 128 * 128
+
+    # packed: slots = tokens / 32 + n_seqs; per slot and head 2 states and
+    # the chunk matrices, plus three fp32 rows per token and head
+    def packed(tokens, n, H):
         slots = tokens // 32 + n
-        return (slots * H * (2 * 128 * 128 + 3 * 32 * 32 + 3 * 128 * 32 + 128)
-                + 3 * tokens * H * 128) * 4
-    assert ws(1, 8192, 96, 128, 128, 0) == expect(8192, 1, 96)
-    assert ws(3, 100, 2, 128, 128, 0) == expect(300, 3, 2)
-    assert ws(32, 270000, 96, 128, 128, 1) == expect(270000, 32, 96)
+        return (slots * H * per_slot + 3 * tokens * H * 128) * 4
+
+    # equal lengths, windows of W chunks: one window of every sequence, the
+    # states at the starts of windows 1.., one carried gradient per unit
+    def windowed(n, T, H, W):
+        C = -(-T // 32)
+        W = max(1, min(W, C))
+        K = max(1, -(-C // W))
+        extra = (K - 1) * n * H * state + (n * H * state if K > 1 else 0)
+        return (n * W * H * per_slot + 3 * n * 32 * W * H * 128 + extra) * 4
+
+    assert ws(1, 8192, 96, 128, 128, 0) == windowed(1, 8192, 96, 64)      # 2048-token windows
+    assert ws(1, 8192, 96, 128, 128, 0) < 1.6e9                          # < 1.6 GB
+    assert ws(3, 100, 2, 128, 128, 0) == windowed(3, 100, 2, 64)         # one window
+    assert ws(32, 270000, 96, 128, 128, 1) == packed(270000, 32, 96)
+    assert wsw(1, 8192, 96, 128, 128, 8192) == windowed(1, 8192, 96, 256)
+    assert wsw(1, 8192, 96, 128, 128, 3000) == windowed(1, 8192, 96, 128)   # 94 chunks -> 128
+    assert wsw(3, 300, 96, 128, 128, 64) == windowed(3, 300, 96, 2)
+    assert wsw(3, 300, 96, 128, 128, 1) == windowed(3, 300, 96, 1)
+    assert wsw(2, 0, 4, 128, 128, 2048) == windowed(2, 0, 4, 1)
+    assert wsw(2, 64, 4, 128, 128, 0) == 0
     assert ws(2, 64, 4, 64, 128, 0) == 0
     assert ws(-1, 64, 4, 128, 128, 0) == 0
 

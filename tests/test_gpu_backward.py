@@ -42,9 +42,9 @@ def inputs(w, lens, s0, ds_std, la_const=None):
     return w, a, S0, dO, dS, cu
 
 
-def run(w, a, S0, dO, dS, cu, equal=None):
+def run(w, a, S0, dO, dS, cu, equal=None, window_tokens=None):
     """GPU backward; `equal` = (B, T) passes the equal-length layout instead
-    of cu_seqlens."""
+    of cu_seqlens; window_tokens sizes its workspace for that window length."""
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     d = {n: torch.from_numpy(np.ascontiguousarray(a[n])).cuda() for n in a}
     for n in ("q", "k", "v"):
@@ -60,7 +60,8 @@ def run(w, a, S0, dO, dS, cu, equal=None):
         go = go.reshape((B, T) + tuple(go.shape[1:]))
     else:
         cu_dev = torch.from_numpy(cu.astype(np.int32)).cuda()
-    g = kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s0, go, gst, cu_dev)
+    g = kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s0, go, gst, cu_dev,
+                      window_tokens=window_tokens)
     torch.cuda.synchronize()
     T = a["q"].shape[0]
     out = [t.cpu().numpy() for t in g]
@@ -69,16 +70,16 @@ def run(w, a, S0, dO, dS, cu, equal=None):
     return out
 
 
-def compare(w, a, S0, dO, dS, cu, tol, label, equal=None):
+def compare(w, a, S0, dO, dS, cu, tol, label, equal=None, window_tokens=None):
     say(f"[bwd] {label}: GPU")
-    got = run(w, a, S0, dO, dS, cu, equal)
+    got = run(w, a, S0, dO, dS, cu, equal, window_tokens)
     say(f"[bwd] {label}: oracle")
     ref = oracle.backward(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], S0, dO, dS, cu)
     errs = {n: rel_err(x, r) for n, x, r in zip(NAMES, got, ref)}
     say(f"[bwd] {label}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f" (tol {tol})")
     for n, e in errs.items():
         assert e <= tol, (n, e)
-    return errs
+    return got
 
 
 @pytest.mark.parametrize("lens,H,s0,ds", [([100, 100], 3, 0.02, 1.0), ([1], 1, 0.0, 0.0),
@@ -219,3 +220,51 @@ def test_bwd_full_size_varlen_lengths_sampled():
         say(f"[bwd] varlen sequence {n} head {h}: " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()))
         for nm, e in errs.items():
             assert e <= TOL_BF16, (n, h, nm, e)
+
+
+# ------------------------------------------------ equal lengths in windows
+@pytest.mark.parametrize("dtype,B,T,H", [("bf16", 3, 300, 3), ("f32", 2, 200, 2),
+                                         ("bf16", 3, 200, 96)])
+def test_bwd_windows_against_oracle(dtype, B, T, H):
+    """Equal-length batches run window by window (the last window first, the
+    state gradient carried between windows, the states at window starts from
+    a forward pass without per-chunk outputs): 2-chunk and 4-chunk windows
+    with a ragged last window, S0 and dL/dS_T given, every element of all
+    six gradients against the oracle; the gradients equal those of the
+    single-window layout bit for bit.  B=3, H=96 runs the one-slice kernels
+    (288 pairs)."""
+    base = W.workload(1 if dtype == "bf16" else 0).shrink(H=H)
+    w, a, S0, dO, dS, cu = inputs(base, [T] * B, 0.02, 1.0)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    C = -(-T // 32)
+    single = run(w, a, S0, dO, dS, cu, (B, T), window_tokens=T)
+    for win in (64, 128):
+        n_win = -(-C // (win // 32))
+        got = compare(w, a, S0, dO, dS, cu, tol, f"{dtype} B={B} T={T} H={H} windows of {win} "
+                      f"tokens ({n_win} windows)", equal=(B, T), window_tokens=win)
+        for n, x, y in zip(NAMES, got, single):
+            assert np.array_equal(x, y), (win, n, float(np.abs(x - y).max()))
+
+
+def test_bwd_window_workspace_sizes():
+    """The default workspace of the T=8192, H=96 shape is the 2048-token
+    window layout (under 1.6 GB, a quarter of the single-window layout), and
+    a workspace one byte short of it runs 1024-token windows with the same
+    gradients."""
+    n = kda.chunk_bwd_workspace_bytes
+    default = n(1, 8192, 96)
+    one = n(1, 8192, 96, window_tokens=8192)
+    say(f"[bwd] workspace T=8192 H=96: default {default / 1e9:.3f} GB, one window {one / 1e9:.3f} GB")
+    assert default == n(1, 8192, 96, window_tokens=2048) and default < 1.6e9 and one > 3.5 * default
+    w, a, S0, dO, dS, cu = inputs(W.workload(1).shrink(H=2), [700], 0.02, 1.0)
+    ws_small = torch.empty(n(1, 700, 2, window_tokens=128) - 1, dtype=torch.uint8, device="cuda")
+    d = {k: torch.from_numpy(np.ascontiguousarray(a[k])).cuda()[None] for k in a}
+    for k in ("q", "k", "v"):
+        d[k] = d[k].to(torch.bfloat16)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], torch.from_numpy(S0).cuda(),
+            torch.from_numpy(dO).cuda()[None], torch.from_numpy(dS).cuda())
+    g_small = kda.chunk_bwd(*args, workspace=ws_small)      # 64-token windows
+    g_one = kda.chunk_bwd(*args, window_tokens=700)
+    torch.cuda.synchronize()
+    for nm, x, y in zip(NAMES, g_small, g_one):
+        assert torch.equal(x, y), nm
