@@ -1,5 +1,10 @@
-// Contraction-phase probe (measurement only; built into its own library,
-// libkda_probe.so, never into libkda.so).
+// Measurement probes (built into their own library, libkda_probe.so, never
+// into libkda.so): the contraction-phase probe below, and a plain in-place
+// stream over a large fp32 buffer (the decode step's access pattern without
+// its arithmetic), which measures the HBM bandwidth a read-then-write pass
+// reaches on the device.
+//
+// Contraction-phase probe.
 //
 // The pipelined prefill's consumer waves spend each 32-token chunk in two
 // matrix-core phases: K+ S / Q+ S (per k-slice: the state tile packed to fp16
@@ -225,6 +230,67 @@ __global__ __launch_bounds__(256) void contraction_probe_kernel(float* out, int 
 
 // Matrix-core flops one launch issues: 16 (K+ S / Q+ S) and 24 (update)
 // 16x16x32 products of 16384 flops per wave and iteration.
+namespace kda {
+namespace {
+// x <- a x in place over n4 float4s: every wave instruction moves 1 KB of
+// consecutive memory (64 lanes x 16 B), nontemporal loads and stores, 8
+// loads in flight per lane before the first store; grid-stride over
+// 8 KB-per-wave blocks, and a tail of single float4s.
+typedef float v4f __attribute__((ext_vector_type(4)));
+// mode 0: x <- a x in place; 1: y <- a x; 2: read x only (one sum per lane
+// written to y, so no load can be dropped).
+template <int MODE>
+__global__ __launch_bounds__(1024) void stream_probe_kernel(v4f* x, v4f* y, int64_t n4, float a) {
+    constexpr int U = 8;
+    const int64_t lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int64_t n_blk = n4 / (64 * U);
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t b = wave; b < n_blk; b += n_waves) {
+        const int64_t o = b * (64 * U) + lane;
+        v4f v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(x + o + 64 * u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (MODE == 0) __builtin_nontemporal_store(v[u] * a, x + o + 64 * u);
+            else if constexpr (MODE == 1) __builtin_nontemporal_store(v[u] * a, y + o + 64 * u);
+            else acc += v[u];
+        }
+    }
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = n_blk * (64 * U) + t; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        if constexpr (MODE == 0) x[i] = x[i] * a;
+        else if constexpr (MODE == 1) y[i] = x[i] * a;
+        else acc += x[i];
+    }
+    if constexpr (MODE == 2) y[t] = acc;
+}
+}  // namespace
+}  // namespace kda
+
+// x: n_floats fp32 (a multiple of 4, 16-byte aligned); n_wg workgroups of
+// 1024 threads.  mode 0: x <- a x in place (y unused); mode 1: y <- a x
+// (y as large as x); mode 2: read x, y receives n_wg * 1024 float4 partial
+// sums.  Returns a hipError_t.
+extern "C" int kda_probe_stream(float* x, float* y, int64_t n_floats, float a, int n_wg, int mode,
+                                hipStream_t stream) {
+    if (!x || n_floats < 4 || (n_floats & 3) || ((uintptr_t)x & 15) || n_wg < 1 || mode < 0 ||
+        mode > 2 || (mode != 0 && (!y || ((uintptr_t)y & 15))))
+        return (int)hipErrorInvalidValue;
+    kda::v4f* xv = (kda::v4f*)x;
+    kda::v4f* yv = (kda::v4f*)y;
+    const int64_t n4 = n_floats / 4;
+    if (mode == 0)
+        hipLaunchKernelGGL(kda::stream_probe_kernel<0>, dim3(n_wg), dim3(1024), 0, stream, xv, yv, n4, a);
+    else if (mode == 1)
+        hipLaunchKernelGGL(kda::stream_probe_kernel<1>, dim3(n_wg), dim3(1024), 0, stream, xv, yv, n4, a);
+    else
+        hipLaunchKernelGGL(kda::stream_probe_kernel<2>, dim3(n_wg), dim3(1024), 0, stream, xv, yv, n4, a);
+    return (int)hipGetLastError();
+}
+
 extern "C" double kda_probe_flops(int n_wg, int iters, int mode) {
     const double per = (mode != 1 ? 16.0 : 0.0) + (mode != 0 ? 24.0 : 0.0);
     return per * 16384.0 * 4.0 * n_wg * (double)iters;

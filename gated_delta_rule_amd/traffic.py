@@ -28,6 +28,14 @@ share of LDS active cycles lost to bank conflicts (SQ_LDS_BANK_CONFLICT over
 SQ_LDS_IDX_ACTIVE), with one wave per SIMD and nothing else on the compute
 units.
 
+    python -m gated_delta_rule_amd.traffic ceiling
+
+times the stream probe (csrc/kda_phase_probe.hip: x <- a x in place over the
+decode state's 1.61 GB with nontemporal 16-byte accesses, the decode step's
+access pattern without its arithmetic) over several grid sizes and writes
+`profiles/hbm_stream_ceiling.json`: the read+write rate one such pass reaches,
+the practical ceiling for the decode step.
+
     python -m gated_delta_rule_amd.traffic mfma [--out DIR]
 
 runs one rocprofv3 pass per counter (MFMA operations per data type, MFMA
@@ -127,6 +135,81 @@ def run_probe_target():
         res[mode] = {"ms_median": med, "flops_per_launch": flops,
                      "tflops": flops / (med * 1e-3) / 1e12}
     print("PROBE " + json.dumps(res), flush=True)
+
+
+STREAM_FLOATS = 256 * 96 * 128 * 128   # the decode workload's fp32 state, 1.61 GB
+STREAM_GRIDS = (256, 512, 1024, 2048, 4096, 8192)
+
+
+STREAM_MODES = {0: ("in place x <- a x", 2), 1: ("copy y <- a x", 2), 2: ("read only", 1)}
+
+
+def collect_ceiling(profiles_dir):
+    """Time the stream probe (csrc/kda_phase_probe.hip) over the decode
+    state's 1.61 GB of fp32, nontemporal 16-byte accesses, after a clock
+    settle: in place (the decode step's read-then-write pattern without its
+    arithmetic), as a copy to a second buffer, and read only, each over
+    several grid sizes.  Writes profiles/hbm_stream_ceiling.json with the
+    best rate of each (bytes moved / time)."""
+    import ctypes
+    import time
+    import torch
+    build_probe(verbose=True)
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.kda_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.kda_probe_stream.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    x = torch.ones(STREAM_FLOATS, dtype=torch.float32, device=dev)
+    y = torch.empty(STREAM_FLOATS, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(n_wg, mode):
+        rc = lib.kda_probe_stream(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                  STREAM_FLOATS, 1.0, n_wg, mode, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"stream probe launch failed: {rc}")
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:   # clock settle
+        launch(2048, 0)
+        torch.cuda.synchronize()
+    modes = {}
+    for mode, (name, passes) in STREAM_MODES.items():
+        nbytes = passes * STREAM_FLOATS * 4
+        rows = []
+        for n_wg in STREAM_GRIDS:
+            launch(n_wg, mode)
+            ms = []
+            for _ in range(10):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch(n_wg, mode)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            ms.sort()
+            med = ms[len(ms) // 2]
+            rows.append({"workgroups": n_wg, "ms_median": med, "ms_min": ms[0],
+                         "gbps_median": nbytes / (med * 1e-3) / 1e9})
+            print(f"stream probe {name}, {n_wg} workgroups: {med:.4f} ms, "
+                  f"{rows[-1]['gbps_median']:.0f} GB/s", flush=True)
+        best = max(rows, key=lambda r: r["gbps_median"])
+        modes[name] = {"bytes_per_launch": nbytes, "grids": rows, "best_gbps": best["gbps_median"],
+                       "best_frac_of_8tbps": best["gbps_median"] / 8000.0}
+    doc = {
+        "probe": "csrc/kda_phase_probe.hip stream_probe_kernel over 1.61 GB of fp32 (the decode "
+                 "state's size): 1024-thread workgroups, 16-byte nontemporal loads and stores, 1 KB "
+                 "per wave instruction, 8 loads in flight per lane",
+        "command": "python -m gated_delta_rule_amd.traffic ceiling",
+        "modes": modes,
+        "probe_source_sha256_16": probe_hash(),
+    }
+    path = os.path.join(profiles_dir, "hbm_stream_ceiling.json")
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    print("stream ceilings: " + ", ".join(f"{k} {v['best_gbps']:.0f} GB/s" for k, v in modes.items())
+          + f" -> {path}", flush=True)
 
 
 def probe_hash():
@@ -441,7 +524,12 @@ def main():
     ph.add_argument("--out", default=os.path.join(ROOT, "counters_out", "phases"))
     ph.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     ph.add_argument("--parse-only", action="store_true")
+    ce = sub.add_parser("ceiling")
+    ce.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
+    if args.cmd == "ceiling":
+        collect_ceiling(os.path.abspath(args.profiles_dir))
+        return
     if args.cmd == "phases":
         collect_phases(os.path.abspath(args.out), os.path.abspath(args.profiles_dir), not args.parse_only)
         return
