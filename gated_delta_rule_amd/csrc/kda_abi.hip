@@ -468,12 +468,15 @@ static bool bwd_layout_packed(int64_t n_seqs, int64_t tokens, int64_t H, BwdLayo
     return bwd_layout(n_seqs, tokens / kChunk + n_seqs, tokens, 1, H, L);
 }
 // Equal lengths with windows of W chunks (W >= 1; W >= the chunks of a
-// sequence: one window).
+// sequence: one window).  At most kMaxBwdWindows windows (five launches
+// each): a window so short that more are needed is refused.
+constexpr int64_t kMaxBwdWindows = 1 << 16;
 static bool bwd_layout_windowed(int64_t n_seqs, int64_t T, int64_t H, int64_t W, BwdLayout* L) {
     const int64_t C = (T + kChunk - 1) / kChunk;
     if (W < 1) return false;
     if (W > C) W = C < 1 ? 1 : C;
     const int64_t n_win = C == 0 ? 1 : (C + W - 1) / W;
+    if (n_win > kMaxBwdWindows) return false;
     int64_t slots = 0, rows = 0;
     if (!mul_ok(n_seqs, W, &slots) || !mul_ok(slots, kChunk, &rows)) return false;
     L->win_chunks = W;
@@ -666,7 +669,7 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     // passes, with dL/dS carried from each window to the one before it.
     const int64_t win_len = L.win_chunks * kChunk;
     const int64_t st_el = units * kHeadDim * kHeadDim;
-    const int nw = (int)L.n_win;
+    const int nw = (int)L.n_win;   // <= kMaxBwdWindows
     auto ckpt = [&](int w) -> float* { return w == 0 ? nullptr : ws + L.ckpt + (int64_t)(w - 1) * st_el; };
     p.seg_len = win_len;
     for (int w = 0; w + 1 < nw; ++w) {

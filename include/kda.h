@@ -303,7 +303,9 @@ size_t kda_chunk_bwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  * window at least as long as T: one window, the largest and fastest
  * layout).  kda_chunk_bwd uses the longest window whose layout fits in the
  * workspace it is given: one window if it fits, else the longest
- * power-of-two number of chunks.  0 for invalid sizes.
+ * power-of-two number of chunks.  At most 65536 windows per sequence: a
+ * window so short that more would be needed gives 0 here (and such a
+ * workspace KDA_ERR_WORKSPACE).  0 for invalid sizes.
  */
 size_t kda_chunk_bwd_workspace_bytes_window(int32_t n_seqs, int64_t T, int32_t H,
                                             int32_t dk, int32_t dv, int64_t window_tokens);

@@ -247,6 +247,8 @@ def test_bwd_workspace_query(lib):
     assert wsw(3, 300, 96, 128, 128, 64) == windowed(3, 300, 96, 2)
     assert wsw(3, 300, 96, 128, 128, 1) == windowed(3, 300, 96, 1)
     assert wsw(2, 0, 4, 128, 128, 2048) == windowed(2, 0, 4, 1)
+    assert wsw(1, 1 << 31, 1, 128, 128, 32) == 0          # 2^26 windows: refused
+    assert wsw(1, 1 << 31, 1, 128, 128, 1 << 16) > 0      # 2^15 windows
     assert wsw(2, 64, 4, 128, 128, 0) == 0
     assert ws(2, 64, 4, 64, 128, 0) == 0
     assert ws(-1, 64, 4, 128, 128, 0) == 0
