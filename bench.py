@@ -335,9 +335,10 @@ def run_decode_only(args, torch, kda, W, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 "
                                    "(every (sequence, head) chain is independent, so more GPUs "
-                                   "would shard heads with no communication -- not built here)"}))
+                                   "would shard heads with no communication; that path is not "
+                                   "implemented)"}))
         sys.exit(2)
 
     import torch
