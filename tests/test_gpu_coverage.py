@@ -192,3 +192,26 @@ def test_decode_beta_zero_is_pure_decay():
     say(f"[coverage] decode beta == 0: rel err o {eo:.3e} S {es:.3e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
     assert rel_err(S.cpu().numpy(), want) <= 1e-6
+
+
+# ------------------------------------------ equal-length batches of length 0
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_length_sequences_pass_the_state_through(dtype):
+    """B = 2 sequences of T = 0 tokens: the forward returns S_T = S0 and the
+    backward grad_S0 = grad_S_T, exactly (no token touches either), through
+    the same entry points and launches as any other equal-length batch."""
+    B, H = 2, 3
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(5)
+    z = lambda *s, t=torch.float32: torch.empty(s, dtype=t, device="cuda")
+    q, k, v = z(B, 0, H, 128, t=dt), z(B, 0, H, 128, t=dt), z(B, 0, H, 128, t=dt)
+    la, b = z(B, 0, H, 128), z(B, 0, H)
+    S0 = torch.randn((B, H, 128, 128), device="cuda", generator=g)
+    o, st = kda.chunk_fwd(q, k, v, la, b, S0)
+    gst = torch.randn((B, H, 128, 128), device="cuda", generator=g)
+    grads = kda.chunk_bwd(q, k, v, la, b, S0, z(B, 0, H, 128), gst)
+    torch.cuda.synchronize()
+    say(f"[coverage] T=0 {dtype}: |S_T - S0| {float((st - S0).abs().max()):.1e}, "
+        f"|dS0 - dS_T| {float((grads[5] - gst).abs().max()):.1e}")
+    assert o.numel() == 0 and torch.equal(st, S0)
+    assert all(t.numel() == 0 for t in grads[:5]) and torch.equal(grads[5], gst)
