@@ -224,7 +224,7 @@ def test_bwd_full_size_varlen_lengths_sampled():
 
 # ------------------------------------------------ equal lengths in windows
 @pytest.mark.parametrize("dtype,B,T,H", [("bf16", 3, 300, 3), ("f32", 2, 200, 2),
-                                         ("bf16", 3, 200, 96)])
+                                         ("bf16", 3, 200, 96), ("f32", 3, 150, 96)])
 def test_bwd_windows_against_oracle(dtype, B, T, H):
     """Equal-length batches run window by window (the last window first, the
     state gradient carried between windows, the states at window starts from
@@ -232,7 +232,7 @@ def test_bwd_windows_against_oracle(dtype, B, T, H):
     with a ragged last window, S0 and dL/dS_T given, every element of all
     six gradients against the oracle; the gradients equal those of the
     single-window layout bit for bit.  B=3, H=96 runs the one-slice kernels
-    (288 pairs)."""
+    (288 pairs) in both dtypes."""
     base = W.workload(1 if dtype == "bf16" else 0).shrink(H=H)
     w, a, S0, dO, dS, cu = inputs(base, [T] * B, 0.02, 1.0)
     tol = TOL_BF16 if dtype == "bf16" else TOL_F32
