@@ -535,6 +535,24 @@ def main():
                          f"heads x {T} tokens of the same workload, {reps} runs, {t_cpu:.2f} s wall each; "
                          f"tokens/s counts a token once across all {H} heads; "
                          f"{cores} cores in the affinity mask"}
+        # the decode step on a sixteenth of the decode workload's states, for
+        # the decode metric's unit (fp32-equivalent state bytes read + written)
+        wdc = W.workload(4).shrink(B=16)
+        xs = W.decode_inputs(wdc, 0)
+        Sd = W.decode_state(wdc)
+        oracle.decode_step(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["beta"], Sd)   # first touch
+        dreps, t_dec = 0, 0.0
+        while dreps < 5 and t_dec < 2.0:
+            t0 = time.perf_counter()
+            oracle.decode_step(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["beta"], Sd)
+            t_dec += time.perf_counter() - t0
+            dreps += 1
+        t_dec /= dreps
+        dbytes = 2 * Sd.size * 4
+        cpu["decode"] = {"value": dbytes / t_dec / 1e9, "unit": "GB/s",
+                         "sample": f"fp64 decode step (C, OpenMP over states) on {wdc.B} x {wdc.H} "
+                                   f"states of the decode workload, {dreps} runs, {t_dec:.3f} s each "
+                                   "(fp32-equivalent state bytes read + written)"}
 
     out = {
         "metric": "KDA prefill tokens/s (H=96,d=128,T=8K) + decode-step state GB/s",
