@@ -344,7 +344,7 @@ def main():
     import torch
     import gated_delta_rule_amd as kda
     from gated_delta_rule_amd import workloads as W
-    from gated_delta_rule_amd.traffic import measured as measured_traffic, measured_mfma
+    from gated_delta_rule_amd.traffic import measured as measured_traffic, measured_mfma, measured_phases
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -507,6 +507,14 @@ def main():
                          "hw_frac_of_bf16_peak": hw / (pf_kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                          "mfma_busy_frac": busy,
                          "source": "profiles/chunk_fwd_workload1_mfma.json"}
+    # the contraction phases alone (the phase probe's rocprof record)
+    ph = measured_phases()
+    phases = None if ph is None else {
+        name: {"frac_of_16bit_peak": m["frac_of_16bit_peak"], "mfma_busy_frac": m["mfma_busy_frac"],
+               "lds_bank_conflict_frac": m.get("lds_bank_conflict_frac")}
+        for name, m in ph["modes"].items()}
+    if phases is not None:
+        phases["source"] = "profiles/contraction_phases_probe.json"
     del d, o, S_T
     torch.cuda.empty_cache()
     if args.only == "prefill":
@@ -584,7 +592,8 @@ def main():
                      "algorithmic_bytes": pf_bytes, "algorithmic_flops": pf_flops,
                      "mfma_tflops_algorithmic": pf_tflops,
                      "mfma_frac_algorithmic": pf_tflops / PEAK_BF16_TFLOPS,
-                     "mfma_counters": mfma_counters},
+                     "mfma_counters": mfma_counters,
+                     "contraction_phases": phases},
         "decode": dec,
         "cpu_baseline": cpu,
         "long_context_prefill": long_ctx,

@@ -338,6 +338,20 @@ def measured_mfma():
     return rec
 
 
+def measured_phases(profiles_dir=None):
+    """The contraction-phase probe's stored results, or None when they were
+    taken on other probe sources (or never)."""
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), "contraction_phases_probe.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("probe_source_sha256_16") != probe_hash():
+        return None
+    return rec
+
+
 def measured(kind):
     """Bytes per launch from the stored counters, or None when they were taken
     on other sources (or never)."""
