@@ -566,6 +566,7 @@ def main():
         "metric": "KDA prefill tokens/s (H=96,d=128,T=8K) + decode-step state GB/s",
         "value": tokens_per_s,
         "unit": "tokens/s",
+        "token_heads_per_s": tokens_per_s * H,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
