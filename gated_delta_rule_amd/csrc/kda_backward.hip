@@ -587,68 +587,91 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
     }
 
     // ---- products over the value columns: block mb covers columns
-    // 16 mb .. 16 mb + 15, lane half kh supplying 16 mb + 8 kh + j (j = 0..7).
-    // fp32 inputs: fp32 matrix cores, one k pair per instruction; bf16
-    // inputs: split-bf16 operands on bf16 matrix cores.
+    // 32 mb .. 32 mb + 31, lane half kh loading 32 mb + 16 kh + j (j = 0..15),
+    // so the two halves read each 128-byte row segment whole in one round;
+    // with bf16 inputs elements 0-7 and 8-15 feed two products (the k order
+    // only has to agree between the operands).  fp32 inputs: fp32 matrix
+    // cores, one k pair per instruction; bf16 inputs: split-bf16 operands on
+    // bf16 matrix cores.
     f32x16 X1 = zero16(), X2 = zero16(), X3 = zero16();
     float rsum = 0.f;   // row dk of Sn * S
-    const int vo_tok = i0 * rowb + 8 * kh * 4;   // token i0, columns 8 kh ..
-    const int vo_key = (dk * BD + 8 * kh) * 4;   // key row dk, columns 8 kh ..
-    auto ld8 = [&](__amdgpu_buffer_rsrc_t r, int vo, float (&x)[8]) {
-        const float4 a = ld4(r, vo), b = ld4(r, vo + 16);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    };
-#pragma unroll 2
-    for (int mb = 0; mb < 8; ++mb) {
-        float a_do[8], a_w[8], a_u[8], b_s[8], b_sn[8];
-        ld8(rdo, vo_tok + 64 * mb, a_do);
-        ld8(rw, vo_tok + 64 * mb, a_w);
-        ld8(ru, vo_tok + 64 * mb, a_u);
-        ld8(rs_, vo_key + 64 * mb, b_s);
-        ld8(rsn, vo_key + 64 * mb, b_sn);
+    const int vo_tok = i0 * rowb + 16 * kh * 4;   // token i0, columns 16 kh ..
+    const int vo_key = (dk * BD + 16 * kh) * 4;   // key row dk, columns 16 kh ..
+    auto ld16 = [&](__amdgpu_buffer_rsrc_t r, int vo, float (&x)[16]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) rsum += b_s[j] * b_sn[j];
+        for (int i = 0; i < 4; ++i) {
+            const float4 a = ld4(r, vo + 16 * i);
+            x[4 * i] = a.x; x[4 * i + 1] = a.y; x[4 * i + 2] = a.z; x[4 * i + 3] = a.w;
+        }
+    };
+    auto half8 = [](const float (&x)[16], int hf, float (&y)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = x[8 * hf + j];
+    };
+    for (int mb = 0; mb < 4; ++mb) {
+        float a_do[16], a_w[16], a_u[16], b_s[16], b_sn[16];
+        ld16(rdo, vo_tok + 128 * mb, a_do);
+        ld16(rw, vo_tok + 128 * mb, a_w);
+        ld16(ru, vo_tok + 128 * mb, a_u);
+        ld16(rs_, vo_key + 128 * mb, b_s);
+        ld16(rsn, vo_key + 128 * mb, b_sn);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) rsum += b_s[j] * b_sn[j];
         if constexpr (F32) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 16; ++j) {
                 X1 = mma(a_do[j], b_s[j], X1);
                 X2 = mma(a_w[j], b_s[j], X2);
                 X3 = mma(a_u[j], b_sn[j], X3);
             }
         } else {
-            const SplitBF<8> ss = split8(b_s);
-            X1 = mma3(split8(a_do), ss, X1);
-            X2 = mma3(split8(a_w), ss, X2);
-            X3 = mma3(split8(a_u), split8(b_sn), X3);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                float x[8], y[8];
+                half8(b_s, hf, y);
+                const SplitBF<8> ss = split8(y);
+                half8(a_do, hf, x);
+                X1 = mma3(split8(x), ss, X1);
+                half8(a_w, hf, x);
+                X2 = mma3(split8(x), ss, X2);
+                half8(a_u, hf, x);
+                half8(b_sn, hf, y);
+                X3 = mma3(split8(x), split8(y), X3);
+            }
         }
     }
     rsum += swap_halves(rsum);
     {
-        // dM = dO U^T and dA' = W U^T over this wave's value quarter, and
-        // the quarter's W . R per token
+        // dM = dO U^T and dA' = W U^T over this wave's value quarter
+        // (columns 32 wave ..), and the quarter's W . R per token
         f32x16 PM = zero16(), PA = zero16();
         float db = 0.f;
+        {
+            const int o = vo_tok + 128 * wave;
+            float a_do[16], a_w[16], a_u[16], a_r[16];
+            ld16(rdo, o, a_do);
+            ld16(rw, o, a_w);
+            ld16(ru, o, a_u);
+            ld16(rr, o, a_r);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int o = vo_tok + 64 * (2 * wave + qb);
-            float a_do[8], a_w[8], a_u[8], a_r[8];
-            ld8(rdo, o, a_do);
-            ld8(rw, o, a_w);
-            ld8(ru, o, a_u);
-            ld8(rr, o, a_r);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) db += a_w[j] * a_r[j];
+            for (int j = 0; j < 16; ++j) db += a_w[j] * a_r[j];
             if constexpr (F32) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < 16; ++j) {
                     PM = mma(a_do[j], a_u[j], PM);
                     PA = mma(a_w[j], a_u[j], PA);
                 }
             } else {
-                const SplitBF<8> su = split8(a_u);
-                PM = mma3(split8(a_do), su, PM);
-                PA = mma3(split8(a_w), su, PA);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    float x[8];
+                    half8(a_u, hf, x);
+                    const SplitBF<8> su = split8(x);
+                    half8(a_do, hf, x);
+                    PM = mma3(split8(x), su, PM);
+                    half8(a_w, hf, x);
+                    PA = mma3(split8(x), su, PA);
+                }
             }
         }
         db += swap_halves(db);
