@@ -430,6 +430,11 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
         if (role == 0) load_t(nch - 1);
         load_b(nch - 1);
     }
+    // Let every load above land before the walk: otherwise the loop head,
+    // which merges this entry with the back edge, waits for all memory
+    // operations in flight (the next chunk's operands included) on every
+    // chunk before its first store.
+    __builtin_amdgcn_s_waitcnt(0);
 
     for (int64_t j = nch - 1; j >= 0; --j) {
         const int64_t c0 = t0 + j * BC;
