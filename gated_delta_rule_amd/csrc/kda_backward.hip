@@ -577,17 +577,25 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
         bv[r] = ld1(rb, t * H * 4);
     }
     if (tid < BC) sBeta[tid] = ld1(rb, tid * H * 4);
+    float pP[4];
+    {
+        const auto rt = make_rsrc(p.tmp + sl * TMP_ELEMS, TMP_ELEMS * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pP[e] = ld1(rt, (OFF_P + tid + 256 * e) * 4);
+    }
     {
         // dv = Diag(beta) W: token tid / 8, value columns 16 (tid % 8) ..
         const int t = tid >> 3, v0 = 16 * (tid & 7);
         if (t < nv) {
             const float bt = ld1(rb, t * H * 4);
+            float4 w4[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) w4[v] = ld4(rw, t * rowb + (v0 + 4 * v) * 4);
             float* dst = p.dv + ((size_t)(c0 + t) * H + h) * BD + v0;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float4 w4 = ld4(rw, t * rowb + (v0 + 4 * v) * 4);
-                *reinterpret_cast<float4*>(dst + 4 * v) = make_float4(bt * w4.x, bt * w4.y, bt * w4.z, bt * w4.w);
-            }
+            for (int v = 0; v < 4; ++v)
+                *reinterpret_cast<float4*>(dst + 4 * v) =
+                    make_float4(bt * w4[v].x, bt * w4[v].y, bt * w4[v].z, bt * w4[v].w);
         }
     }
 
@@ -690,7 +698,6 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
     lds_barrier();
     {
         // dM (j <= t), dPm = -beta_t dA' (j < t), dbeta_t -= sum_j dA'_tj P_tj
-        const auto rt = make_rsrc(p.tmp + sl * TMP_ELEMS, TMP_ELEMS * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int idx = tid + 256 * e;
@@ -700,7 +707,7 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
             const float da = j < t ? (sPa[0][o] + sPa[1][o]) + (sPa[2][o] + sPa[3][o]) : 0.f;
             sdM[o] = j <= t ? dm : 0.f;
             sdP[o] = -sBeta[t] * da;
-            const float s2 = half_sum_dpp(-da * ld1(rt, (OFF_P + idx) * 4));
+            const float s2 = half_sum_dpp(-da * pP[e]);
             if (j == 0) sDb[4][t] = s2;
         }
     }
