@@ -36,6 +36,14 @@ access pattern without its arithmetic) over several grid sizes and writes
 `profiles/hbm_stream_ceiling.json`: the read+write rate one such pass reaches,
 the practical ceiling for the decode step.
 
+    python -m gated_delta_rule_amd.traffic bwd [--out DIR]
+
+does the same for the backward pass (`kda_chunk_bwd` at B=1, T=8192, H=96,
+bf16, with a one-window workspace): one FETCH_SIZE and one WRITE_SIZE pass
+over its four kernels, scaled by the copy, into
+`profiles/chunk_bwd_workload1_traffic.json` (bytes per launch of each
+kernel).
+
     python -m gated_delta_rule_amd.traffic mfma [--out DIR]
 
 runs one rocprofv3 pass per counter (MFMA operations per data type, MFMA
@@ -64,7 +72,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 
 COPY_ELEMS = 1 << 28          # 1 GiB of fp32
-LAUNCHES = {"copy": 6, "prefill": 6, "decode": 8}
+LAUNCHES = {"copy": 6, "prefill": 6, "decode": 8, "backward": 3}
 
 # Kernel symbol fragment, profile name, sources the kernel is built from.
 TARGETS = {
@@ -73,7 +81,15 @@ TARGETS = {
                  "kda_abi.hip")),
     "decode": ("recurrent_kernel", "decode_step_workload4",
                ("kda_recurrent.hip", "kda_device.h", "kda_launch.h", "kda_abi.hip")),
+    "backward": ("bwd_", "chunk_bwd_workload1",
+                 ("kda_backward.hip", "kda_prefill_pipe.hip", "kda_chunk.h", "kda_device.h", "kda_launch.h",
+                  "kda_abi.hip")),
 }
+# the backward's kernels, in launch order (symbol fragment, what it is)
+BWD_KERNELS = (("chunk_fwd_pipe_kernel<4, true>", "forward keeping chunk states, V - K+S and U"),
+               ("bwd_tmp_kernel", "chunk matrices"),
+               ("bwd_scan_kernel", "state-gradient walk"),
+               ("bwd_grad_kernel", "per-chunk gradients"))
 
 
 PROBE_SRC = "kda_phase_probe.hip"
@@ -392,6 +408,23 @@ def run_target(kind):
         st = torch.empty((w.B, w.H, 128, 128), dtype=torch.float32, device=dev)
         for _ in range(n):
             kda.chunk_fwd(d["q"], d["k"], d["v"], la, b, None, None, o=o, S_T=st)
+    elif kind == "backward":
+        # the benchmark's backward inputs: B=1, T=8192, H=96, drawn on the device
+        T, H = 8192, 96
+        g = torch.Generator(device=dev).manual_seed(13)
+        shp = (1, T, H, 128)
+        nrm = torch.nn.functional.normalize
+        q = nrm(torch.randn(shp, device=dev, generator=g), dim=-1).to(torch.bfloat16)
+        k = nrm(torch.randn(shp, device=dev, generator=g), dim=-1).to(torch.bfloat16)
+        v = torch.randn(shp, device=dev, generator=g).to(torch.bfloat16)
+        la = -5.0 * torch.sigmoid(torch.randn(shp, device=dev, generator=g))
+        beta = torch.sigmoid(torch.randn((1, T, H), device=dev, generator=g))
+        go = torch.randn(shp, device=dev, generator=g)
+        gst = torch.randn((1, H, 128, 128), device=dev, generator=g)
+        ws = torch.empty(kda.chunk_bwd_workspace_bytes(1, T, H, window_tokens=T), dtype=torch.uint8,
+                         device=dev)
+        for _ in range(n):
+            kda.chunk_bwd(q, k, v, la, beta, None, go, gst, workspace=ws)
     else:
         w = W.workload(4)
         S = torch.from_numpy(W.decode_state(w)).to(dev)
@@ -445,9 +478,8 @@ def kib_per_dispatch(per, fragment):
     return sum(vals) / len(vals), len(vals)
 
 
-def collect(out, profiles_dir):
-    os.makedirs(out, exist_ok=True)
-    os.makedirs(profiles_dir, exist_ok=True)
+def calibrate(out):
+    """FETCH_SIZE and WRITE_SIZE of the plain copy, as counter KiB per byte moved."""
     copy_bytes = COPY_ELEMS * 4
     cal = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -459,6 +491,51 @@ def collect(out, profiles_dir):
         cal[counter] = {"kib_per_dispatch": kib, "dispatches": n, "kernel": big,
                         "scale": kib * 1024.0 / copy_bytes}
         print(f"copy {counter}: {kib:.0f} KiB per dispatch, scale {cal[counter]['scale']:.4f}", flush=True)
+    return cal
+
+
+def calibration_doc(cal):
+    return {"kernel": "torch elementwise y = 1 * x, 1 GiB fp32 read + 1 GiB written",
+            **{k: {kk: vv for kk, vv in v.items() if kk != "kernel"} for k, v in cal.items()}}
+
+
+def collect_bwd(out, profiles_dir):
+    os.makedirs(out, exist_ok=True)
+    os.makedirs(profiles_dir, exist_ok=True)
+    cal = calibrate(out)
+    passes = {c: counter_pass("backward", c, out) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    kernels = []
+    for frag, what in BWD_KERNELS:
+        rec = {"kernel": frag, "pass": what}
+        for counter, per in passes.items():
+            kib, n = kib_per_dispatch(per, frag)
+            rec[counter] = {"kib_per_dispatch": kib, "dispatches": n,
+                            "bytes_scaled": kib * 1024.0 / cal[counter]["scale"]}
+        rec["hbm_bytes_per_launch"] = rec["FETCH_SIZE"]["bytes_scaled"] + rec["WRITE_SIZE"]["bytes_scaled"]
+        kernels.append(rec)
+        print(f"{frag}: read {rec['FETCH_SIZE']['bytes_scaled'] / 1e9:.3f} GB, "
+              f"written {rec['WRITE_SIZE']['bytes_scaled'] / 1e9:.3f} GB per launch", flush=True)
+    doc = {
+        "workload": "kda_chunk_bwd B=1 T=8192 H=96 d=128, bf16 q/k/v, fp32 gates, dL/do and dL/dS_T given, "
+                    "one-window workspace (every chunk's values kept)",
+        "command": "python -m gated_delta_rule_amd.traffic bwd (per pass: rocprofv3 --pmc "
+                   "<FETCH_SIZE|WRITE_SIZE> -d <dir> -o run --output-format csv -- python -u -m "
+                   "gated_delta_rule_amd.traffic target backward)",
+        "kernels": kernels,
+        "copy_calibration": calibration_doc(cal),
+        "kernel_sources_sha256_16": sources_hash("backward"),
+    }
+    path = profile_path("backward", profiles_dir)
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    print(f"backward -> {path}", flush=True)
+
+
+def collect(out, profiles_dir):
+    os.makedirs(out, exist_ok=True)
+    os.makedirs(profiles_dir, exist_ok=True)
+    cal = calibrate(out)
     for kind in ("prefill", "decode"):
         frag = TARGETS[kind][0]
         rec = {}
@@ -475,9 +552,7 @@ def collect(out, profiles_dir):
                        "<FETCH_SIZE|WRITE_SIZE> -d <dir> -o run --output-format csv -- python -u -m "
                        f"gated_delta_rule_amd.traffic target {kind})",
             "counters": rec,
-            "copy_calibration": {"kernel": "torch elementwise y = 1 * x, 1 GiB fp32 read + 1 GiB written",
-                                 **{k: {kk: vv for kk, vv in v.items() if kk != "kernel"}
-                                    for k, v in cal.items()}},
+            "copy_calibration": calibration_doc(cal),
             "hbm_bytes_per_launch": total,
             "kernel_sources_sha256_16": sources_hash(kind),
         }
@@ -523,7 +598,10 @@ def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("target")
-    t.add_argument("kind", choices=["copy", "prefill", "decode", "probe"])
+    t.add_argument("kind", choices=["copy", "prefill", "decode", "backward", "probe"])
+    bw = sub.add_parser("bwd")
+    bw.add_argument("--out", default=os.path.join(ROOT, "counters_out", "bwd"))
+    bw.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
     c = sub.add_parser("collect")
     c.add_argument("--out", default=os.path.join(ROOT, "counters_out", "traffic"),
                    help="directory for the raw counter output")
@@ -546,6 +624,9 @@ def main():
         return
     if args.cmd == "phases":
         collect_phases(os.path.abspath(args.out), os.path.abspath(args.profiles_dir), not args.parse_only)
+        return
+    if args.cmd == "bwd":
+        collect_bwd(os.path.abspath(args.out), os.path.abspath(args.profiles_dir))
         return
     if args.cmd == "target":
         run_target(args.kind)
