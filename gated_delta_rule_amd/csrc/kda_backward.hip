@@ -547,7 +547,6 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
         return make_float4(__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]),
                            __uint_as_float(u[3]));
     };
-    auto f4 = [](const float4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; };
     // token-major tiles of this chunk (rows past the sequence end read 0)
     const auto rdo = make_rsrc(p.dO + e0i, span);
     const int64_t e0s = ((c0 + ch.rs) * H + h) * BD;   // same rows in w, u, r

@@ -82,9 +82,11 @@ __device__ __forceinline__ uint32_t lds_addr(const __bf16* p) {
 
 }  // namespace
 
+// WANT_O: form o (Q+ S and M U); the passes that only need states or the
+// backward's per-chunk values skip Q+ S, q e^{g}, QX and M altogether.
 // STORE_H: also store, per chunk, the state at its start (h_states), V - K+ S
 // (r_out) and U (u_out), as chunk_fwd_kernel does for the backward pass.
-template <int NSCAN, bool STORE_H>
+template <int NSCAN, bool STORE_H, bool WANT_O>
 __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(PrefillParams p) {
     constexpr int WCOLS = 16;         // value columns per consumer wave
     constexpr int DVW = 4 * WCOLS;    // value columns per workgroup
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
                     load_tile(aK[0][tb], Xb + tb * 16 * LDR);
-                    aQ[0][tb] = load_tile_h(Qb + tb * 16 * LDR);
+                    if constexpr (WANT_O) aQ[0][tb] = load_tile_h(Qb + tb * 16 * LDR);
                     ev[0][tb] = *reinterpret_cast<const float4*>(e0 + tb * 16);
                 }
 #pragma unroll
@@ -313,20 +315,23 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
 #pragma unroll
                         for (int tb = 0; tb < 2; ++tb) {
                             load_tile(aK[cur ^ 1][tb], Xb + tb * 16 * LDR + (ks + 1) * 32);
-                            aQ[cur ^ 1][tb] = load_tile_h(Qb + tb * 16 * LDR + (ks + 1) * 32);
+                            if constexpr (WANT_O)
+                                aQ[cur ^ 1][tb] = load_tile_h(Qb + tb * 16 * LDR + (ks + 1) * 32);
                             ev[cur ^ 1][tb] = *reinterpret_cast<const float4*>(e0 + (2 * ks + 2 + tb) * 16);
                         }
                     }
                     f16x8 bS16;
                     Fr bS;
                     {
-                        u32x4 w;
+                        if constexpr (WANT_O) {
+                            u32x4 w;
 #pragma unroll
-                        for (int i = 0; i < 2; ++i) {
-                            w[2 * i] = pack_h2(S[2 * ks + i][0], S[2 * ks + i][1]);
-                            w[2 * i + 1] = pack_h2(S[2 * ks + i][2], S[2 * ks + i][3]);
+                            for (int i = 0; i < 2; ++i) {
+                                w[2 * i] = pack_h2(S[2 * ks + i][0], S[2 * ks + i][1]);
+                                w[2 * i + 1] = pack_h2(S[2 * ks + i][2], S[2 * ks + i][3]);
+                            }
+                            bS16 = __builtin_bit_cast(f16x8, w);
                         }
-                        bS16 = __builtin_bit_cast(f16x8, w);
 #pragma unroll
                         for (int i = 0; i < 2; ++i) {
                             const float4 sc4 = ev[cur][i];
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb) {
                         mma(R[tb], aK[cur][tb], bS);
-                        O[tb] = mfma32h(aQ[cur][tb], bS16, O[tb]);
+                        if constexpr (WANT_O) O[tb] = mfma32h(aQ[cur][tb], bS16, O[tb]);
                     }
                     // keep the next slice's loads ahead of this slice's products
                     __builtin_amdgcn_sched_barrier(0);
@@ -379,10 +384,12 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 load_v(s + 1);
                 load_beta(s + 1, pb);
                 Fr aM[2], aMl[2];
+                if constexpr (WANT_O) {
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    load_tile(aM[tb], sMh[b2] + (tb * 16 + ln) * LDMB + g * 4);
-                    load_tile(aMl[tb], sMl[b2] + (tb * 16 + ln) * LDMB + g * 4);
+                    for (int tb = 0; tb < 2; ++tb) {
+                        load_tile(aM[tb], sMh[b2] + (tb * 16 + ln) * LDMB + g * 4);
+                        load_tile(aMl[tb], sMl[b2] + (tb * 16 + ln) * LDMB + g * 4);
+                    }
                 }
                 // Block forward substitution of (I + L) U = R':
                 //   U0 = T00 R'0,  U1 = T11 (R'1 - L10 U0)
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                 }
                 // O = Q+ S + M U (skipped when o is not wanted); rows past the
                 // sequence end fall outside the store range.
-                if (p.o) {
+                if (WANT_O && p.o) {
                     const int64_t c0 = t0 + s * CH;
                     const auto ro = make_rsrc(p.o + ((size_t)c0 * H + h) * DK, span_bytes(n_valid(c0), 4));
 #pragma unroll
@@ -523,7 +530,7 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
         auto load_kq = [&](const ScanSrc& r, int tau) {
             const int el = (part * TPL + tau) * rowel + sc;
             xk[tau] = __builtin_amdgcn_raw_buffer_load_b32(r.k, el * 2, 0, 0);
-            xq[tau] = __builtin_amdgcn_raw_buffer_load_b32(r.q, el * 2, 0, 0);
+            if constexpr (WANT_O) xq[tau] = __builtin_amdgcn_raw_buffer_load_b32(r.q, el * 2, 0, 0);
         };
         auto load_la = [&](const ScanSrc& r, int tau) {
             const int el = (part * TPL + tau) * rowel + sc;
@@ -591,22 +598,36 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                     const float d0 = cs0[tau] + o0, d1 = cs1[tau] + o1;
                     const float fx0 = __builtin_amdgcn_exp2f(d0), fx1 = __builtin_amdgcn_exp2f(d1);
                     const float fy0 = __builtin_amdgcn_exp2f(-d0), fy1 = __builtin_amdgcn_exp2f(-d1);
-                    const float2 kf = bf2_to_f2(xk[tau]), qf = bf2_to_f2(xq[tau]);
-                    load_kq(nx, tau);
-                    const float X0 = kf.x * fx0, X1 = kf.y * fx1;
-                    const float Q0 = qf.x * fx0, Q1 = qf.y * fx1;
-                    const float Y0 = kf.x * fy0, Y1 = kf.y * fy1;
-                    const uint32_t qh = f2_to_bf2(Q0, Q1);
-                    const uint32_t yh = f2_to_bf2(Y0, Y1);
-                    const float2 qhf = bf2_to_f2(qh), yhf = bf2_to_f2(yh);
-                    const uint32_t ro = tau * LDR * 2;
-                    st(aX + ro, f2_to_bf2(X0, X1));
-                    st(aQ + ro, qh);
-                    st(aQl + ro, f2_to_bf2(Q0 - qhf.x, Q1 - qhf.y));
-                    st(aY + ro, yh);
-                    st(aYl + ro, f2_to_bf2(Y0 - yhf.x, Y1 - yhf.y));
-                    // q e^{g} = QX e^{E0} in fp16 (at most |q|)
-                    st(aQp + ro, pack_h2(Q0 * ee0, Q1 * ee1));
+                    if constexpr (WANT_O) {
+                        const float2 kf = bf2_to_f2(xk[tau]), qf = bf2_to_f2(xq[tau]);
+                        load_kq(nx, tau);
+                        const float X0 = kf.x * fx0, X1 = kf.y * fx1;
+                        const float Q0 = qf.x * fx0, Q1 = qf.y * fx1;
+                        const float Y0 = kf.x * fy0, Y1 = kf.y * fy1;
+                        const uint32_t qh = f2_to_bf2(Q0, Q1);
+                        const uint32_t yh = f2_to_bf2(Y0, Y1);
+                        const float2 qhf = bf2_to_f2(qh), yhf = bf2_to_f2(yh);
+                        const uint32_t ro = tau * LDR * 2;
+                        st(aX + ro, f2_to_bf2(X0, X1));
+                        st(aQ + ro, qh);
+                        st(aQl + ro, f2_to_bf2(Q0 - qhf.x, Q1 - qhf.y));
+                        st(aY + ro, yh);
+                        st(aYl + ro, f2_to_bf2(Y0 - yhf.x, Y1 - yhf.y));
+                        // q e^{g} = QX e^{E0} in fp16 (at most |q|)
+                        st(aQp + ro, pack_h2(Q0 * ee0, Q1 * ee1));
+                    } else {
+                        // k only: X, Y (hi, lo)
+                        const float2 kf = bf2_to_f2(xk[tau]);
+                        load_kq(nx, tau);
+                        const float X0 = kf.x * fx0, X1 = kf.y * fx1;
+                        const float Y0 = kf.x * fy0, Y1 = kf.y * fy1;
+                        const uint32_t yh = f2_to_bf2(Y0, Y1);
+                        const float2 yhf = bf2_to_f2(yh);
+                        const uint32_t ro = tau * LDR * 2;
+                        st(aX + ro, f2_to_bf2(X0, X1));
+                        st(aY + ro, yh);
+                        st(aYl + ro, f2_to_bf2(Y0 - yhf.x, Y1 - yhf.y));
+                    }
                 }
                 b3 = b3 == 2 ? 0 : b3 + 1;
             }
@@ -655,8 +676,8 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
                     const f32x4 v = block(X, X, 16, Yh, Yh, 0, false);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Tb[(16 + g * 4 + r) * LDM + ln] = -pbp[1][r] * v[r];
-                    store_m(Mh, Ml, block(QX, QXl, 0, Yh, Yl, 0, true), 0, 0, true);
-                } else {
+                    if constexpr (WANT_O) store_m(Mh, Ml, block(QX, QXl, 0, Yh, Yl, 0, true), 0, 0, true);
+                } else if constexpr (WANT_O) {
                     f32x4 m10, m11;
                     block2(QX, QXl, 16, Yh, Yl, 0, 16, m10, m11);
                     store_m(Mh, Ml, m10, 16, 0, false);
@@ -675,10 +696,15 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
 hipError_t launch_chunk_fwd_pipe(const PrefillParams& p, hipStream_t stream) {
     const int64_t groups = ((int64_t)p.n_units + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * p.n_slices)), block(64 * (8 + KDA_PIPE_NSCAN));
+    // the per-chunk outputs are only kept for the backward pass, which takes
+    // no o (the launch is refused if both are asked for)
+    if (p.h_states && p.o) return hipErrorInvalidValue;
     if (p.h_states)
-        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, true, false>), grid, block, 0, stream, p);
+    else if (p.o)
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false, true>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -86,7 +86,7 @@ TARGETS = {
                   "kda_abi.hip")),
 }
 # the backward's kernels, in launch order (symbol fragment, what it is)
-BWD_KERNELS = (("chunk_fwd_pipe_kernel<4, true>", "forward keeping chunk states, V - K+S and U"),
+BWD_KERNELS = (("chunk_fwd_pipe_kernel<4, true", "forward keeping chunk states, V - K+S and U"),
                ("bwd_tmp_kernel", "chunk matrices"),
                ("bwd_scan_kernel", "state-gradient walk"),
                ("bwd_grad_kernel", "per-chunk gradients"))
@@ -478,12 +478,12 @@ def kib_per_dispatch(per, fragment):
     return sum(vals) / len(vals), len(vals)
 
 
-def calibrate(out):
+def calibrate(out, run=True):
     """FETCH_SIZE and WRITE_SIZE of the plain copy, as counter KiB per byte moved."""
     copy_bytes = COPY_ELEMS * 4
     cal = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        per = counter_pass("copy", counter, out)
+        per = counter_pass("copy", counter, out, run)
         # the copy kernel is the one launched most often in its process
         names = [name for (_, name) in per]
         big = max(set(names), key=names.count)
@@ -499,11 +499,11 @@ def calibration_doc(cal):
             **{k: {kk: vv for kk, vv in v.items() if kk != "kernel"} for k, v in cal.items()}}
 
 
-def collect_bwd(out, profiles_dir):
+def collect_bwd(out, profiles_dir, run=True):
     os.makedirs(out, exist_ok=True)
     os.makedirs(profiles_dir, exist_ok=True)
-    cal = calibrate(out)
-    passes = {c: counter_pass("backward", c, out) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    cal = calibrate(out, run)
+    passes = {c: counter_pass("backward", c, out, run) for c in ("FETCH_SIZE", "WRITE_SIZE")}
     kernels = []
     for frag, what in BWD_KERNELS:
         rec = {"kernel": frag, "pass": what}
@@ -602,6 +602,8 @@ def main():
     bw = sub.add_parser("bwd")
     bw.add_argument("--out", default=os.path.join(ROOT, "counters_out", "bwd"))
     bw.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"))
+    bw.add_argument("--parse-only", action="store_true",
+                    help="summarise the counter output already under --out")
     c = sub.add_parser("collect")
     c.add_argument("--out", default=os.path.join(ROOT, "counters_out", "traffic"),
                    help="directory for the raw counter output")
@@ -626,7 +628,7 @@ def main():
         collect_phases(os.path.abspath(args.out), os.path.abspath(args.profiles_dir), not args.parse_only)
         return
     if args.cmd == "bwd":
-        collect_bwd(os.path.abspath(args.out), os.path.abspath(args.profiles_dir))
+        collect_bwd(os.path.abspath(args.out), os.path.abspath(args.profiles_dir), not args.parse_only)
         return
     if args.cmd == "target":
         run_target(args.kind)
