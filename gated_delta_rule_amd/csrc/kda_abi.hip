@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_launch.h"
 
@@ -49,6 +51,62 @@ Split split_for(int64_t n_seqs, int64_t T, int64_t H) {
     if (sp.P < 2) sp = Split{1, T};
     return sp;
 }
+
+// A second stream per device (default priority, not synchronising with the
+// null stream) on which the backward's chunk-matrix pass runs beside the
+// forward pass it does not depend on, and the two events that order it
+// against the caller's stream.  Created on first use and kept until the
+// process ends (events are never destroyed while a wait may still refer to
+// them); a call holds the device's lock while it enqueues, so calls from
+// several host threads cannot interleave their records.
+constexpr int kMaxDevices = 64;
+struct Side {
+    std::mutex mu;
+    bool tried = false;
+    hipStream_t stream = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+};
+Side* side_for(int dev) {
+    static Side sides[kMaxDevices];
+    return dev >= 0 && dev < kMaxDevices ? &sides[dev] : nullptr;
+}
+
+// Fork / join of side-stream passes: fork() makes the side stream wait for
+// everything enqueued on `main` so far and returns it; join() makes `main`
+// wait for what was enqueued on the side stream since.  Without a side
+// stream both are no-ops and the passes run on `main` in order.
+struct Fork {
+    hipStream_t main;
+    Side* sd = nullptr;
+    std::unique_lock<std::mutex> lock;
+    bool ok = true;
+    explicit Fork(hipStream_t s) : main(s) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return;
+        Side* c = side_for(dev);
+        if (!c) return;
+        lock = std::unique_lock<std::mutex>(c->mu);
+        if (!c->tried) {
+            c->tried = true;
+            if (hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking) != hipSuccess ||
+                hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess)
+                c->stream = nullptr;   // (a partly created set is simply not used)
+        }
+        if (c->stream) sd = c;
+    }
+    hipStream_t fork() {
+        if (!sd) return main;
+        if (hipEventRecord(sd->ev_fork, main) != hipSuccess || hipStreamWaitEvent(sd->stream, sd->ev_fork, 0) != hipSuccess)
+            ok = false;
+        return sd->stream;
+    }
+    void join() {
+        if (!sd) return;
+        if (hipEventRecord(sd->ev_join, sd->stream) != hipSuccess || hipStreamWaitEvent(main, sd->ev_join, 0) != hipSuccess)
+            ok = false;
+    }
+};
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -659,8 +717,12 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
         p.h_states = ws + L.h;
         p.r_out = ws + L.r;
         p.u_out = ws + L.u;
+        Fork fk(stream);
+        if (kda::launch_chunk_bwd_tmp(b, bf16_in, fk.fork()) != hipSuccess) return KDA_ERR_HIP;
         if (kda::launch_chunk_fwd(p, bf16_in, wcols, false, stream) != hipSuccess) return KDA_ERR_HIP;
-        return kda::launch_chunk_bwd(b, bf16_in, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+        fk.join();
+        if (!fk.ok) return KDA_ERR_HIP;
+        return kda::launch_chunk_bwd_walk_grad(b, bf16_in, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     // Equal lengths, windows of W chunks.  The states at the window starts
     // come first (forward passes without per-chunk outputs, window by
@@ -672,6 +734,18 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     const int nw = (int)L.n_win;   // <= kMaxBwdWindows
     auto ckpt = [&](int w) -> float* { return w == 0 ? nullptr : ws + L.ckpt + (int64_t)(w - 1) * st_el; };
     p.seg_len = win_len;
+    float* carry = nw > 1 ? ws + L.carry : nullptr;
+    b.win_len = win_len;
+    // The chunk matrices of a window read only the inputs: each runs on the
+    // side stream beside the forward pass(es) before its walk, once the
+    // previous window's gradients (which read the same workspace) are done.
+    Fork fk(stream);
+    auto fork_tmp = [&](int w) -> bool {
+        kda::BwdParams bw = b;
+        bw.win_idx = w;
+        return kda::launch_chunk_bwd_tmp(bw, bf16_in, fk.fork()) == hipSuccess;
+    };
+    if (nw > 0 && !fork_tmp(nw - 1)) return KDA_ERR_HIP;
     for (int w = 0; w + 1 < nw; ++w) {
         kda::PrefillParams pw = p;
         pw.seg_sel = w;
@@ -679,9 +753,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
         pw.S_T = ckpt(w + 1);
         if (kda::launch_chunk_fwd(pw, bf16_in, wcols, false, stream) != hipSuccess) return KDA_ERR_HIP;
     }
-    float* carry = nw > 1 ? ws + L.carry : nullptr;
-    b.win_len = win_len;
     for (int w = nw - 1; w >= 0; --w) {
+        if (w < nw - 1 && !fork_tmp(w)) return KDA_ERR_HIP;
         kda::PrefillParams pw = p;
         pw.seg_sel = w;
         pw.S0 = w == 0 ? S0 : ckpt(w);
@@ -689,13 +762,14 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
         pw.r_out = ws + L.r;
         pw.u_out = ws + L.u;
         if (kda::launch_chunk_fwd(pw, bf16_in, wcols, false, stream) != hipSuccess) return KDA_ERR_HIP;
+        fk.join();
         kda::BwdParams bw = b;
         bw.win_idx = w;
         bw.dS_T = w == nw - 1 ? grad_S_T : carry;
         bw.dS0 = w == 0 ? grad_S0 : carry;
-        if (kda::launch_chunk_bwd(bw, bf16_in, stream) != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_chunk_bwd_walk_grad(bw, bf16_in, stream) != hipSuccess) return KDA_ERR_HIP;
     }
-    return KDA_OK;
+    return fk.ok ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // extern "C"

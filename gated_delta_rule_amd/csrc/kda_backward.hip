@@ -814,13 +814,18 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
         p.dbeta[(c0 + tid) * H + h] = ((sDb[0][tid] + sDb[1][tid]) + (sDb[2][tid] + sDb[3][tid])) + sDb[4][tid];
 }
 
-hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream) {
+hipError_t launch_chunk_bwd_tmp(const BwdParams& p, bool bf16_in, hipStream_t stream) {
     const int64_t chunks = p.slots * p.H;
-    const int64_t units = (int64_t)p.n_seqs * p.H;
     if (chunks > 0) {
         if (bf16_in) hipLaunchKernelGGL(bwd_tmp_kernel<__bf16>, dim3((unsigned)chunks), dim3(256), 0, stream, p);
         else hipLaunchKernelGGL(bwd_tmp_kernel<float>, dim3((unsigned)chunks), dim3(256), 0, stream, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd_walk_grad(const BwdParams& p, bool bf16_in, hipStream_t stream) {
+    const int64_t chunks = p.slots * p.H;
+    const int64_t units = (int64_t)p.n_seqs * p.H;
     if (units > 0) {
         const dim3 grid((unsigned)(((units + 7) / 8) * 8 * 2));
         if (bf16_in) hipLaunchKernelGGL(bwd_scan_kernel<__bf16>, grid, dim3(512), 0, stream, p);
@@ -831,6 +836,11 @@ hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream
         else hipLaunchKernelGGL(bwd_grad_kernel<float>, dim3((unsigned)chunks), dim3(256), 0, stream, p);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream) {
+    const hipError_t e = launch_chunk_bwd_tmp(p, bf16_in, stream);
+    return e != hipSuccess ? e : launch_chunk_bwd_walk_grad(p, bf16_in, stream);
 }
 
 }  // namespace kda

@@ -142,5 +142,9 @@ struct BwdParams {
     int32_t n_seqs, H;
 };
 hipError_t launch_chunk_bwd(const BwdParams& p, bool bf16_in, hipStream_t stream);
+// The same passes split at the point where they need the forward pass: the
+// chunk matrices read only the inputs, so they may run beside it.
+hipError_t launch_chunk_bwd_tmp(const BwdParams& p, bool bf16_in, hipStream_t stream);
+hipError_t launch_chunk_bwd_walk_grad(const BwdParams& p, bool bf16_in, hipStream_t stream);
 
 }  // namespace kda

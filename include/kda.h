@@ -27,9 +27,12 @@
  *     memory accesses.
  *   - All tensor pointers are DEVICE pointers owned by the caller, which
  *     allocates every buffer (including the workspace).  The library
- *     allocates nothing, keeps no mutable global state (apart from the
- *     scratch array of kda_chunk_fwd_noalloc), never synchronises the host,
- *     and enqueues its kernels on `stream` (0 = the null stream).
+ *     allocates no memory, keeps no mutable global state (apart from the
+ *     scratch array of kda_chunk_fwd_noalloc and the per-device second
+ *     stream of kda_chunk_bwd), never synchronises the host, and enqueues
+ *     its kernels on `stream` (0 = the null stream); kda_chunk_bwd also
+ *     runs one pass on its second stream, ordered against `stream` by
+ *     events (see there).
  *   - Every argument is validated before anything is enqueued; on error the
  *     call returns a non-zero kda_status and has no effect.  Faults raised by
  *     the device asynchronously surface at the caller's next synchronisation.
@@ -345,6 +348,17 @@ size_t kda_chunk_bwd_workspace_bytes_window(int32_t n_seqs, int64_t T, int32_t H
  * the state-gradient walk and of the per-chunk gradients use split (hi + lo)
  * bf16 operands, and the states come from the same kernel as kda_chunk_fwd
  * (its split-bf16 rounding).  Deterministic: no atomics.
+ * Streams: the chunk-matrix pass reads only the inputs, so it runs beside
+ * the forward pass on a second stream of the current device (created by the
+ * library on the first call, default priority, never destroyed).  Events
+ * order it: each such pass starts after everything enqueued on `stream`
+ * before it (for the first, before the call), and the walk that reads it
+ * waits for it, so all of the call's work is complete before anything
+ * enqueued on `stream` after the call runs.  Under HIP graph capture of
+ * `stream` the second stream joins the capture the same way.  If the
+ * second stream cannot be created every pass runs on `stream`.  Calls on
+ * one device serialise their enqueueing on a lock; their work on the
+ * second stream runs in call order.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
                   const float* log_alpha, const float* beta, const float* S0,

@@ -5,7 +5,10 @@
 // so every validation branch and every launch plan (packed batches, equal
 // lengths, the sequence-parallel path, decode, recurrent, layer steps,
 // backward) runs under the sanitizers without a GPU.  The pointers are fake
-// device addresses that are never dereferenced.
+// device addresses that are never dereferenced.  The few HIP runtime calls
+// the ABI makes itself (the backward's second stream and its events) are
+// stubbed too and logged beside the launches, so the fork / join order of
+// the backward's passes is checked as well.
 #include <stdint.h>
 #include <stdio.h>
 
@@ -17,15 +20,24 @@ int n_launch = 0, n_merge = 0, n_dual = 0, last_slices = 0, last_units = 0;
 int fails = 0;
 // forward and backward launches in order, for the backward's window plan
 struct Rec {
-    char kind;                 // 'f' forward, 'b' backward passes
+    char kind;                 // 'f' forward, 't' chunk matrices, 'g' walk + gradients,
+                               // 'r' event record, 'w' stream waits for event
     int seg_sel, win_idx;
     bool stores;               // forward keeps per-chunk values
     const float *S0, *S_T, *dS_T;
     float* dS0;
     int64_t seg_len, win_len, slots;
+    hipStream_t stream;        // stream of the launch / record / wait
+    hipEvent_t event;          // 'r', 'w'
 };
-Rec recs[256];
+Rec recs[512];
 int n_recs = 0;
+void rec(const Rec& r) {
+    if (n_recs < 512) recs[n_recs++] = r;
+}
+// the stubbed runtime's objects: fake handles, never dereferenced
+hipStream_t const kSide = (hipStream_t)(uintptr_t)0x5100;
+int n_events = 0, n_streams = 0;
 #define CHECK(c)                                                               \
     do {                                                                       \
         if (!(c)) {                                                            \
@@ -37,11 +49,10 @@ int n_recs = 0;
 
 namespace kda {
 hipError_t launch_chunk_fwd_pipe(const PrefillParams&, hipStream_t) { return hipSuccess; }
-hipError_t launch_chunk_fwd(const PrefillParams& p, bool, int wcols, bool, hipStream_t) {
+hipError_t launch_chunk_fwd(const PrefillParams& p, bool, int wcols, bool, hipStream_t stream) {
     ++n_launch;
-    if (n_recs < 256)
-        recs[n_recs++] = Rec{'f', p.seg_sel, 0, p.h_states != nullptr, p.S0, p.S_T, nullptr, nullptr,
-                             p.seg_len, 0, 0};
+    rec(Rec{'f', p.seg_sel, 0, p.h_states != nullptr, p.S0, p.S_T, nullptr, nullptr, p.seg_len, 0, 0,
+            stream, nullptr});
     CHECK(p.seg_sel < 0 || (!p.cu && p.seg_len % 32 == 0 && p.seg_len > 0));
     CHECK(!p.h_states || (p.r_out && p.u_out && !p.o));
     last_slices = p.n_slices;
@@ -82,16 +93,48 @@ hipError_t launch_epilogue(const float*, const float*, const float*, float*, int
     CHECK(items >= 1);
     return hipSuccess;
 }
-hipError_t launch_chunk_bwd(const BwdParams& p, bool, hipStream_t) {
-    ++n_launch;
+static void bwd_checks(const BwdParams& p) {
     CHECK(p.slots >= 1);
     CHECK(p.win_len == 0 || (!p.cu && p.win_len % 32 == 0 && p.slots * 32 == p.n_seqs * p.win_len));
-    if (n_recs < 256)
-        recs[n_recs++] = Rec{'b', -1, p.win_idx, false, nullptr, nullptr, p.dS_T, p.dS0, 0,
-                             p.win_len, p.slots};
+}
+hipError_t launch_chunk_bwd_tmp(const BwdParams& p, bool, hipStream_t stream) {
+    ++n_launch;
+    bwd_checks(p);
+    rec(Rec{'t', -1, p.win_idx, false, nullptr, nullptr, p.dS_T, p.dS0, 0, p.win_len, p.slots, stream,
+            nullptr});
+    return hipSuccess;
+}
+hipError_t launch_chunk_bwd_walk_grad(const BwdParams& p, bool, hipStream_t stream) {
+    ++n_launch;
+    bwd_checks(p);
+    rec(Rec{'g', -1, p.win_idx, false, nullptr, nullptr, p.dS_T, p.dS0, 0, p.win_len, p.slots, stream,
+            nullptr});
     return hipSuccess;
 }
 }  // namespace kda
+
+// HIP runtime calls of the ABI itself
+hipError_t hipGetDevice(int* d) {
+    *d = 0;
+    return hipSuccess;
+}
+hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int) {
+    ++n_streams;
+    *s = kSide;
+    return hipSuccess;
+}
+hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) {
+    *e = (hipEvent_t)(uintptr_t)(0xe000 + 16 * ++n_events);
+    return hipSuccess;
+}
+hipError_t hipEventRecord(hipEvent_t e, hipStream_t s) {
+    rec(Rec{'r', -1, -1, false, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, s, e});
+    return hipSuccess;
+}
+hipError_t hipStreamWaitEvent(hipStream_t s, hipEvent_t e, unsigned int) {
+    rec(Rec{'w', -1, -1, false, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, s, e});
+    return hipSuccess;
+}
 
 // 1 TiB apart, so no two of them overlap at these sizes
 static const void* P(int i) { return (const void*)(uintptr_t)((1ull << 44) + (uint64_t)i * (1ull << 40)); }
@@ -160,32 +203,70 @@ int main() {
     CHECK(kda_epilogue(F(0), F(1), F(2), 64, 4, 128, F(0), nullptr) == KDA_OK);
     CHECK(kda_epilogue(F(0), F(1), F(2), 64, 4, 128, F(1), nullptr) == KDA_ERR_ALIASING);
     // backward: equal lengths run in windows, the last first
+    // The launches of the last call, without the event records and waits,
+    // and a check that every chunk-matrix pass runs on the second stream
+    // after a fork from the caller's stream and is joined before the walk
+    // that reads it.
+    hipStream_t const kMain = (hipStream_t)(uintptr_t)0x3300;
+    auto launches = [&](Rec* out, int cap) {
+        int n = 0;
+        for (int i = 0; i < n_recs && n < cap; ++i)
+            if (recs[i].kind != 'r' && recs[i].kind != 'w') out[n++] = recs[i];
+        return n;
+    };
+    auto check_fork_join = [&]() {
+        hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+        bool side_waited = false;   // the side stream waits for the latest fork record
+        bool pending = false;       // a chunk-matrix pass not yet joined
+        for (int i = 0; i < n_recs; ++i) {
+            const Rec& r = recs[i];
+            if (r.kind == 'r' && r.stream == kMain) { fork_ev = r.event; side_waited = false; }
+            else if (r.kind == 'w' && r.stream == kSide) CHECK(side_waited = (r.event == fork_ev));
+            else if (r.kind == 'r' && r.stream == kSide) join_ev = r.event;
+            else if (r.kind == 'w' && r.stream == kMain) { CHECK(r.event == join_ev && join_ev); pending = false; }
+            else if (r.kind == 't') { CHECK(r.stream == kSide && side_waited); pending = true; }
+            else if (r.kind == 'g') { CHECK(r.stream == kMain && !pending); }
+            else if (r.kind == 'f') CHECK(r.stream == kMain);
+        }
+        CHECK(!pending);
+    };
     auto bwd_plan = [&](int n_seqs, int64_t T, size_t ws, const float* S0, const float* gST,
                         float* gS0, int expect_windows, int64_t expect_win_len) {
         n_recs = 0;
         CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), S0, nullptr, n_seqs, T, 96, 128,
                             128, F(20), gST, F(21), F(22), F(23), F(24), F(25), gS0, (void*)P(27), ws,
-                            nullptr) == KDA_OK);
+                            kMain) == KDA_OK);
+        check_fork_join();
+        Rec L[512];
+        const int n = launches(L, 512);
         const int K = expect_windows;
-        CHECK(n_recs == (K - 1) + 2 * K);
-        if (n_recs != (K - 1) + 2 * K) return;
+        // the last window's chunk matrices, the K - 1 window-start passes,
+        // then per window (last first) its chunk matrices (all but the
+        // first), the forward keeping values, the walk and gradients
+        CHECK(n == 1 + (K - 1) + 3 * K - 1);
+        if (n != 1 + (K - 1) + 3 * K - 1) return;
+        CHECK(L[0].kind == 't' && L[0].win_idx == K - 1);
         // the states at the window starts: forward over windows 0 .. K-2
         const float* prev_end = nullptr;
         for (int w = 0; w + 1 < K; ++w) {
-            const Rec& r = recs[w];
+            const Rec& r = L[1 + w];
             CHECK(r.kind == 'f' && r.seg_sel == w && !r.stores && r.S_T && r.seg_len == expect_win_len);
             CHECK(w == 0 ? r.S0 == S0 : r.S0 == prev_end);
             prev_end = r.S_T;
         }
-        // then per window, last first: forward keeping values, backward passes
         const float* carry = nullptr;
+        int at = K;
         for (int i = 0; i < K; ++i) {
             const int w = K - 1 - i;
-            const Rec& f = recs[K - 1 + 2 * i];
-            const Rec& b = recs[K + 2 * i];
+            if (i > 0) {
+                const Rec& t = L[at++];
+                CHECK(t.kind == 't' && t.win_idx == w && t.win_len == expect_win_len);
+            }
+            const Rec& f = L[at++];
+            const Rec& b = L[at++];
             CHECK(f.kind == 'f' && f.seg_sel == w && f.stores && f.seg_len == expect_win_len);
-            CHECK(w == 0 ? f.S0 == S0 : f.S0 == recs[w - 1].S_T);
-            CHECK(b.kind == 'b' && b.win_idx == w && b.win_len == expect_win_len);
+            CHECK(w == 0 ? f.S0 == S0 : f.S0 == L[w].S_T);
+            CHECK(b.kind == 'g' && b.win_idx == w && b.win_len == expect_win_len);
             CHECK(b.slots == n_seqs * expect_win_len / 32);
             CHECK(w == K - 1 ? b.dS_T == gST : b.dS_T == carry);
             if (w == 0) CHECK(b.dS0 == gS0);
@@ -217,13 +298,18 @@ int main() {
         const size_t wp = kda_chunk_bwd_workspace_bytes(4, 5000, 96, 128, 128, 1);
         CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(28), 4,
                             5000, 96, 128, 128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26),
-                            (void*)P(27), wp, nullptr) == KDA_OK);
-        CHECK(n_recs == 2 && recs[0].kind == 'f' && recs[0].seg_sel < 0 && recs[0].stores &&
-              recs[1].kind == 'b' && recs[1].win_len == 0 && recs[1].slots == 5000 / 32 + 4);
+                            (void*)P(27), wp, kMain) == KDA_OK);
+        check_fork_join();
+        Rec L[8];
+        CHECK(launches(L, 8) == 3 && L[0].kind == 't' && L[0].win_len == 0 && L[0].slots == 5000 / 32 + 4 &&
+              L[1].kind == 'f' && L[1].seg_sel < 0 && L[1].stores && L[2].kind == 'g' &&
+              L[2].win_len == 0 && L[2].slots == 5000 / 32 + 4);
         CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(28), 4,
                             5000, 96, 128, 128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26),
                             (void*)P(27), wp - 1, nullptr) == KDA_ERR_WORKSPACE);
     }
+    // one second stream and two events for the whole process
+    CHECK(n_streams == 1 && n_events == 2);
     for (int s = -1; s <= 9; ++s) CHECK(kda_status_str(s) != nullptr);
     CHECK(kda_abi_version() == KDA_ABI_VERSION);
     if (fails) {
