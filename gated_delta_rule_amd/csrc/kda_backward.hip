@@ -42,7 +42,8 @@
 //            buffer-loaded straight into registers one phase ahead.  Writes
 //            W and the gradient at every chunk end, and dS0.
 //   3. grad: one workgroup per (chunk, head), all chunks at once: streams
-//            rows of dO, W, U and of S, Sn into matrix-core operands, then
+//            rows of S, Sn (per wave) and of dO, W, U (staged once per
+//            workgroup in LDS) into matrix-core operands, then
 //            the products over the chunk's tokens, the elementwise chain
 //            rule and the in-chunk suffix sums of dg, all in registers.
 // With fp32 inputs the products run on the fp32 matrix cores
@@ -512,9 +513,9 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
 // (i0, kh) holds key column dk = 32 w + i0 and tokens t = crow(r, lane),
 // r = 0..15, both in the accumulators and in its per-element values (q, k,
 // decay sums), so the chain rule needs no data movement.  The products
-// over the value columns stream rows of dO, W, U (token i0) and of S, Sn
-// (key dk) from memory, 4 consecutive value columns per lane and load:
-// the k order pairs column 8 m + s (lanes 0-31) with 8 m + 4 + s.
+// over the value columns take, 32 columns per block, the rows of S and Sn
+// (key dk) straight from memory and the rows of dO, W and U (token i0) from
+// LDS, where the workgroup stages each block once for all four waves.
 template <typename InT>
 __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
     __shared__ float sPm[4][BC * LC];   // dM by value quarter
@@ -522,6 +523,8 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
     __shared__ float sdM[BC * LC], sdP[BC * LC];   // dM, dPm = -Diag(beta) dA'
     __shared__ float sDb[5][BC];
     __shared__ float sBeta[BC];
+    constexpr int LT = 36;   // row stride of the staged token rows
+    __shared__ __attribute__((aligned(16))) float sTok[2][3][BC * LT];   // dO, W, U rows of one block
 
     constexpr bool F32 = std::is_same<InT, float>::value;
     const int64_t m = blockIdx.x / p.H;
@@ -620,13 +623,42 @@ __global__ __launch_bounds__(256, 2) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) y[j] = x[8 * hf + j];
     };
+    // The dO, W and U rows of a block are the same for all four waves: the
+    // workgroup loads them once (thread: token tid / 8, columns 4 (tid % 8) ..)
+    // into LDS, double-buffered, the next block's loads in flight meanwhile.
+    const int st_row = tid >> 3, st_c = 4 * (tid & 7);
+    const int st_vo = st_row * rowb + st_c * 4;
+    float4 stg[3];
+    auto stage_load = [&](int mb) {
+        stg[0] = ld4(rdo, st_vo + 128 * mb);
+        stg[1] = ld4(rw, st_vo + 128 * mb);
+        stg[2] = ld4(ru, st_vo + 128 * mb);
+    };
+    stage_load(0);
     for (int mb = 0; mb < 4; ++mb) {
         float a_do[16], a_w[16], a_u[16], b_s[16], b_sn[16];
-        ld16(rdo, vo_tok + 128 * mb, a_do);
-        ld16(rw, vo_tok + 128 * mb, a_w);
-        ld16(ru, vo_tok + 128 * mb, a_u);
         ld16(rs_, vo_key + 128 * mb, b_s);
         ld16(rsn, vo_key + 128 * mb, b_sn);
+        {
+            float* buf = &sTok[mb & 1][0][0];
+#pragma unroll
+            for (int a = 0; a < 3; ++a)
+                *reinterpret_cast<float4*>(buf + a * (BC * LT) + st_row * LT + st_c) = stg[a];
+        }
+        if (mb < 3) stage_load(mb + 1);
+        lds_barrier();
+        {
+            const float* buf = &sTok[mb & 1][0][0] + i0 * LT + 16 * kh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 x0 = *reinterpret_cast<const float4*>(buf + 4 * i);
+                const float4 x1 = *reinterpret_cast<const float4*>(buf + BC * LT + 4 * i);
+                const float4 x2 = *reinterpret_cast<const float4*>(buf + 2 * BC * LT + 4 * i);
+                a_do[4 * i] = x0.x; a_do[4 * i + 1] = x0.y; a_do[4 * i + 2] = x0.z; a_do[4 * i + 3] = x0.w;
+                a_w[4 * i] = x1.x; a_w[4 * i + 1] = x1.y; a_w[4 * i + 2] = x1.z; a_w[4 * i + 3] = x1.w;
+                a_u[4 * i] = x2.x; a_u[4 * i + 1] = x2.y; a_u[4 * i + 2] = x2.z; a_u[4 * i + 3] = x2.w;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) rsum += b_s[j] * b_sn[j];
         if constexpr (F32) {
