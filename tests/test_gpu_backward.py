@@ -268,3 +268,60 @@ def test_bwd_window_workspace_sizes():
     torch.cuda.synchronize()
     for nm, x, y in zip(NAMES, g_small, g_one):
         assert torch.equal(x, y), nm
+
+
+def test_bwd_graph_capture_replays_bitwise():
+    """kda_chunk_bwd captured into a HIP graph replays to the eager result,
+    bitwise, three times with eager work and synchronisations between the
+    replays.  Its chunk-matrix passes fork onto the library's second stream
+    and join back, so the capture covers that stream too: an equal-length
+    batch in 64-token windows (five windows per sequence, five forks) and a
+    packed batch (one fork)."""
+    import ctypes
+    lib = kda.load_library()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+    for equal in (True, False):
+        lens = [300, 300] if equal else [300, 45, 0, 130]
+        w, a, S0, dO, dS, cu = inputs(W.workload(1).shrink(H=3), lens, 0.02, 1.0)
+        T, H, N = a["q"].shape[0], a["q"].shape[1], len(lens)
+        d = {n: torch.from_numpy(np.ascontiguousarray(a[n])).cuda() for n in a}
+        for n in ("q", "k", "v"):
+            d[n] = d[n].to(torch.bfloat16)
+        s0 = torch.from_numpy(S0).cuda()
+        go = torch.from_numpy(dO).cuda()
+        gst = torch.from_numpy(dS).cuda()
+        cu_dev = None if equal else torch.from_numpy(cu.astype(np.int32)).cuda()
+        Tc = 300 if equal else T   # tokens per sequence (equal) or in total (packed)
+        wsb = (lib.kda_chunk_bwd_workspace_bytes_window(N, Tc, H, 128, 128, 64) if equal
+               else lib.kda_chunk_bwd_workspace_bytes(N, Tc, H, 128, 128, 1))
+        assert wsb > 0
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        outs = [torch.empty_like(d["log_alpha"]) for _ in range(4)] + [torch.empty_like(d["beta"]),
+                                                                       torch.empty_like(s0)]
+
+        def call(stream_handle):
+            return lib.kda_chunk_bwd(vp(d["q"]), vp(d["k"]), vp(d["v"]), 0, vp(d["log_alpha"]),
+                                     vp(d["beta"]), vp(s0), vp(cu_dev), N, Tc, H, 128, 128, vp(go),
+                                     vp(gst), *[vp(o) for o in outs], vp(ws), wsb,
+                                     ctypes.c_void_p(stream_handle))
+
+        say(f"[bwd] graph capture ({'equal lengths, 5 windows' if equal else 'packed'}): eager")
+        assert call(torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        ref = [o.clone() for o in outs]
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        say("[bwd] graph capture: capture")
+        with torch.cuda.graph(g, stream=s):
+            rc = call(s.cuda_stream)
+        assert rc == 0
+        for rep in range(3):
+            for o in outs:
+                o.fill_(float("nan"))
+            ws.fill_(0xFF)
+            torch.cuda.synchronize()
+            say(f"[bwd] graph capture: replay {rep}")
+            g.replay()
+            torch.cuda.synchronize()
+            for o, r in zip(outs, ref):
+                assert torch.equal(o, r)
