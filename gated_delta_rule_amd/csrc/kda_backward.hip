@@ -444,7 +444,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
         // gradient at the end of this chunk
         float* dsn = p.dsn + sl * (BD * BD);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dsn[(size_t)(row0 + crow(r, lane)) * BD + col] = dS[r];
+        for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(dS[r], &dsn[(size_t)(row0 + crow(r, lane)) * BD + col]);
 
         // ---- phase 1 (the k order of every product below pairs row / token
         // crow(r, lane) of the two lane halves; r = 4 m4 + s)
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(BwdParams p) {
             for (int r = 0; r < 16; ++r) {
                 const int t = crow(r, lane);
                 sW[sw][t * LC + i0] = W[r];
-                if (t < nv) p.w[((size_t)(c0 + wrs + t) * H + h) * BD + col] = W[r];
+                if (t < nv) __builtin_nontemporal_store(W[r], &p.w[((size_t)(c0 + wrs + t) * H + h) * BD + col]);
             }
             if (j > 0) load_t(j - 1);
         }
