@@ -30,8 +30,9 @@
  *     allocates no memory, keeps no mutable global state (apart from the
  *     scratch array of kda_chunk_fwd_noalloc and the per-device second
  *     stream of kda_chunk_bwd), never synchronises the host, and enqueues
- *     its kernels on `stream` (0 = the null stream); kda_chunk_bwd also
- *     runs one pass on its second stream, ordered against `stream` by
+ *     its kernels on `stream` (0 = the null stream), which must belong to
+ *     the current device (the one every pointer refers to); kda_chunk_bwd
+ *     also runs one pass on its second stream, ordered against `stream` by
  *     events (see there).
  *   - Every argument is validated before anything is enqueued; on error the
  *     call returns a non-zero kda_status and has no effect.  Faults raised by
