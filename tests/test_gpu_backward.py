@@ -325,3 +325,64 @@ def test_bwd_graph_capture_replays_bitwise():
             torch.cuda.synchronize()
             for o, r in zip(outs, ref):
                 assert torch.equal(o, r)
+
+
+def test_bwd_concurrent_calls_from_two_threads_bitwise():
+    """Two host threads call kda_chunk_bwd at the same time on two streams
+    with their own inputs, outputs and workspaces (the calls share the
+    library's second stream and its events, and enqueue under one lock):
+    every result equals the same call made alone, bitwise."""
+    import ctypes
+    import threading
+    lib = kda.load_library()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+    jobs = []
+    for seed_h, lens in ((3, [300, 300]), (2, [200, 200, 200])):
+        w, a, S0, dO, dS, cu = inputs(W.workload(1).shrink(H=seed_h), lens, 0.02, 1.0)
+        T, H, N = a["q"].shape[0], a["q"].shape[1], len(lens)
+        d = {n: torch.from_numpy(np.ascontiguousarray(a[n])).cuda() for n in a}
+        for n in ("q", "k", "v"):
+            d[n] = d[n].to(torch.bfloat16)
+        job = dict(d=d, s0=torch.from_numpy(S0).cuda(), go=torch.from_numpy(dO).cuda(),
+                   gst=torch.from_numpy(dS).cuda(), N=N, Tc=lens[0], H=H)
+        job["wsb"] = lib.kda_chunk_bwd_workspace_bytes_window(N, lens[0], H, 128, 128, 64)
+        job["ws"] = torch.empty(job["wsb"], dtype=torch.uint8, device="cuda")
+        job["outs"] = [torch.empty_like(d["log_alpha"]) for _ in range(4)] + [
+            torch.empty_like(d["beta"]), torch.empty_like(job["s0"])]
+        job["stream"] = torch.cuda.Stream()
+        jobs.append(job)
+
+    def call(job):
+        d = job["d"]
+        return lib.kda_chunk_bwd(vp(d["q"]), vp(d["k"]), vp(d["v"]), 0, vp(d["log_alpha"]), vp(d["beta"]),
+                                 vp(job["s0"]), None, job["N"], job["Tc"], job["H"], 128, 128, vp(job["go"]),
+                                 vp(job["gst"]), *[vp(o) for o in job["outs"]], vp(job["ws"]), job["wsb"],
+                                 ctypes.c_void_p(job["stream"].cuda_stream))
+
+    say("[bwd] two threads: each call alone")
+    ref = []
+    for job in jobs:
+        assert call(job) == 0
+        torch.cuda.synchronize()
+        ref.append([o.clone() for o in job["outs"]])
+    for rep in range(3):
+        for job in jobs:
+            for o in job["outs"]:
+                o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        rcs = [None, None]
+
+        def worker(i):
+            rcs[i] = [call(jobs[i]) for _ in range(2)]
+
+        say(f"[bwd] two threads: round {rep}")
+        th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+        torch.cuda.synchronize()
+        assert rcs == [[0, 0], [0, 0]]
+        for job, r in zip(jobs, ref):
+            for o, x in zip(job["outs"], r):
+                assert torch.equal(o, x)
