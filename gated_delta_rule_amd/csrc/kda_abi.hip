@@ -74,12 +74,17 @@ Side* side_for(int dev) {
 // Fork / join of side-stream passes: fork() makes the side stream wait for
 // everything enqueued on `main` so far and returns it; join() makes `main`
 // wait for what was enqueued on the side stream since.  Without a side
-// stream both are no-ops and the passes run on `main` in order.
+// stream both are no-ops and the passes run on `main` in order.  A fork
+// still open when the call returns (an early error return after a failed
+// launch) is joined by the destructor, so work already on the side stream
+// is ordered before whatever the caller enqueues on `main` next (freeing
+// the workspace, say).
 struct Fork {
     hipStream_t main;
     Side* sd = nullptr;
     std::unique_lock<std::mutex> lock;
     bool ok = true;
+    bool pending = false;   // side-stream work not yet joined
     explicit Fork(hipStream_t s) : main(s) {
         int dev = -1;
         if (hipGetDevice(&dev) != hipSuccess) return;
@@ -99,13 +104,20 @@ struct Fork {
         if (!sd) return main;
         if (hipEventRecord(sd->ev_fork, main) != hipSuccess || hipStreamWaitEvent(sd->stream, sd->ev_fork, 0) != hipSuccess)
             ok = false;
+        pending = true;
         return sd->stream;
     }
     void join() {
         if (!sd) return;
+        pending = false;
         if (hipEventRecord(sd->ev_join, sd->stream) != hipSuccess || hipStreamWaitEvent(main, sd->ev_join, 0) != hipSuccess)
             ok = false;
     }
+    ~Fork() {
+        if (pending) join();
+    }
+    Fork(const Fork&) = delete;
+    Fork& operator=(const Fork&) = delete;
 };
 
 struct Range {

@@ -359,7 +359,10 @@ size_t kda_chunk_bwd_workspace_bytes_window(int32_t n_seqs, int64_t T, int32_t H
  * `stream` the second stream joins the capture the same way.  If the
  * second stream cannot be created every pass runs on `stream`.  Calls on
  * one device serialise their enqueueing on a lock; their work on the
- * second stream runs in call order.
+ * second stream runs in call order.  A call that fails with KDA_ERR_HIP
+ * after work reached the second stream still makes `stream` wait for that
+ * work before it returns, so the buffers may be released in stream order
+ * as after a successful call (their contents are then unspecified).
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
                   const float* log_alpha, const float* beta, const float* S0,

@@ -18,6 +18,7 @@
 namespace {
 int n_launch = 0, n_merge = 0, n_dual = 0, last_slices = 0, last_units = 0;
 int fails = 0;
+int fail_fwd_in = -1;   // > 0: the forward launch that many calls from now fails
 // forward and backward launches in order, for the backward's window plan
 struct Rec {
     char kind;                 // 'f' forward, 't' chunk matrices, 'g' walk + gradients,
@@ -53,6 +54,7 @@ hipError_t launch_chunk_fwd(const PrefillParams& p, bool, int wcols, bool, hipSt
     ++n_launch;
     rec(Rec{'f', p.seg_sel, 0, p.h_states != nullptr, p.S0, p.S_T, nullptr, nullptr, p.seg_len, 0, 0,
             stream, nullptr});
+    if (fail_fwd_in > 0 && --fail_fwd_in == 0) return hipErrorInvalidValue;
     CHECK(p.seg_sel < 0 || (!p.cu && p.seg_len % 32 == 0 && p.seg_len > 0));
     CHECK(!p.h_states || (p.r_out && p.u_out && !p.o));
     last_slices = p.n_slices;
@@ -307,6 +309,30 @@ int main() {
         CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(28), 4,
                             5000, 96, 128, 128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26),
                             (void*)P(27), wp - 1, nullptr) == KDA_ERR_WORKSPACE);
+        // a forward launch that fails while a chunk-matrix pass is on the
+        // second stream: the call reports KDA_ERR_HIP and joins that stream
+        // back into the caller's before it returns (windowed: the first
+        // window-start pass, and the storing forward of the third window
+        // from the end; packed: its one forward)
+        for (int at : {1, 5}) {
+            n_recs = 0;
+            fail_fwd_in = at;
+            CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, nullptr, 1, 8192, 96,
+                                128, 128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26),
+                                (void*)P(27), ws, kMain) == KDA_ERR_HIP);
+            CHECK(fail_fwd_in == 0 && n_recs > 0 && recs[n_recs - 1].kind == 'w' &&
+                  recs[n_recs - 1].stream == kMain);
+            check_fork_join();
+        }
+        n_recs = 0;
+        fail_fwd_in = 1;
+        CHECK(kda_chunk_bwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(28), 4,
+                            5000, 96, 128, 128, F(20), nullptr, F(21), F(22), F(23), F(24), F(25), F(26),
+                            (void*)P(27), wp, kMain) == KDA_ERR_HIP);
+        CHECK(fail_fwd_in == 0 && n_recs > 0 && recs[n_recs - 1].kind == 'w' &&
+              recs[n_recs - 1].stream == kMain);
+        check_fork_join();
+        fail_fwd_in = -1;
     }
     // one second stream and two events for the whole process
     CHECK(n_streams == 1 && n_events == 2);
