@@ -24,32 +24,48 @@ constexpr int32_t kMaxRecurrent = 64;      // tokens per request on the recurren
 // [32][32] each, K_end^T, Q+^T, -(B_beta K+)^T [128][32] each, e^{g_C} [128]
 constexpr int64_t kBwdChunkElems = 3 * 32 * 32 + 3 * 128 * 32 + 128;
 
-// Sequence-parallel split of an equal-length batch: segments per sequence
-// (1 = none) and tokens per segment (a multiple of the chunk).  Used when
-// the (sequence, head) chains, at two workgroups each, cover at most half
-// the compute units; the segments then fill the compute units with one
-// (512-thread, all-columns) workgroup per chain, which ran workload 3
-// (1M tokens, 16 heads) in 23.0 ms against 34.4 ms for half as many
-// segments at two workgroups each and 23.1 ms for twice as many.
+// Sequence-parallel split of an equal-length batch.  Every sequence is cut
+// into P segments.  Segment 0 starts from the known initial state: it runs
+// once, writing o, on the two-slice kernel (two workgroups per (sequence,
+// head)), beside the dual-chain pass over the middle segments 1 .. P-2 (one
+// workgroup each; zero start and identity start on the same tiles); the
+// merge then gives the incoming state of segments 1 .. P-1, which rerun from
+// it (one workgroup each).  The two passes hold units * P and units * (P - 1)
+// workgroups, within the 256 compute units.  Segment 0 is made longer than
+// the others so that it ends with the dual pass: with both running, its
+// chain steps through a chunk about 2.1 times as fast as a dual chain.  The
+// ratio (in sixteenths, per input type) is the one that ran the 1M-token,
+// 16-head shape fastest: 34 for bf16 (16.3 ms against 17.7 ms with equal
+// segments all through the dual pass; 30 gave 16.5, 40 gave 17.3), 32 for
+// fp32 (262,144 tokens: 9.45 ms against 10.17; 30 gave 9.56, 36 gave 9.98).
 struct Split {
-    int32_t P;
-    int64_t L;
+    int32_t P;       // segments per sequence (1: no split)
+    int64_t L;       // tokens of every segment after the first (the last shorter)
+    int64_t first;   // tokens of segment 0
 };
 
-Split split_for(int64_t n_seqs, int64_t T, int64_t H) {
-    Split sp{1, T};
+// Segments per sequence; the workspace depends on this count only.
+int32_t seg_count(int64_t n_seqs, int64_t T, int64_t H) {
     const int64_t units = n_seqs * H;
-    if (units <= 0 || T <= 0 || units * 4 > kFillUnits) return sp;
+    if (units <= 0 || T <= 0 || units * 4 > kFillUnits) return 1;
     int64_t P = kFillUnits / units;
     const int64_t by_len = T / kMinSegTokens;
     if (P > by_len) P = by_len;
-    if (P < 2) return sp;
-    int64_t L = (T + P - 1) / P;
-    L = (L + kChunk - 1) / kChunk * kChunk;
-    sp.P = (int32_t)((T + L - 1) / L);
-    sp.L = L;
-    if (sp.P < 2) sp = Split{1, T};
-    return sp;
+    return P < 3 ? 1 : (int32_t)P;
+}
+
+// With T >= 2048 P and a ratio R of 16 .. 48 sixteenths, L (rounded down to
+// whole chunks) and segment 0 both come to at least 1,216 tokens and the
+// last segment is at most 31 tokens shorter than L: the plan never
+// degenerates (the check below only guards the arithmetic).
+Split split_for(int64_t n_seqs, int64_t T, int64_t H, bool bf16_in) {
+    const int64_t R = bf16_in ? 34 : 32;
+    const int64_t P = seg_count(n_seqs, T, H);
+    if (P < 3) return Split{1, T, T};
+    const int64_t L = 16 * T / (16 * (P - 1) + R) / kChunk * kChunk;
+    const int64_t first = (T - (P - 1) * L + kChunk - 1) / kChunk * kChunk;
+    if (L < kChunk || first < kChunk || T - first - (P - 2) * L < 1) return Split{1, T, T};
+    return Split{(int32_t)P, L, first};
 }
 
 // A second stream per device (default priority, not synchronising with the
@@ -171,10 +187,11 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H, int32
     if (n_seqs < 0 || dk != kHeadDim || dv != kHeadDim || H < 1 || T < 0) return 0;
     if (H > KDA_MAX_HEADS) return 0;
     if (varlen) return n_seqs > kOrderMax ? 0 : (size_t)n_seqs * sizeof(int32_t);
-    const Split sp = split_for(n_seqs, T, H);
-    if (sp.P < 2) return 0;
-    // transitions, local final states and incoming states of every segment
-    return (size_t)3 * n_seqs * sp.P * H * kStateBytes;
+    const int32_t P = seg_count(n_seqs, T, H);
+    if (P < 3) return 0;
+    // transitions and zero-start final states of the P - 2 middle segments,
+    // incoming states of the P - 1 later segments, segment 0's final state
+    return (size_t)(3 * P - 4) * n_seqs * H * kStateBytes;
 }
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
@@ -260,6 +277,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     kda::PrefillParams p{};
     p.seg_len = T;
     p.seg_per_seq = 1;
+    p.seg_first = 0;
+    p.seg_r0 = 0;
     p.seg_sel = -1;
     p.s0_identity = 0;
     p.h_states = nullptr;
@@ -282,61 +301,72 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     p.n_slices = n_slices;
     p.n_units = (int32_t)units;
     const bool bf16_in = in_dtype == KDA_BF16;
-    if (varlen || !use_ws) {
+    const Split sp = varlen || !use_ws ? Split{1, T, T} : split_for(n_seqs, T, H, bf16_in);
+    if (sp.P < 3) {
         hipError_t e = kda::launch_chunk_fwd(p, bf16_in, wcols, varlen && use_ws, stream);
         return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
 
-    // Sequence-parallel path (equal lengths, few chains): every sequence is
-    // cut into P segments.  Pass 1 runs each segment from a zero state (its
-    // local final state) and from the identity with v = 0 (its transition);
-    // the merge chains them into each segment's incoming state and the
-    // final states; pass 2 reruns each segment from its incoming state and
-    // writes o.
-    const Split sp = split_for(n_seqs, T, H);
-    const int64_t chains = (int64_t)n_seqs * sp.P;
-    const int64_t cunits = chains * H;
-    float* wF = (float*)workspace;
-    float* wSl = wF + cunits * (kHeadDim * kHeadDim);
-    float* wSin = wSl + cunits * (kHeadDim * kHeadDim);
-    kda::PrefillParams ps = p;
-    ps.n_seqs = (int32_t)chains;
-    ps.n_units = (int32_t)cunits;
-    ps.n_slices = cunits < 256 ? 2 : 1;
-    ps.seg_len = sp.L;
-    ps.seg_per_seq = sp.P;
-    const int swcols = 128 / (4 * ps.n_slices);
-    if (((cunits + 7) / 8) * 8 * ps.n_slices > kMaxGrid) return KDA_ERR_TOO_LARGE;
+    // Sequence-parallel path (equal lengths, few chains; the plan is
+    // described at split_for).  Pass 1: segment 0 from S0 with o, on the
+    // second stream, beside the dual-chain pass over the middle segments;
+    // then the merge and the rerun of the later segments from their
+    // incoming states.
+    const int32_t n_mid = sp.P - 2;
+    const int64_t st = kHeadDim * kHeadDim;
+    const int64_t mid_units = units * n_mid, late_units = units * (n_mid + 1);
+    float* wF = (float*)workspace;             // [n_seqs * n_mid, H] transitions
+    float* wSl = wF + mid_units * st;          // [n_seqs * n_mid, H] zero-start final states
+    float* wSin = wSl + mid_units * st;        // [n_seqs * (n_mid + 1), H] incoming states
+    float* wE = wSin + late_units * st;        // [n_seqs, H] segment 0's final states
+    float* wST = wF;                           // rerun final states (F and Sl are dead by then)
+    if (2 * units > kMaxGrid || late_units + 8 > kMaxGrid) return KDA_ERR_TOO_LARGE;
 
-    kda::PrefillParams pc = ps;   // outputs from the true incoming states
+    kda::PrefillParams ps = p;
+    ps.seg_len = sp.L;
+    ps.seg_first = sp.first;
+    kda::PrefillParams p0 = ps;   // segment 0: from S0, writes o and its final state
+    p0.seg_len = sp.first;        // (one uniform segment of that length per sequence)
+    p0.seg_first = 0;
+    p0.seg_per_seq = 1;
+    p0.seg_r0 = 0;
+    p0.S_T = wE;
+    kda::PrefillParams pd = ps;   // middle segments: zero start -> Sl, identity start -> F
+    pd.seg_per_seq = n_mid;
+    pd.seg_r0 = 1;
+    pd.n_seqs = n_seqs * n_mid;
+    pd.n_units = (int32_t)mid_units;
+    pd.n_slices = 1;
+    pd.S0 = nullptr;
+    pd.o = nullptr;
+    pd.S_T = wSl;
+    pd.S_T2 = wF;
+    kda::PrefillParams pc = ps;   // segments 1 .. P-1 from their incoming states, write o
+    pc.seg_per_seq = n_mid + 1;
+    pc.seg_r0 = 1;
+    pc.n_seqs = n_seqs * (n_mid + 1);
+    pc.n_units = (int32_t)late_units;
+    pc.n_slices = 1;
     pc.S0 = wSin;
-    pc.S_T = nullptr;
-    hipError_t e;
-    if (ps.n_slices == 1) {
-        // one launch runs both chains of every segment on the same tiles
-        kda::PrefillParams pd = ps;
-        pd.S0 = nullptr;
-        pd.o = nullptr;
-        pd.S_T = wSl;
-        pd.S_T2 = wF;
-        e = kda::launch_chunk_fwd_dual(pd, bf16_in, stream);
-    } else {
-        kda::PrefillParams pa = ps;   // local final states
-        pa.S0 = nullptr;
-        pa.o = nullptr;
-        pa.S_T = wSl;
-        kda::PrefillParams pb = ps;   // transitions
-        pb.S0 = nullptr;
-        pb.o = nullptr;
-        pb.S_T = wF;
-        pb.s0_identity = 1;
-        e = kda::launch_chunk_fwd(pa, bf16_in, swcols, false, stream);
-        if (e == hipSuccess) e = kda::launch_chunk_fwd(pb, bf16_in, swcols, false, stream);
+    pc.S_T = S_T ? wST : nullptr;
+
+    Fork fk(stream);
+    if (kda::launch_chunk_fwd(p0, bf16_in, 128 / (4 * p0.n_slices), false, fk.fork()) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (kda::launch_chunk_fwd_dual(pd, bf16_in, stream) != hipSuccess) return KDA_ERR_HIP;
+    fk.join();
+    if (!fk.ok) return KDA_ERR_HIP;
+    if (kda::launch_segment_merge(wF, wSl, wE, wSin, n_seqs, n_mid, H, stream) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (kda::launch_chunk_fwd(pc, bf16_in, 32, false, stream) != hipSuccess) return KDA_ERR_HIP;
+    if (S_T) {
+        // the final states are those of each sequence's last segment
+        const size_t row = (size_t)H * st * 4;
+        if (hipMemcpy2DAsync(S_T, row, wST + (int64_t)n_mid * H * st, row * (n_mid + 1), row,
+                             (size_t)n_seqs, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+            return KDA_ERR_HIP;
     }
-    if (e == hipSuccess)
-        e = kda::launch_segment_merge(wF, wSl, S0, wSin, S_T, n_seqs, sp.P, H, stream);
-    if (e == hipSuccess) e = kda::launch_chunk_fwd(pc, bf16_in, swcols, false, stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return KDA_OK;
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,
@@ -685,6 +715,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, int in_dtype,
     p.T = T;
     p.seg_len = T;
     p.seg_per_seq = 1;
+    p.seg_first = 0;
+    p.seg_r0 = 0;
     p.seg_sel = -1;
     p.s0_identity = 0;
     p.n_seqs = n_seqs;

@@ -18,9 +18,14 @@ struct PrefillParams {
     float* o;
     float* S_T;
     int64_t T;              // tokens per sequence (equal lengths) or total (packed)
-    // Equal lengths only: each sequence is cut into seg_per_seq segments of
-    // seg_len tokens (the last one shorter), run as independent chains
-    // numbered b * seg_per_seq + r.  seg_per_seq = 1, seg_len = T: no split.
+    // Equal lengths only: each sequence is cut into segments, segment 0 of
+    // seg_first tokens (0: seg_len) and every later one of seg_len tokens
+    // (the last one shorter); a launch runs segments seg_r0 .. seg_r0 +
+    // seg_per_seq - 1 of every sequence as independent chains, chain
+    // b * seg_per_seq + (r - seg_r0) for segment r of sequence b.
+    // seg_per_seq = 1, seg_len = T, seg_first = seg_r0 = 0: no split.  The
+    // pipelined kernel takes uniform segments only (seg_first 0 or seg_len,
+    // seg_r0 0).
     int64_t seg_len;
     int32_t seg_per_seq;
     // Window mode (equal lengths, backward pass): seg_sel >= 0 runs only
@@ -46,6 +51,9 @@ struct PrefillParams {
     // identity with v read as zero, whose final state (the transition) goes
     // to S_T2.  o is not written.  nullptr otherwise.
     float* S_T2;
+    // (segment plan, see seg_len)
+    int64_t seg_first;
+    int32_t seg_r0;
 };
 
 // The bf16 prefill with 16 value columns per consumer wave as a three-stage
@@ -62,11 +70,13 @@ hipError_t launch_chunk_fwd(const PrefillParams& prm, bool bf16_in, int wcols, b
 // zero into S_T and the transition (identity start, v = 0) into S_T2.
 hipError_t launch_chunk_fwd_dual(const PrefillParams& prm, bool bf16_in, hipStream_t stream);
 
-// S_in[b, r] and S_T[b] of the segmented prefill: S_in[b, 0] = S0[b] (or 0),
-// S_in[b, r + 1] = F[b, r] S_in[b, r] + Sl[b, r]; S_T[b] = the state after
-// the last segment (skipped when S_T is null).  Arrays [B * P, H, 128, 128].
-hipError_t launch_segment_merge(const float* F, const float* Sl, const float* S0, float* S_in,
-                                float* S_T, int32_t B, int32_t P, int32_t H, hipStream_t stream);
+// Incoming states of the segmented prefill's segments after the first:
+// S_in[b, 0] = E[b] (the first segment's final state), S_in[b, j + 1] =
+// F[b, j] S_in[b, j] + Sl[b, j] for the n_mid segments whose transition F and
+// zero-start final state Sl were computed.  E [B, H, 128, 128], F and Sl
+// [B * n_mid, H, 128, 128], S_in [B * (n_mid + 1), H, 128, 128].
+hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_in,
+                                int32_t B, int32_t n_mid, int32_t H, hipStream_t stream);
 
 // Multi-token recurrent decode: per state, apply the first n_replay[b]
 // (NULL: all Tr) replay tokens, then T tokens with outputs; the state is

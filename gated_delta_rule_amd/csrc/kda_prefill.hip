@@ -91,11 +91,13 @@ __global__ __launch_bounds__(64 * (4 + NPROD)) void chunk_fwd_kernel(PrefillPara
         t1 = b < t0 ? t0 : (b > Tt ? Tt : b);
     } else {
         const int64_t b = p.seg_sel >= 0 ? n : n / p.seg_per_seq;
-        const int64_t r = p.seg_sel >= 0 ? p.seg_sel : n - b * p.seg_per_seq;
+        const int64_t r = p.seg_sel >= 0 ? p.seg_sel : p.seg_r0 + (n - b * p.seg_per_seq);
+        const int64_t first = p.seg_first > 0 ? p.seg_first : p.seg_len;
+        const int64_t len = r == 0 ? first : p.seg_len;
         const int64_t e = (b + 1) * Tt;
-        t0 = b * Tt + r * p.seg_len;
+        t0 = b * Tt + (r == 0 ? 0 : first + (r - 1) * p.seg_len);
         t0 = t0 < e ? t0 : e;
-        t1 = e - t0 > p.seg_len ? t0 + p.seg_len : e;
+        t1 = e - t0 > len ? t0 + len : e;
     }
     const int64_t nch = (t1 - t0 + CH - 1) / CH;
     // STORE_H outputs: first state slot of this chain and the offset added to

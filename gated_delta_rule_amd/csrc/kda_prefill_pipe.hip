@@ -699,6 +699,8 @@ hipError_t launch_chunk_fwd_pipe(const PrefillParams& p, hipStream_t stream) {
     // the per-chunk outputs are only kept for the backward pass, which takes
     // no o (the launch is refused if both are asked for)
     if (p.h_states && p.o) return hipErrorInvalidValue;
+    // uniform segments only
+    if (p.seg_r0 != 0 || (p.seg_first != 0 && p.seg_first != p.seg_len)) return hipErrorInvalidValue;
     if (p.h_states)
         hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, true, false>), grid, block, 0, stream, p);
     else if (p.o)

@@ -1,19 +1,21 @@
 // Merge step of the sequence-parallel prefill (gfx950).
 //
-// A long sequence is cut into P segments that run as independent chains.
+// A long sequence is cut into segments that run as independent chains.
 // Because the recurrence is linear in the state, a segment's final state is
 // S_out = F S_in + Sl, where Sl is the segment's final state from a zero
 // start and F (d_k x d_k) is the segment's transition, obtained by running
 // the same chain from the identity with v = 0.  "Kimi K3 技术报告解读"
 // section 7.3 describes this within-GPU sequence parallelism (a segment's
 // transition does not depend on its incoming state, so segments run
-// independently and merge exactly) next to its multi-GPU form.  The
-// incoming states follow from one left-to-right pass
-//   S_in[0] = S0,  S_in[r + 1] = F[r] S_in[r] + Sl[r],
-// after which every segment reruns from its true S_in.
+// independently and merge exactly) next to its multi-GPU form.  The first
+// segment starts from the known initial state, so it runs once, directly;
+// its final state E opens one left-to-right pass over the middle segments,
+//   S_in[0] = E,  S_in[j + 1] = F[j] S_in[j] + Sl[j],
+// which gives the incoming state of every later segment, after which those
+// segments rerun from their true S_in.
 //
 // One workgroup per (sequence, head, 16-column block of S): the 128 x 16
-// slice of the running state stays in registers, F[r] (64 KB) is staged in
+// slice of the running state stays in registers, F[j] (64 KB) is staged in
 // LDS, and each thread forms 8 outputs as 128-term fp32 dot products in a
 // fixed order (deterministic).
 #include "kda_device.h"
@@ -26,10 +28,8 @@ constexpr int MG_COLS = 16;     // value columns per workgroup
 constexpr int MG_LDF = 132;     // LDS row stride of F (floats)
 
 __global__ __launch_bounds__(MG_THREADS) void segment_merge_kernel(
-    const float* __restrict__ F, const float* __restrict__ Sl, const float* S0,
-    float* __restrict__ S_in, float* S_T, int32_t P, int32_t H) {
-    // S0 and S_T may be the same array (in-place carry): each thread reads
-    // its S0 elements before it writes the same elements of S_T.
+    const float* __restrict__ F, const float* __restrict__ Sl, const float* __restrict__ E,
+    float* __restrict__ S_in, int32_t n_mid, int32_t H) {
     constexpr size_t ST = 128 * 128;
     const int cb = blockIdx.x & 7;
     const int bh = blockIdx.x >> 3;
@@ -44,13 +44,14 @@ __global__ __launch_bounds__(MG_THREADS) void segment_merge_kernel(
     const size_t own = ((size_t)b * H + h) * ST;
     float s[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s[i] = S0 ? S0[own + (size_t)(rg + 16 * i) * 128 + col] : 0.f;
+    for (int i = 0; i < 8; ++i) s[i] = E[own + (size_t)(rg + 16 * i) * 128 + col];
 
-    for (int r = 0; r < P; ++r) {
-        const size_t base = (((size_t)b * P + r) * H + h) * ST;
+    for (int r = 0; r <= n_mid; ++r) {
+        const size_t out = (((size_t)b * (n_mid + 1) + r) * H + h) * ST;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) S_in[base + (size_t)(rg + 16 * i) * 128 + col] = s[i];
-        if (r == P - 1 && !S_T) break;
+        for (int i = 0; i < 8; ++i) S_in[out + (size_t)(rg + 16 * i) * 128 + col] = s[i];
+        if (r == n_mid) break;
+        const size_t base = (((size_t)b * n_mid + r) * H + h) * ST;
         const float4* Fg = reinterpret_cast<const float4*>(F + base);
         for (int e = tid; e < 128 * 32; e += MG_THREADS)
             *reinterpret_cast<float4*>(&sF[(e >> 5) * MG_LDF + 4 * (e & 31)]) = Fg[e];
@@ -75,16 +76,12 @@ __global__ __launch_bounds__(MG_THREADS) void segment_merge_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) s[i] = acc[i];
     }
-    if (S_T) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) S_T[own + (size_t)(rg + 16 * i) * 128 + col] = s[i];
-    }
 }
 
-hipError_t launch_segment_merge(const float* F, const float* Sl, const float* S0, float* S_in,
-                                float* S_T, int32_t B, int32_t P, int32_t H, hipStream_t stream) {
+hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_in,
+                                int32_t B, int32_t n_mid, int32_t H, hipStream_t stream) {
     dim3 grid((unsigned)((int64_t)B * H * 8)), block(MG_THREADS);
-    hipLaunchKernelGGL(segment_merge_kernel, grid, block, 0, stream, F, Sl, S0, S_in, S_T, P, H);
+    hipLaunchKernelGGL(segment_merge_kernel, grid, block, 0, stream, F, Sl, E, S_in, n_mid, H);
     return hipGetLastError();
 }
 

@@ -32,8 +32,9 @@
  *     stream of kda_chunk_bwd), never synchronises the host, and enqueues
  *     its kernels on `stream` (0 = the null stream), which must belong to
  *     the current device (the one every pointer refers to); kda_chunk_bwd
- *     also runs one pass on its second stream, ordered against `stream` by
- *     events (see there).
+ *     and the sequence-parallel path of kda_chunk_fwd also run one pass on
+ *     that second stream, ordered against `stream` by events (see
+ *     kda_chunk_bwd).
  *   - Every argument is validated before anything is enqueued; on error the
  *     call returns a non-zero kda_status and has no effect.  Faults raised by
  *     the device asynchronously surface at the caller's next synchronisation.
@@ -91,12 +92,15 @@ const char* kda_status_str(int status);
  *       workspace is then required.
  *   equal lengths: when n_seqs * H is small (at most 64 (sequence, head)
  *       pairs) and T is long, the sequence-parallel path cuts every
- *       sequence into P = min(256 / (n_seqs * H), T / 2048) segments (rounded
- *       so every segment is a whole number of 32-token chunks) and needs
- *       3 * n_seqs * P * H * 64 KiB
- *       (each segment's transition, local final state and incoming state).
- *       That workspace is optional: without it (NULL or smaller), the
- *       sequential path runs instead, with the same result up to rounding.
+ *       sequence into P = min(256 / (n_seqs * H), T / 2048) segments, if
+ *       that is at least 3 (every segment a whole number of 32-token chunks
+ *       but the last; the first about 2.5 times as long as the others), and
+ *       needs (3 * P - 4) * n_seqs * H * 64 KiB (the transition and local
+ *       final state of each of the P - 2 middle segments, the incoming state
+ *       of each of the P - 1 later segments and the first segment's final
+ *       state).  That workspace is optional: without it (NULL or smaller),
+ *       the sequential path runs instead, with the same result up to
+ *       rounding.
  * Returns 0 for invalid sizes as well; kda_chunk_fwd then reports the real
  * error.
  */
@@ -107,10 +111,13 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  * Chunkwise prefill: runs the recurrence over whole sequences and returns
  * every o_t and, optionally, each sequence's final state.  With equal-length
  * sequences and few (sequence, head) pairs, the sequence-parallel path
- * (when its workspace is given) runs the segments of each sequence as
- * independent chains, merges them through each segment's transition
- * d_k x d_k matrix and reruns every segment from its true incoming state;
- * "Kimi K3 技术报告解读" section 7.3 describes this within-GPU split.  The chunkwise
+ * (when its workspace is given) runs the first segment of each sequence
+ * from S0 (writing its o) beside the middle segments, which run as
+ * independent chains from zero and from the identity (their local final
+ * states and d_k x d_k transitions); a merge through the transitions gives
+ * the incoming state of every later segment, which then reruns from it and
+ * writes its o; "Kimi K3 技术报告解读" section 7.3 describes this within-GPU
+ * split.  The chunkwise
  * evaluation (cumulative in-chunk log-decay, k+ = k e^{g}, k- = k e^{-g},
  * the strictly lower-triangular A_tj = beta_t k+_t . k-_j solved by forward
  * substitution, O = Q+ S + Tril(Q+ K-^T) U and the state hand-off
@@ -159,6 +166,9 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  *   The two plans round differently, so the same sequence can give results
  *   that differ in the last bits depending on how many (sequence, head)
  *   pairs share the call; both stay within 2e-3 of the exact recurrence.
+ *   On the sequence-parallel path the first segment of every sequence runs
+ *   on the two-workgroup plan and the later segments on the one-workgroup
+ *   plan.
  * The chunk form carries per-channel factors of up to e^{+-80}: in a key
  * channel whose decay sits at the bound (log_alpha = -5 for 16 tokens) the
  * state enters the products scaled by e^{-80}, so its entries below about
@@ -180,7 +190,7 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
  * its address is looked up on a device's first call).  That size covers
  * every case kda_chunk_fwd_workspace_bytes can report (a longest-first
  * order of up to 4096 sequences, or the sequence-parallel path's at most
- * 3 x 256 segment states); a larger need returns KDA_ERR_TOO_LARGE.  The call
+ * 3 * 256 - 4 segment states); a larger need returns KDA_ERR_TOO_LARGE.  The call
  * allocates nothing.  All calls on one GPU share its scratch array and it
  * keeps the last call's contents: calls that may overlap on one GPU (other
  * streams, other threads) race and must be serialised by the caller.

@@ -21,7 +21,8 @@ int fails = 0;
 int fail_fwd_in = -1;   // > 0: the forward launch that many calls from now fails
 // forward and backward launches in order, for the backward's window plan
 struct Rec {
-    char kind;                 // 'f' forward, 't' chunk matrices, 'g' walk + gradients,
+    char kind;                 // 'f' forward, 'd' dual-chain forward, 'm' merge, 'c' copy,
+                               // 't' chunk matrices, 'g' walk + gradients,
                                // 'r' event record, 'w' stream waits for event
     int seg_sel, win_idx;
     bool stores;               // forward keeps per-chunk values
@@ -30,6 +31,11 @@ struct Rec {
     int64_t seg_len, win_len, slots;
     hipStream_t stream;        // stream of the launch / record / wait
     hipEvent_t event;          // 'r', 'w'
+    // forward launches ('f', and 'd' for the dual-chain pass): the segment plan
+    int64_t seg_first = 0;
+    int seg_r0 = 0, seg_per_seq = 0, n_seqs = 0, n_units = 0, n_slices = 0;
+    bool has_o = false;
+    const float* S_T2 = nullptr;
 };
 Rec recs[512];
 int n_recs = 0;
@@ -50,10 +56,22 @@ int n_events = 0, n_streams = 0;
 
 namespace kda {
 hipError_t launch_chunk_fwd_pipe(const PrefillParams&, hipStream_t) { return hipSuccess; }
+static void rec_fwd(char kind, const PrefillParams& p, hipStream_t stream) {
+    Rec r{kind, p.seg_sel, 0, p.h_states != nullptr, p.S0, p.S_T, nullptr, nullptr, p.seg_len, 0, 0,
+          stream, nullptr};
+    r.seg_first = p.seg_first;
+    r.seg_r0 = p.seg_r0;
+    r.seg_per_seq = p.seg_per_seq;
+    r.n_seqs = p.n_seqs;
+    r.n_units = p.n_units;
+    r.n_slices = p.n_slices;
+    r.has_o = p.o != nullptr;
+    r.S_T2 = p.S_T2;
+    rec(r);
+}
 hipError_t launch_chunk_fwd(const PrefillParams& p, bool, int wcols, bool, hipStream_t stream) {
     ++n_launch;
-    rec(Rec{'f', p.seg_sel, 0, p.h_states != nullptr, p.S0, p.S_T, nullptr, nullptr, p.seg_len, 0, 0,
-            stream, nullptr});
+    rec_fwd('f', p, stream);
     if (fail_fwd_in > 0 && --fail_fwd_in == 0) return hipErrorInvalidValue;
     CHECK(p.seg_sel < 0 || (!p.cu && p.seg_len % 32 == 0 && p.seg_len > 0));
     CHECK(!p.h_states || (p.r_out && p.u_out && !p.o));
@@ -63,17 +81,22 @@ hipError_t launch_chunk_fwd(const PrefillParams& p, bool, int wcols, bool, hipSt
     CHECK(p.n_units == p.n_seqs * p.H);
     return hipSuccess;
 }
-hipError_t launch_chunk_fwd_dual(const PrefillParams& p, bool, hipStream_t) {
+hipError_t launch_chunk_fwd_dual(const PrefillParams& p, bool, hipStream_t stream) {
     ++n_launch;
     ++n_dual;
-    CHECK(p.n_slices == 1 && p.S_T && p.S_T2 && !p.o);
-    CHECK(p.n_units == p.n_seqs * p.H && p.n_units >= 256);
+    rec_fwd('d', p, stream);
+    CHECK(p.n_slices == 1 && p.S_T && p.S_T2 && !p.o && !p.S0);
+    CHECK(p.n_units == p.n_seqs * p.H);
     return hipSuccess;
 }
-hipError_t launch_segment_merge(const float*, const float*, const float*, float*, float*, int32_t B,
-                                int32_t P, int32_t H, hipStream_t) {
+hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_in, int32_t B,
+                                int32_t n_mid, int32_t H, hipStream_t stream) {
     ++n_merge;
-    CHECK(B >= 1 && P >= 2 && H >= 1);
+    Rec r{'m', -1, -1, false, E, S_in, F, nullptr, n_mid, 0, 0, stream, nullptr};
+    r.S_T2 = Sl;
+    r.n_seqs = B;
+    rec(r);
+    CHECK(B >= 1 && n_mid >= 1 && H >= 1 && F && Sl && E && S_in);
     return hipSuccess;
 }
 hipError_t launch_recurrent(const void*, const void*, const void*, bool, const float*, const float*,
@@ -137,6 +160,17 @@ hipError_t hipStreamWaitEvent(hipStream_t s, hipEvent_t e, unsigned int) {
     rec(Rec{'w', -1, -1, false, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, s, e});
     return hipSuccess;
 }
+// 'c': S0 = source, S_T = destination, seg_len = width, win_len = height,
+// slots = source pitch (bytes), seg_first = destination pitch
+hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
+                            size_t height, hipMemcpyKind kind, hipStream_t s) {
+    Rec r{'c', -1, -1, false, (const float*)src, (float*)dst, nullptr, nullptr, (int64_t)width,
+          (int64_t)height, (int64_t)spitch, s, nullptr};
+    r.seg_first = (int64_t)dpitch;
+    rec(r);
+    CHECK(kind == hipMemcpyDeviceToDevice && width <= dpitch && width <= spitch);
+    return hipSuccess;
+}
 
 // 1 TiB apart, so no two of them overlap at these sizes
 static const void* P(int i) { return (const void*)(uintptr_t)((1ull << 44) + (uint64_t)i * (1ull << 40)); }
@@ -154,26 +188,104 @@ int main() {
     // packed batch with its order workspace
     CHECK(kda_chunk_fwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(8), 32,
                         270000, 96, 128, 128, F(5), nullptr, (void*)P(9), 128, nullptr) == KDA_OK);
-    // sequence-parallel path with 256 segment chains: one launch for both
-    // chains of every segment, the merge, the rerun
-    {
-        const size_t ws = kda_chunk_fwd_workspace_bytes(1, 1 << 20, 16, 128, 128, 0);
-        CHECK(ws == (size_t)3 * 16 * 16 * 65536);
-        const int before = n_launch, mb = n_merge, db = n_dual;
-        CHECK(kda_chunk_fwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, nullptr, 1, 1 << 20, 16,
-                            128, 128, F(5), F(6), (void*)P(9), ws, nullptr) == KDA_OK);
-        CHECK(n_launch - before == 2 && n_merge - mb == 1 && n_dual - db == 1);
-    }
-    // ... and with fewer chains (two workgroups per chain): the two chains
-    // as separate launches
-    {
-        const size_t ws = kda_chunk_fwd_workspace_bytes(2, 6000, 3, 128, 128, 0);
-        CHECK(ws == (size_t)3 * 2 * 2 * 3 * 65536);
-        const int before = n_launch, mb = n_merge, db = n_dual;
-        CHECK(kda_chunk_fwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, nullptr, 2, 6000, 3,
-                            128, 128, F(5), F(6), (void*)P(9), ws, nullptr) == KDA_OK);
-        CHECK(n_launch - before == 3 && n_merge - mb == 1 && n_dual == db);
-    }
+    // sequence-parallel path: segment 0 from S0 (writing o) on the second
+    // stream beside the dual-chain pass over the middle segments, the merge
+    // from segment 0's final state, the rerun of segments 1 .. P-1 and the
+    // copy of the last segments' final states.  The segments of the plan
+    // (the kernels' mapping from chain index to tokens, restated here) tile
+    // every sequence exactly, and both passes fit the 256 compute units.
+    hipStream_t const kMainF = (hipStream_t)(uintptr_t)0x3400;
+    auto seg_range = [](const Rec& f, int64_t T, int64_t n, int64_t* t0, int64_t* t1) {
+        const int64_t b = n / f.seg_per_seq, r = f.seg_r0 + (n - b * f.seg_per_seq);
+        const int64_t first = f.seg_first > 0 ? f.seg_first : f.seg_len;
+        const int64_t len = r == 0 ? first : f.seg_len, e = (b + 1) * T;
+        *t0 = b * T + (r == 0 ? 0 : first + (r - 1) * f.seg_len);
+        if (*t0 > e) *t0 = e;
+        *t1 = e - *t0 > len ? *t0 + len : e;
+    };
+    auto seq_parallel_plan = [&](int n_seqs, int64_t T, int H, const float* S0, float* S_T,
+                                 int expect_P, int dtype = KDA_BF16) {
+        const size_t ws = kda_chunk_fwd_workspace_bytes(n_seqs, T, H, 128, 128, 0);
+        const int64_t units = (int64_t)n_seqs * H;
+        CHECK(ws == (size_t)(3 * expect_P - 4) * units * 65536);
+        n_recs = 0;
+        CHECK(kda_chunk_fwd(P(0), P(1), P(2), dtype, F(3), F(4), S0, nullptr, n_seqs, T, H, 128,
+                            128, F(5), S_T, (void*)P(9), ws, kMainF) == KDA_OK);
+        const Rec *f0 = nullptr, *fd = nullptr, *fm = nullptr, *fc = nullptr, *cp = nullptr;
+        bool forked = false, joined = false;
+        hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+        for (int i = 0; i < n_recs; ++i) {
+            const Rec& r = recs[i];
+            if (r.kind == 'r' && r.stream == kMainF) fork_ev = r.event;
+            else if (r.kind == 'w' && r.stream == kSide) forked = r.event == fork_ev && fork_ev;
+            else if (r.kind == 'r' && r.stream == kSide) join_ev = r.event;
+            else if (r.kind == 'w' && r.stream == kMainF) joined = r.event == join_ev && join_ev && f0 && fd;
+            else if (r.kind == 'f' && !f0) { f0 = &r; CHECK(r.stream == kSide && forked && !joined); }
+            else if (r.kind == 'd') { fd = &r; CHECK(r.stream == kMainF && !joined); }
+            else if (r.kind == 'm') { fm = &r; CHECK(r.stream == kMainF && joined); }
+            else if (r.kind == 'f') { fc = &r; CHECK(r.stream == kMainF && fm); }
+            else if (r.kind == 'c') { cp = &r; CHECK(r.stream == kMainF && fc); }
+        }
+        CHECK(f0 && fd && fm && fc && (S_T ? cp != nullptr : cp == nullptr));
+        if (!(f0 && fd && fm && fc)) return;
+        const int Pn = fd->seg_per_seq + 2;
+        CHECK(Pn == expect_P);
+        // segment 0: from S0, writes o and its final state E
+        CHECK(f0->seg_r0 == 0 && f0->seg_per_seq == 1 && f0->n_seqs == n_seqs && f0->has_o &&
+              f0->S0 == S0 && f0->S_T && f0->n_slices == 2 && f0->n_units == units &&
+              f0->seg_first == 0);   // one uniform segment: the pipelined kernel's mapping
+        // dual pass over the middle segments: no o, from zero and from I
+        CHECK(fd->seg_r0 == 1 && fd->n_seqs == n_seqs * (Pn - 2) && fd->n_slices == 1 && !fd->has_o);
+        // the merge: E -> incoming states of segments 1 .. P-1
+        CHECK(fm->S0 == f0->S_T && fm->dS_T == fd->S_T2 && fm->S_T2 == fd->S_T &&
+              fm->seg_len == Pn - 2 && fm->n_seqs == n_seqs);
+        // rerun of segments 1 .. P-1 from the merged states, writes o
+        CHECK(fc->seg_r0 == 1 && fc->seg_per_seq == Pn - 1 && fc->n_seqs == n_seqs * (Pn - 1) &&
+              fc->has_o && fc->S0 == fm->S_T && (S_T ? fc->S_T != nullptr : fc->S_T == nullptr));
+        CHECK(fd->seg_len == fc->seg_len && fd->seg_first == fc->seg_first && f0->seg_len == fc->seg_first);
+        CHECK(fc->n_slices == 1 && units * Pn <= 256 && units * (Pn - 1) <= 256);
+        // tiling: segment 0 from f0, 1 .. P-2 from fd, 1 .. P-1 from fc
+        for (int64_t b = 0; b < n_seqs; ++b) {
+            int64_t t0, t1, at = b * T;
+            seg_range(*f0, T, b, &t0, &t1);
+            CHECK(t0 == at && t1 > t0 && (t1 - t0) % 32 == 0);
+            at = t1;
+            for (int r = 1; r < Pn; ++r) {
+                int64_t c0, c1;
+                seg_range(*fc, T, b * (Pn - 1) + (r - 1), &c0, &c1);
+                CHECK(c0 == at && c1 > c0 && (c0 - b * T) % 32 == 0);
+                if (r < Pn - 1) {
+                    int64_t d0, d1;
+                    seg_range(*fd, T, b * (Pn - 2) + (r - 1), &d0, &d1);
+                    CHECK(d0 == c0 && d1 == c1);
+                }
+                at = c1;
+            }
+            CHECK(at == (b + 1) * T);
+        }
+        if (cp) {
+            // the last segment's final state of every sequence, [n_seqs, H] rows
+            const int64_t row = (int64_t)H * 65536;
+            CHECK(cp->S_T == S_T && cp->seg_len == row && cp->win_len == n_seqs &&
+                  cp->seg_first == row && cp->slots == row * (Pn - 1) &&
+                  (const char*)cp->S0 == (const char*)fc->S_T + (Pn - 2) * row);
+        }
+    };
+    seq_parallel_plan(1, 1 << 20, 16, nullptr, F(6), 16);   // 1M tokens, 16 heads
+    seq_parallel_plan(1, 1 << 20, 16, F(7), F(7), 16);      // S_T == S0
+    seq_parallel_plan(2, 7000, 3, F(7), F(6), 3);           // ragged last segment
+    seq_parallel_plan(1, 8192, 64, F(7), nullptr, 4);       // rerun on 192 one-slice chains
+    seq_parallel_plan(1, 8192, 4, nullptr, F(6), 4);        // 12 rerun chains
+    seq_parallel_plan(3, 100000, 1, F(7), F(6), 48);
+    seq_parallel_plan(1, 1 << 22, 1, nullptr, F(6), 256);
+    for (int64_t T = 6144; T < 6144 + 40; ++T) seq_parallel_plan(1, T, 5, nullptr, F(6), 3);
+    for (int64_t T = 6144; T < 6144 + 40; ++T) seq_parallel_plan(1, T, 5, nullptr, F(6), 3, KDA_F32);
+    seq_parallel_plan(1, 1 << 18, 16, F(7), F(6), 16, KDA_F32);
+    for (int P = 3; P <= 256; P += 23) seq_parallel_plan(1, 2048 * P, 1, nullptr, F(6), P);
+    for (int P = 3; P <= 256; P += 23) seq_parallel_plan(1, 2048 * P + 2047, 1, F(7), F(6), P, KDA_F32);
+    // too short for three segments: the sequential path, no workspace
+    CHECK(kda_chunk_fwd_workspace_bytes(2, 6000, 3, 128, 128, 0) == 0);
+    CHECK(kda_chunk_fwd_workspace_bytes(1, 8192, 96, 128, 128, 0) == 0);
     // error paths
     CHECK(kda_chunk_fwd(P(0), P(1), P(2), 9, F(3), F(4), nullptr, nullptr, 1, 8, 4, 128, 128, F(5),
                         nullptr, nullptr, 0, nullptr) == KDA_ERR_BAD_DTYPE);

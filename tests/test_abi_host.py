@@ -65,12 +65,16 @@ def test_workspace_query(lib):
     assert ws(32, 1000, 96, 64, 128, 1) == 0              # invalid head size
     assert ws(-1, 1000, 96, 128, 128, 1) == 0
     # equal lengths, few (sequence, head) pairs, long T: sequence-parallel
-    # path with P segments, 3 state-sized arrays per segment and head
-    assert ws(1, 1 << 20, 16, 128, 128, 0) == 3 * 16 * 16 * 65536     # P = 256 / 16
-    assert ws(2, 6000, 3, 128, 128, 0) == 3 * 2 * 2 * 3 * 65536       # P limited by T / 2048
-    assert ws(1, 8192, 16, 128, 128, 0) == 3 * 4 * 16 * 65536        # P = 8192 / 2048
-    assert ws(1, 4095, 16, 128, 128, 0) == 0                           # too short to split
-    assert ws(1, 1 << 20, 65, 128, 128, 0) == 0                        # enough pairs already
+    # path with P >= 3 segments; per (sequence, head) 3P - 4 state-sized
+    # arrays (transition and local final state of the P - 2 middle segments,
+    # incoming state of the P - 1 later ones, segment 0's final state)
+    assert ws(1, 1 << 20, 16, 128, 128, 0) == (3 * 16 - 4) * 16 * 65536   # P = 256 / 16
+    assert ws(2, 7000, 3, 128, 128, 0) == (3 * 3 - 4) * 2 * 3 * 65536   # P limited by T / 2048
+    assert ws(1, 8192, 16, 128, 128, 0) == (3 * 4 - 4) * 16 * 65536      # P = 8192 / 2048
+    assert ws(1, 1 << 22, 1, 128, 128, 0) == (3 * 256 - 4) * 65536      # the largest: P = 256
+    assert ws(2, 6000, 3, 128, 128, 0) == 0                              # two segments: no gain
+    assert ws(1, 4095, 16, 128, 128, 0) == 0                             # too short to split
+    assert ws(1, 1 << 20, 65, 128, 128, 0) == 0                          # enough pairs already
 
 
 # Fake, never-dereferenced device addresses for validation-only calls.

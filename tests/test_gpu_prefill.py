@@ -200,9 +200,9 @@ def test_deterministic():
 # as independent segments merged through their transitions (the workspace
 # query reports the path: nonzero for equal lengths means it is taken).
 
-@pytest.mark.parametrize("T,H,B,s0,dtype", [(6000, 3, 2, 0.02, "bf16"),   # 2 segments, ragged
+@pytest.mark.parametrize("T,H,B,s0,dtype", [(7000, 3, 2, 0.02, "bf16"),   # 3 segments, ragged
                                             (8192, 4, 1, 0.0, "bf16"),    # 4 segments
-                                            (5000, 2, 1, 0.02, "f32")])   # fp32 inputs
+                                            (6144, 2, 1, 0.02, "f32")])   # fp32 inputs, 3 segments
 def test_sequence_parallel_matches_oracle(T, H, B, s0, dtype):
     assert kda.chunk_fwd_workspace_bytes(B, T, H, varlen=False) > 0
     w, arrs = small(T, H, B, s0, dtype=dtype, wid=0 if dtype == "f32" else 1)
@@ -213,17 +213,21 @@ def test_sequence_parallel_matches_oracle(T, H, B, s0, dtype):
 @pytest.mark.parametrize("T,H,B,dtype", [(8192, 64, 1, "bf16"),    # 4 segments x 64 heads
                                          (8192, 32, 2, "f32")])    # 2 x 4 segments x 32 heads
 def test_sequence_parallel_fused_chains_match_oracle(T, H, B, dtype):
-    """With 256 segment chains (one workgroup each) the local final states and
-    the transitions come from one launch that carries both chains over the
-    same tiles; every output element against the oracle."""
-    assert kda.chunk_fwd_workspace_bytes(B, T, H, varlen=False) == 3 * 256 * 65536
+    """64 (sequence, head) pairs cut into four segments each: segment 0 on
+    two workgroups per pair beside the dual-chain pass over the 128 middle
+    chains (local final states and transitions from one launch on the same
+    tiles), then the rerun on 192 one-workgroup chains; every output element
+    against the oracle.  Workspace: transitions and local final states of
+    the middle segments, incoming states of the later ones, segment 0's final
+    states."""
+    assert kda.chunk_fwd_workspace_bytes(B, T, H, varlen=False) == (2 * 2 + 3 + 1) * 64 * 65536
     w, arrs = small(T, H, B, 0.02, dtype=dtype, wid=0 if dtype == "f32" else 1)
     check_full(w, arrs, tol=TOL_F32 if dtype == "f32" else TOL_BF16,
                label=f"sequence-parallel fused chains {dtype} T={T} H={H} B={B}")
 
 
 def test_sequence_parallel_agrees_with_sequential_and_in_place():
-    w, arrs = small(6000, 3, 2, 0.02)
+    w, arrs = small(7000, 3, 2, 0.02)
     d = to_dev(arrs, w)
     say("[prefill] sequence-parallel vs sequential")
     o_p, s_p = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
@@ -289,6 +293,6 @@ def test_workload2_full_size_sampled_units():
 @pytest.mark.timeout(900)
 def test_workload3_full_size_sampled_columns():
     """T=1,048,576, H=16: eight value columns of two heads, every token (the
-    sequence-parallel path: 16 segments per head, one 512-thread workgroup
-    per segment chain)."""
+    sequence-parallel path: 16 segments per head, the first on two
+    workgroups, every later one on one 512-thread workgroup per chain)."""
     _sampled_check(W.workload(3), [0, 9], "workload 3 (T=1M H=16)", cols=(40, 48))

@@ -4,8 +4,8 @@ against kda_chunk_fwd with a caller-supplied workspace, through the C ABI.
 The two paths that use a workspace are covered, each with two calls in a
 row, the second on a smaller input (the scratch array keeps the previous
 call's contents): the sequence-parallel path (segment transitions, local and
-incoming states in the scratch array; once with 256 segment chains, the
-fused two-chain launch, then with 16) and the packed batch (the
+incoming states in the scratch array; once with 64 (sequence, head) pairs
+in four segments, then with 8 pairs in three) and the packed batch (the
 longest-first order in the scratch array).  Same kernels, so the outputs
 must be bitwise equal; the first call of each pair is also checked against
 the fp64 oracle on sampled heads."""
@@ -50,7 +50,7 @@ def equal_lengths(T, H, s0):
     return w, arrs
 
 
-@pytest.mark.parametrize("first,second", [((8192, 64), (4096, 8))])
+@pytest.mark.parametrize("first,second", [((8192, 64), (6144, 8))])
 def test_noalloc_sequence_parallel_two_calls(first, second):
     for i, (T, H) in enumerate((first, second)):
         assert kda.chunk_fwd_workspace_bytes(1, T, H, varlen=False) > 0
