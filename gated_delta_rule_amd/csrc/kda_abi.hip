@@ -25,23 +25,27 @@ constexpr int32_t kMaxRecurrent = 64;      // tokens per request on the recurren
 constexpr int64_t kBwdChunkElems = 3 * 32 * 32 + 3 * 128 * 32 + 128;
 
 // Sequence-parallel split of an equal-length batch.  Every sequence is cut
-// into P segments.  Segment 0 starts from the known initial state: it runs
-// once, writing o, on the two-slice kernel (two workgroups per (sequence,
-// head)), beside the dual-chain pass over the middle segments 1 .. P-2 (one
-// workgroup each; zero start and identity start on the same tiles); the
-// merge then gives the incoming state of segments 1 .. P-1, which rerun from
-// it (one workgroup each).  The two passes hold units * P and units * (P - 1)
-// workgroups, within the 256 compute units.  Segment 0 is made longer than
-// the others so that it ends with the dual pass: with both running, its
-// chain steps through a chunk about 2.1 times as fast as a dual chain.  The
-// ratio (in sixteenths, per input type) is the one that ran the 1M-token,
-// 16-head shape fastest: 34 for bf16 (16.3 ms against 17.7 ms with equal
-// segments all through the dual pass; 30 gave 16.5, 40 gave 17.3), 32 for
-// fp32 (262,144 tokens: 9.45 ms against 10.17; 30 gave 9.56, 36 gave 9.98).
+// into P segments: segment 0, P - 2 middle segments of L tokens and the last
+// segment.  Pass 1: segment 0 starts from the known initial state, so it
+// runs once, writing o, on the two-slice kernel (two workgroups per
+// (sequence, head)), beside the dual-chain pass over the middle segments
+// (one workgroup each; zero start and identity start on the same tiles).
+// The merge gives the incoming state of every later segment.  Pass 2: the
+// middle segments rerun from theirs on the one-slice kernel (one workgroup
+// each), beside the last segment, which has no dual pass and runs once on
+// the two-slice kernel.  Each pass holds units * P workgroups, within the
+// 256 compute units.  The two-slice chains step through a chunk faster than
+// the others, so segment 0 and the last segment are made longer than L by
+// the ratios (in sixteenths, per input type) that ran the 1M-token, 16-head
+// shape fastest: bf16 34 and 26 (16.07 ms, against 16.36 with the last
+// segment as long as the middle ones and rerun beside them, and 17.5 with
+// every segment through the dual pass; 18 and 34 for the last one gave
+// 16.38 and 17.34), fp32 32 and 28 (262,144 tokens: 9.28 ms against 9.49
+// and 10.09; 20 and 32 gave 9.39 and 9.74).
 struct Split {
     int32_t P;       // segments per sequence (1: no split)
-    int64_t L;       // tokens of every segment after the first (the last shorter)
-    int64_t first;   // tokens of segment 0
+    int64_t L;       // tokens of every middle segment
+    int64_t first;   // tokens of segment 0 (the last one has the rest)
 };
 
 // Segments per sequence; the workspace depends on this count only.
@@ -54,17 +58,18 @@ int32_t seg_count(int64_t n_seqs, int64_t T, int64_t H) {
     return P < 3 ? 1 : (int32_t)P;
 }
 
-// With T >= 2048 P and a ratio R of 16 .. 48 sixteenths, L (rounded down to
-// whole chunks) and segment 0 both come to at least 1,216 tokens and the
-// last segment is at most 31 tokens shorter than L: the plan never
+// Segment 0 : L = R0 / 16 and last : L = R1 / 16.  With T >= 2048 P and
+// ratios of 16 .. 48 sixteenths, L (rounded down to whole chunks), segment 0
+// and the last segment all come to at least 864 tokens: the plan never
 // degenerates (the check below only guards the arithmetic).
 Split split_for(int64_t n_seqs, int64_t T, int64_t H, bool bf16_in) {
-    const int64_t R = bf16_in ? 34 : 32;
+    const int64_t R0 = bf16_in ? 34 : 32;
+    const int64_t R1 = bf16_in ? 26 : 28;
     const int64_t P = seg_count(n_seqs, T, H);
     if (P < 3) return Split{1, T, T};
-    const int64_t L = 16 * T / (16 * (P - 1) + R) / kChunk * kChunk;
-    const int64_t first = (T - (P - 1) * L + kChunk - 1) / kChunk * kChunk;
-    if (L < kChunk || first < kChunk || T - first - (P - 2) * L < 1) return Split{1, T, T};
+    const int64_t L = 16 * T / (16 * (P - 2) + R0 + R1) / kChunk * kChunk;
+    const int64_t first = (R0 * L / 16 + kChunk - 1) / kChunk * kChunk;
+    if (L < kChunk || first < kChunk || T - first - (P - 2) * L < kChunk) return Split{1, T, T};
     return Split{(int32_t)P, L, first};
 }
 
@@ -308,19 +313,17 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     }
 
     // Sequence-parallel path (equal lengths, few chains; the plan is
-    // described at split_for).  Pass 1: segment 0 from S0 with o, on the
-    // second stream, beside the dual-chain pass over the middle segments;
-    // then the merge and the rerun of the later segments from their
-    // incoming states.
+    // described at split_for).  Each pass runs its two launches on the
+    // caller's stream and the second stream, joined before what follows.
     const int32_t n_mid = sp.P - 2;
     const int64_t st = kHeadDim * kHeadDim;
-    const int64_t mid_units = units * n_mid, late_units = units * (n_mid + 1);
+    const int64_t mid_units = units * n_mid;
     float* wF = (float*)workspace;             // [n_seqs * n_mid, H] transitions
     float* wSl = wF + mid_units * st;          // [n_seqs * n_mid, H] zero-start final states
-    float* wSin = wSl + mid_units * st;        // [n_seqs * (n_mid + 1), H] incoming states
-    float* wE = wSin + late_units * st;        // [n_seqs, H] segment 0's final states
-    float* wST = wF;                           // rerun final states (F and Sl are dead by then)
-    if (2 * units > kMaxGrid || late_units + 8 > kMaxGrid) return KDA_ERR_TOO_LARGE;
+    float* wSmid = wSl + mid_units * st;       // [n_seqs * n_mid, H] incoming states
+    float* wSlast = wSmid + mid_units * st;    // [n_seqs, H] the last segment's incoming states
+    float* wE = wSlast + units * st;           // [n_seqs, H] segment 0's final states
+    if (2 * units + 8 > kMaxGrid || mid_units + 8 > kMaxGrid) return KDA_ERR_TOO_LARGE;
 
     kda::PrefillParams ps = p;
     ps.seg_len = sp.L;
@@ -341,32 +344,28 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, int in_dtype,
     pd.o = nullptr;
     pd.S_T = wSl;
     pd.S_T2 = wF;
-    kda::PrefillParams pc = ps;   // segments 1 .. P-1 from their incoming states, write o
-    pc.seg_per_seq = n_mid + 1;
-    pc.seg_r0 = 1;
-    pc.n_seqs = n_seqs * (n_mid + 1);
-    pc.n_units = (int32_t)late_units;
-    pc.n_slices = 1;
-    pc.S0 = wSin;
-    pc.S_T = S_T ? wST : nullptr;
+    kda::PrefillParams pm = pd;   // middle segments from their incoming states, write o
+    pm.S0 = wSmid;
+    pm.o = o;
+    pm.S_T = nullptr;
+    pm.S_T2 = nullptr;
+    kda::PrefillParams pl = ps;   // the last segment from its incoming state: o and S_T
+    pl.seg_first = sp.first + n_mid * sp.L;   // (everything before it as segment 0)
+    pl.seg_len = T;
+    pl.seg_per_seq = 1;
+    pl.seg_r0 = 1;
+    pl.S0 = wSlast;
 
     Fork fk(stream);
-    if (kda::launch_chunk_fwd(p0, bf16_in, 128 / (4 * p0.n_slices), false, fk.fork()) != hipSuccess)
-        return KDA_ERR_HIP;
+    if (kda::launch_chunk_fwd(p0, bf16_in, 16, false, fk.fork()) != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_chunk_fwd_dual(pd, bf16_in, stream) != hipSuccess) return KDA_ERR_HIP;
     fk.join();
-    if (!fk.ok) return KDA_ERR_HIP;
-    if (kda::launch_segment_merge(wF, wSl, wE, wSin, n_seqs, n_mid, H, stream) != hipSuccess)
+    if (kda::launch_segment_merge(wF, wSl, wE, wSmid, wSlast, n_seqs, n_mid, H, stream) != hipSuccess)
         return KDA_ERR_HIP;
-    if (kda::launch_chunk_fwd(pc, bf16_in, 32, false, stream) != hipSuccess) return KDA_ERR_HIP;
-    if (S_T) {
-        // the final states are those of each sequence's last segment
-        const size_t row = (size_t)H * st * 4;
-        if (hipMemcpy2DAsync(S_T, row, wST + (int64_t)n_mid * H * st, row * (n_mid + 1), row,
-                             (size_t)n_seqs, hipMemcpyDeviceToDevice, stream) != hipSuccess)
-            return KDA_ERR_HIP;
-    }
-    return KDA_OK;
+    if (kda::launch_chunk_fwd(pl, bf16_in, 16, false, fk.fork()) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chunk_fwd(pm, bf16_in, 32, false, stream) != hipSuccess) return KDA_ERR_HIP;
+    fk.join();
+    return fk.ok ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,

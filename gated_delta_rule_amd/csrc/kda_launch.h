@@ -72,11 +72,14 @@ hipError_t launch_chunk_fwd_dual(const PrefillParams& prm, bool bf16_in, hipStre
 
 // Incoming states of the segmented prefill's segments after the first:
 // S_in[b, 0] = E[b] (the first segment's final state), S_in[b, j + 1] =
-// F[b, j] S_in[b, j] + Sl[b, j] for the n_mid segments whose transition F and
-// zero-start final state Sl were computed.  E [B, H, 128, 128], F and Sl
-// [B * n_mid, H, 128, 128], S_in [B * (n_mid + 1), H, 128, 128].
-hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_in,
-                                int32_t B, int32_t n_mid, int32_t H, hipStream_t stream);
+// F[b, j] S_in[b, j] + Sl[b, j] for the n_mid middle segments, whose
+// transition F and zero-start final state Sl were computed.  S_in[b, j] for
+// j < n_mid goes to S_mid[b, j], S_in[b, n_mid] (the last segment's) to
+// S_last[b].  E and S_last [B, H, 128, 128]; F, Sl and S_mid
+// [B * n_mid, H, 128, 128].
+hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_mid,
+                                float* S_last, int32_t B, int32_t n_mid, int32_t H,
+                                hipStream_t stream);
 
 // Multi-token recurrent decode: per state, apply the first n_replay[b]
 // (NULL: all Tr) replay tokens, then T tokens with outputs; the state is

@@ -86,7 +86,7 @@ __device__ __forceinline__ uint32_t lds_addr(const __bf16* p) {
 // backward's per-chunk values skip Q+ S, q e^{g}, QX and M altogether.
 // STORE_H: also store, per chunk, the state at its start (h_states), V - K+ S
 // (r_out) and U (u_out), as chunk_fwd_kernel does for the backward pass.
-template <int NSCAN, bool STORE_H, bool WANT_O>
+template <int NSCAN, bool STORE_H, bool WANT_O, bool SEG>
 __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(PrefillParams p) {
     constexpr int WCOLS = 16;         // value columns per consumer wave
     constexpr int DVW = 4 * WCOLS;    // value columns per workgroup
@@ -109,6 +109,15 @@ __global__ __launch_bounds__(64 * (8 + NSCAN)) void chunk_fwd_pipe_kernel(Prefil
         int64_t a = p.cu[n], b = p.cu[n + 1];
         t0 = a < 0 ? 0 : (a > Tt ? Tt : a);
         t1 = b < t0 ? t0 : (b > Tt ? Tt : b);
+    } else if constexpr (SEG) {
+        // a first segment of its own length (seg_first, seg_r0)
+        const int64_t b = n / p.seg_per_seq;
+        const int64_t r = p.seg_r0 + (n - b * p.seg_per_seq);
+        const int64_t len = r == 0 ? p.seg_first : p.seg_len;
+        const int64_t e = (b + 1) * Tt;
+        t0 = b * Tt + (r == 0 ? 0 : p.seg_first + (r - 1) * p.seg_len);
+        t0 = t0 < e ? t0 : e;
+        t1 = e - t0 > len ? t0 + len : e;
     } else {
         const int64_t b = p.seg_sel >= 0 ? n : n / p.seg_per_seq;
         const int64_t r = p.seg_sel >= 0 ? p.seg_sel : n - b * p.seg_per_seq;
@@ -699,14 +708,17 @@ hipError_t launch_chunk_fwd_pipe(const PrefillParams& p, hipStream_t stream) {
     // the per-chunk outputs are only kept for the backward pass, which takes
     // no o (the launch is refused if both are asked for)
     if (p.h_states && p.o) return hipErrorInvalidValue;
-    // uniform segments only
-    if (p.seg_r0 != 0 || (p.seg_first != 0 && p.seg_first != p.seg_len)) return hipErrorInvalidValue;
-    if (p.h_states)
-        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, true, false>), grid, block, 0, stream, p);
+    // segments of two lengths: equal-length sequences writing o, no window
+    const bool seg = p.seg_r0 != 0 || (p.seg_first != 0 && p.seg_first != p.seg_len);
+    if (seg && (p.cu || p.seg_sel >= 0 || !p.o || p.seg_first <= 0)) return hipErrorInvalidValue;
+    if (seg)
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false, true, true>), grid, block, 0, stream, p);
+    else if (p.h_states)
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, true, false, false>), grid, block, 0, stream, p);
     else if (p.o)
-        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false, true, false>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((chunk_fwd_pipe_kernel<KDA_PIPE_NSCAN, false, false, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

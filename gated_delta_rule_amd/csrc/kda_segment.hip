@@ -11,7 +11,8 @@
 // segment starts from the known initial state, so it runs once, directly;
 // its final state E opens one left-to-right pass over the middle segments,
 //   S_in[0] = E,  S_in[j + 1] = F[j] S_in[j] + Sl[j],
-// which gives the incoming state of every later segment, after which those
+// which gives the incoming state of every later segment (the middle ones
+// and the last one, which has no transition of its own), after which those
 // segments rerun from their true S_in.
 //
 // One workgroup per (sequence, head, 16-column block of S): the 128 x 16
@@ -29,7 +30,7 @@ constexpr int MG_LDF = 132;     // LDS row stride of F (floats)
 
 __global__ __launch_bounds__(MG_THREADS) void segment_merge_kernel(
     const float* __restrict__ F, const float* __restrict__ Sl, const float* __restrict__ E,
-    float* __restrict__ S_in, int32_t n_mid, int32_t H) {
+    float* __restrict__ S_mid, float* __restrict__ S_last, int32_t n_mid, int32_t H) {
     constexpr size_t ST = 128 * 128;
     const int cb = blockIdx.x & 7;
     const int bh = blockIdx.x >> 3;
@@ -47,11 +48,11 @@ __global__ __launch_bounds__(MG_THREADS) void segment_merge_kernel(
     for (int i = 0; i < 8; ++i) s[i] = E[own + (size_t)(rg + 16 * i) * 128 + col];
 
     for (int r = 0; r <= n_mid; ++r) {
-        const size_t out = (((size_t)b * (n_mid + 1) + r) * H + h) * ST;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) S_in[out + (size_t)(rg + 16 * i) * 128 + col] = s[i];
-        if (r == n_mid) break;
         const size_t base = (((size_t)b * n_mid + r) * H + h) * ST;
+        float* out = r < n_mid ? S_mid + base : S_last + own;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[(size_t)(rg + 16 * i) * 128 + col] = s[i];
+        if (r == n_mid) break;
         const float4* Fg = reinterpret_cast<const float4*>(F + base);
         for (int e = tid; e < 128 * 32; e += MG_THREADS)
             *reinterpret_cast<float4*>(&sF[(e >> 5) * MG_LDF + 4 * (e & 31)]) = Fg[e];
@@ -78,10 +79,12 @@ __global__ __launch_bounds__(MG_THREADS) void segment_merge_kernel(
     }
 }
 
-hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_in,
-                                int32_t B, int32_t n_mid, int32_t H, hipStream_t stream) {
+hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_mid,
+                                float* S_last, int32_t B, int32_t n_mid, int32_t H,
+                                hipStream_t stream) {
     dim3 grid((unsigned)((int64_t)B * H * 8)), block(MG_THREADS);
-    hipLaunchKernelGGL(segment_merge_kernel, grid, block, 0, stream, F, Sl, E, S_in, n_mid, H);
+    hipLaunchKernelGGL(segment_merge_kernel, grid, block, 0, stream, F, Sl, E, S_mid, S_last, n_mid,
+                       H);
     return hipGetLastError();
 }
 

@@ -94,7 +94,8 @@ const char* kda_status_str(int status);
  *       pairs) and T is long, the sequence-parallel path cuts every
  *       sequence into P = min(256 / (n_seqs * H), T / 2048) segments, if
  *       that is at least 3 (every segment a whole number of 32-token chunks
- *       but the last; the first about 2.5 times as long as the others), and
+ *       but the last; the first and the last about twice as long as the
+ *       others), and
  *       needs (3 * P - 4) * n_seqs * H * 64 KiB (the transition and local
  *       final state of each of the P - 2 middle segments, the incoming state
  *       of each of the P - 1 later segments and the first segment's final
@@ -115,9 +116,9 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  * from S0 (writing its o) beside the middle segments, which run as
  * independent chains from zero and from the identity (their local final
  * states and d_k x d_k transitions); a merge through the transitions gives
- * the incoming state of every later segment, which then reruns from it and
- * writes its o; "Kimi K3 技术报告解读" section 7.3 describes this within-GPU
- * split.  The chunkwise
+ * the incoming state of every later segment, from which the middle segments
+ * run again and the last one runs once, writing their o; "Kimi K3 技术报告解读"
+ * section 7.3 describes this within-GPU split.  The chunkwise
  * evaluation (cumulative in-chunk log-decay, k+ = k e^{g}, k- = k e^{-g},
  * the strictly lower-triangular A_tj = beta_t k+_t . k-_j solved by forward
  * substitution, O = Q+ S + Tril(Q+ K-^T) U and the state hand-off
@@ -166,9 +167,9 @@ size_t kda_chunk_fwd_workspace_bytes(int32_t n_seqs, int64_t T, int32_t H,
  *   The two plans round differently, so the same sequence can give results
  *   that differ in the last bits depending on how many (sequence, head)
  *   pairs share the call; both stay within 2e-3 of the exact recurrence.
- *   On the sequence-parallel path the first segment of every sequence runs
- *   on the two-workgroup plan and the later segments on the one-workgroup
- *   plan.
+ *   On the sequence-parallel path the first and the last segment of every
+ *   sequence run on the two-workgroup plan and the middle segments on the
+ *   one-workgroup plan.
  * The chunk form carries per-channel factors of up to e^{+-80}: in a key
  * channel whose decay sits at the bound (log_alpha = -5 for 16 tokens) the
  * state enters the products scaled by e^{-80}, so its entries below about

@@ -21,7 +21,7 @@ int fails = 0;
 int fail_fwd_in = -1;   // > 0: the forward launch that many calls from now fails
 // forward and backward launches in order, for the backward's window plan
 struct Rec {
-    char kind;                 // 'f' forward, 'd' dual-chain forward, 'm' merge, 'c' copy,
+    char kind;                 // 'f' forward, 'd' dual-chain forward, 'm' merge,
                                // 't' chunk matrices, 'g' walk + gradients,
                                // 'r' event record, 'w' stream waits for event
     int seg_sel, win_idx;
@@ -89,14 +89,15 @@ hipError_t launch_chunk_fwd_dual(const PrefillParams& p, bool, hipStream_t strea
     CHECK(p.n_units == p.n_seqs * p.H);
     return hipSuccess;
 }
-hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_in, int32_t B,
-                                int32_t n_mid, int32_t H, hipStream_t stream) {
+hipError_t launch_segment_merge(const float* F, const float* Sl, const float* E, float* S_mid,
+                                float* S_last, int32_t B, int32_t n_mid, int32_t H, hipStream_t stream) {
     ++n_merge;
-    Rec r{'m', -1, -1, false, E, S_in, F, nullptr, n_mid, 0, 0, stream, nullptr};
+    // S0 = E, S_T = S_mid, dS_T = F, S_T2 = Sl, dS0 = S_last, seg_len = n_mid
+    Rec r{'m', -1, -1, false, E, S_mid, F, S_last, n_mid, 0, 0, stream, nullptr};
     r.S_T2 = Sl;
     r.n_seqs = B;
     rec(r);
-    CHECK(B >= 1 && n_mid >= 1 && H >= 1 && F && Sl && E && S_in);
+    CHECK(B >= 1 && n_mid >= 1 && H >= 1 && F && Sl && E && S_mid && S_last);
     return hipSuccess;
 }
 hipError_t launch_recurrent(const void*, const void*, const void*, bool, const float*, const float*,
@@ -160,17 +161,6 @@ hipError_t hipStreamWaitEvent(hipStream_t s, hipEvent_t e, unsigned int) {
     rec(Rec{'w', -1, -1, false, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, s, e});
     return hipSuccess;
 }
-// 'c': S0 = source, S_T = destination, seg_len = width, win_len = height,
-// slots = source pitch (bytes), seg_first = destination pitch
-hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
-                            size_t height, hipMemcpyKind kind, hipStream_t s) {
-    Rec r{'c', -1, -1, false, (const float*)src, (float*)dst, nullptr, nullptr, (int64_t)width,
-          (int64_t)height, (int64_t)spitch, s, nullptr};
-    r.seg_first = (int64_t)dpitch;
-    rec(r);
-    CHECK(kind == hipMemcpyDeviceToDevice && width <= dpitch && width <= spitch);
-    return hipSuccess;
-}
 
 // 1 TiB apart, so no two of them overlap at these sizes
 static const void* P(int i) { return (const void*)(uintptr_t)((1ull << 44) + (uint64_t)i * (1ull << 40)); }
@@ -188,12 +178,13 @@ int main() {
     // packed batch with its order workspace
     CHECK(kda_chunk_fwd(P(0), P(1), P(2), KDA_BF16, F(3), F(4), nullptr, (const int32_t*)P(8), 32,
                         270000, 96, 128, 128, F(5), nullptr, (void*)P(9), 128, nullptr) == KDA_OK);
-    // sequence-parallel path: segment 0 from S0 (writing o) on the second
-    // stream beside the dual-chain pass over the middle segments, the merge
-    // from segment 0's final state, the rerun of segments 1 .. P-1 and the
-    // copy of the last segments' final states.  The segments of the plan
-    // (the kernels' mapping from chain index to tokens, restated here) tile
-    // every sequence exactly, and both passes fit the 256 compute units.
+    // sequence-parallel path.  Pass 1: segment 0 from S0 (writing o) on the
+    // second stream beside the dual-chain pass over the middle segments; the
+    // merge from segment 0's final state; pass 2: the last segment (from its
+    // incoming state, writing o and S_T) on the second stream beside the
+    // rerun of the middle segments.  The segments of the plan (the kernels'
+    // mapping from chain index to tokens, restated here) tile every sequence
+    // exactly, and both passes fit the 256 compute units.
     hipStream_t const kMainF = (hipStream_t)(uintptr_t)0x3400;
     auto seg_range = [](const Rec& f, int64_t T, int64_t n, int64_t* t0, int64_t* t1) {
         const int64_t b = n / f.seg_per_seq, r = f.seg_r0 + (n - b * f.seg_per_seq);
@@ -211,64 +202,63 @@ int main() {
         n_recs = 0;
         CHECK(kda_chunk_fwd(P(0), P(1), P(2), dtype, F(3), F(4), S0, nullptr, n_seqs, T, H, 128,
                             128, F(5), S_T, (void*)P(9), ws, kMainF) == KDA_OK);
-        const Rec *f0 = nullptr, *fd = nullptr, *fm = nullptr, *fc = nullptr, *cp = nullptr;
-        bool forked = false, joined = false;
+        // launches in order, with the fork / join state at each
+        const Rec* L[8] = {};
+        bool forked[8] = {}, side_joined = false;
+        int nl = 0, joins = 0;
         hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+        bool fork_open = false;
         for (int i = 0; i < n_recs; ++i) {
             const Rec& r = recs[i];
-            if (r.kind == 'r' && r.stream == kMainF) fork_ev = r.event;
-            else if (r.kind == 'w' && r.stream == kSide) forked = r.event == fork_ev && fork_ev;
+            if (r.kind == 'r' && r.stream == kMainF) { fork_ev = r.event; fork_open = false; }
+            else if (r.kind == 'w' && r.stream == kSide) fork_open = r.event == fork_ev && fork_ev;
             else if (r.kind == 'r' && r.stream == kSide) join_ev = r.event;
-            else if (r.kind == 'w' && r.stream == kMainF) joined = r.event == join_ev && join_ev && f0 && fd;
-            else if (r.kind == 'f' && !f0) { f0 = &r; CHECK(r.stream == kSide && forked && !joined); }
-            else if (r.kind == 'd') { fd = &r; CHECK(r.stream == kMainF && !joined); }
-            else if (r.kind == 'm') { fm = &r; CHECK(r.stream == kMainF && joined); }
-            else if (r.kind == 'f') { fc = &r; CHECK(r.stream == kMainF && fm); }
-            else if (r.kind == 'c') { cp = &r; CHECK(r.stream == kMainF && fc); }
+            else if (r.kind == 'w' && r.stream == kMainF) { CHECK(r.event == join_ev && join_ev); ++joins; side_joined = true; }
+            else if (nl < 8 && r.kind != 'r' && r.kind != 'w') {
+                forked[nl] = r.stream == kSide && fork_open;
+                L[nl++] = &r;
+                if (r.stream == kSide) side_joined = false;
+            }
         }
-        CHECK(f0 && fd && fm && fc && (S_T ? cp != nullptr : cp == nullptr));
-        if (!(f0 && fd && fm && fc)) return;
-        const int Pn = fd->seg_per_seq + 2;
+        CHECK(nl == 5 && joins == 2 && side_joined);
+        if (nl != 5) return;
+        const Rec &f0 = *L[0], &fd = *L[1], &fm = *L[2], &fl = *L[3], &fc = *L[4];
+        CHECK(f0.kind == 'f' && forked[0] && fd.kind == 'd' && fd.stream == kMainF);
+        CHECK(fm.kind == 'm' && fm.stream == kMainF);
+        CHECK(fl.kind == 'f' && forked[3] && fc.kind == 'f' && fc.stream == kMainF);
+        const int Pn = fd.seg_per_seq + 2;
         CHECK(Pn == expect_P);
-        // segment 0: from S0, writes o and its final state E
-        CHECK(f0->seg_r0 == 0 && f0->seg_per_seq == 1 && f0->n_seqs == n_seqs && f0->has_o &&
-              f0->S0 == S0 && f0->S_T && f0->n_slices == 2 && f0->n_units == units &&
-              f0->seg_first == 0);   // one uniform segment: the pipelined kernel's mapping
+        // segment 0: from S0, writes o and its final state E (one uniform
+        // segment: the pipelined kernel's plain mapping)
+        CHECK(f0.seg_r0 == 0 && f0.seg_per_seq == 1 && f0.n_seqs == n_seqs && f0.has_o &&
+              f0.S0 == S0 && f0.S_T && f0.n_slices == 2 && f0.n_units == units && f0.seg_first == 0);
         // dual pass over the middle segments: no o, from zero and from I
-        CHECK(fd->seg_r0 == 1 && fd->n_seqs == n_seqs * (Pn - 2) && fd->n_slices == 1 && !fd->has_o);
-        // the merge: E -> incoming states of segments 1 .. P-1
-        CHECK(fm->S0 == f0->S_T && fm->dS_T == fd->S_T2 && fm->S_T2 == fd->S_T &&
-              fm->seg_len == Pn - 2 && fm->n_seqs == n_seqs);
-        // rerun of segments 1 .. P-1 from the merged states, writes o
-        CHECK(fc->seg_r0 == 1 && fc->seg_per_seq == Pn - 1 && fc->n_seqs == n_seqs * (Pn - 1) &&
-              fc->has_o && fc->S0 == fm->S_T && (S_T ? fc->S_T != nullptr : fc->S_T == nullptr));
-        CHECK(fd->seg_len == fc->seg_len && fd->seg_first == fc->seg_first && f0->seg_len == fc->seg_first);
-        CHECK(fc->n_slices == 1 && units * Pn <= 256 && units * (Pn - 1) <= 256);
-        // tiling: segment 0 from f0, 1 .. P-2 from fd, 1 .. P-1 from fc
+        CHECK(fd.seg_r0 == 1 && fd.n_seqs == n_seqs * (Pn - 2) && fd.n_slices == 1 && !fd.has_o);
+        // the merge: E -> incoming states (middle segments, last segment)
+        CHECK(fm.S0 == f0.S_T && fm.dS_T == fd.S_T2 && fm.S_T2 == fd.S_T &&
+              fm.seg_len == Pn - 2 && fm.n_seqs == n_seqs);
+        // the middle segments rerun from their incoming states, write o
+        CHECK(fc.seg_r0 == 1 && fc.seg_per_seq == Pn - 2 && fc.n_seqs == n_seqs * (Pn - 2) &&
+              fc.has_o && fc.S0 == fm.S_T && fc.S_T == nullptr && fc.n_slices == 1);
+        CHECK(fc.seg_len == fd.seg_len && fc.seg_first == fd.seg_first && f0.seg_len == fd.seg_first);
+        // the last segment: from its incoming state, writes o and S_T
+        CHECK(fl.seg_r0 == 1 && fl.seg_per_seq == 1 && fl.n_seqs == n_seqs && fl.n_slices == 2 &&
+              fl.has_o && fl.S_T == S_T && fl.S0 == fm.dS0 && fl.seg_len >= T);
+        CHECK(units * Pn <= 256);
         for (int64_t b = 0; b < n_seqs; ++b) {
             int64_t t0, t1, at = b * T;
-            seg_range(*f0, T, b, &t0, &t1);
+            seg_range(f0, T, b, &t0, &t1);
             CHECK(t0 == at && t1 > t0 && (t1 - t0) % 32 == 0);
             at = t1;
-            for (int r = 1; r < Pn; ++r) {
-                int64_t c0, c1;
-                seg_range(*fc, T, b * (Pn - 1) + (r - 1), &c0, &c1);
-                CHECK(c0 == at && c1 > c0 && (c0 - b * T) % 32 == 0);
-                if (r < Pn - 1) {
-                    int64_t d0, d1;
-                    seg_range(*fd, T, b * (Pn - 2) + (r - 1), &d0, &d1);
-                    CHECK(d0 == c0 && d1 == c1);
-                }
+            for (int r = 1; r < Pn - 1; ++r) {
+                int64_t c0, c1, d0, d1;
+                seg_range(fc, T, b * (Pn - 2) + (r - 1), &c0, &c1);
+                seg_range(fd, T, b * (Pn - 2) + (r - 1), &d0, &d1);
+                CHECK(c0 == at && c1 > c0 && (c1 - c0) % 32 == 0 && d0 == c0 && d1 == c1);
                 at = c1;
             }
-            CHECK(at == (b + 1) * T);
-        }
-        if (cp) {
-            // the last segment's final state of every sequence, [n_seqs, H] rows
-            const int64_t row = (int64_t)H * 65536;
-            CHECK(cp->S_T == S_T && cp->seg_len == row && cp->win_len == n_seqs &&
-                  cp->seg_first == row && cp->slots == row * (Pn - 1) &&
-                  (const char*)cp->S0 == (const char*)fc->S_T + (Pn - 2) * row);
+            seg_range(fl, T, b, &t0, &t1);
+            CHECK(t0 == at && t1 == (b + 1) * T && t1 - t0 >= 32);
         }
     };
     seq_parallel_plan(1, 1 << 20, 16, nullptr, F(6), 16);   // 1M tokens, 16 heads
