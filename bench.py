@@ -116,7 +116,7 @@ def long_context(torch, kda, W, dev, reps=3):
     return {"workload": f"KDA prefill B=1 T={T} H={H} d=128 bf16, S0=0 (device-drawn inputs)",
             "tokens_per_s": T / (ms * 1e-3), "ms": ms,
             "sequential_path_ms": out["sequential"],
-            "path": "sequence-parallel: segments from zero and from the identity, merge, rerun",
+            "path": "sequence-parallel: the first segment from S0 beside the middle segments from zero and from the identity, merge, the middle segments rerun beside the last one",
             "workspace_bytes": ws_bytes}
 
 
