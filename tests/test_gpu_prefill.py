@@ -243,6 +243,99 @@ def test_sequence_parallel_agrees_with_sequential_and_in_place():
     assert torch.equal(o_i, o_p) and torch.equal(S, s_p)   # S_T may be S0
 
 
+def _seq_parallel_job(T, H, B, seed_s0=0.02):
+    """Device inputs, outputs and workspace of one sequence-parallel call."""
+    w, arrs = small(T, H, B, seed_s0)
+    d = to_dev(arrs, w)
+    lib = kda.load_library()
+    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, 128, 128, 0)
+    assert wsb > 0
+    return dict(d=d, B=B, T=T, H=H, wsb=wsb,
+                ws=torch.empty(wsb, dtype=torch.uint8, device="cuda"),
+                o=torch.empty(d["v"].shape, dtype=torch.float32, device="cuda"),
+                st=torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda"))
+
+
+def _seq_parallel_call(job, stream_handle, noalloc=False):
+    import ctypes
+    lib = kda.load_library()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+    d = job["d"]
+    args = [vp(d["q"]), vp(d["k"]), vp(d["v"]), kda.KDA_BF16, vp(d["log_alpha"]), vp(d["beta"]),
+            vp(d["S0"]), None, job["B"], job["T"], job["H"], 128, 128, vp(job["o"]), vp(job["st"])]
+    if noalloc:
+        return lib.kda_chunk_fwd_noalloc(*args, ctypes.c_void_p(stream_handle))
+    return lib.kda_chunk_fwd(*args, vp(job["ws"]), job["wsb"], ctypes.c_void_p(stream_handle))
+
+
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_sequence_parallel_graph_capture_replays_bitwise(noalloc):
+    """The sequence-parallel path runs each pass as two launches, one on the
+    library's second stream (forked from and joined back into the caller's
+    stream by events), so a HIP graph captured on the caller's stream takes
+    in both: captured once, replayed three times with eager work and
+    synchronisations between the replays, every replay equals the eager
+    result bitwise (with a caller's workspace, and through the entry point
+    that allocates nothing)."""
+    job = _seq_parallel_job(7000, 3, 2)
+    say(f"[prefill] graph capture (sequence-parallel, noalloc={noalloc}): eager")
+    assert _seq_parallel_call(job, torch.cuda.current_stream().cuda_stream, noalloc) == 0
+    torch.cuda.synchronize()
+    ref = (job["o"].clone(), job["st"].clone())
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    say("[prefill] graph capture: capture")
+    with torch.cuda.graph(g, stream=s):
+        rc = _seq_parallel_call(job, s.cuda_stream, noalloc)
+    assert rc == 0
+    for rep in range(3):
+        job["o"].fill_(float("nan"))
+        job["st"].fill_(float("nan"))
+        job["ws"].fill_(0xFF)
+        torch.cuda.synchronize()
+        say(f"[prefill] graph capture: replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(job["o"], ref[0]) and torch.equal(job["st"], ref[1])
+
+
+def test_sequence_parallel_concurrent_threads_bitwise():
+    """Two host threads run sequence-parallel calls at the same time on their
+    own streams, inputs, outputs and workspaces (they share the library's
+    second stream and its events and enqueue under one lock): every result
+    equals the same call made alone, bitwise."""
+    import threading
+    jobs = [_seq_parallel_job(7000, 3, 2), _seq_parallel_job(8192, 4, 1)]
+    for job in jobs:
+        job["stream"] = torch.cuda.Stream()
+    say("[prefill] two threads: each call alone")
+    ref = []
+    for job in jobs:
+        assert _seq_parallel_call(job, job["stream"].cuda_stream) == 0
+        torch.cuda.synchronize()
+        ref.append((job["o"].clone(), job["st"].clone()))
+    for rep in range(3):
+        for job in jobs:
+            job["o"].fill_(float("nan"))
+            job["st"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        rcs = [None, None]
+
+        def worker(i):
+            rcs[i] = [_seq_parallel_call(jobs[i], jobs[i]["stream"].cuda_stream) for _ in range(2)]
+
+        say(f"[prefill] two threads: round {rep}")
+        th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+        torch.cuda.synchronize()
+        assert rcs == [[0, 0], [0, 0]]
+        for job, (o, st) in zip(jobs, ref):
+            assert torch.equal(job["o"], o) and torch.equal(job["st"], st)
+
+
 def _sampled_check(w, heads, label, seqs=None, cols=None):
     say(f"[prefill] {label}: generating inputs on the device")
     d, cu = device_prefill_inputs(w)
