@@ -59,9 +59,10 @@ int32_t seg_count(int64_t n_seqs, int64_t T, int64_t H) {
 }
 
 // Segment 0 : L = R0 / 16 and last : L = R1 / 16.  With T >= 2048 P and
-// ratios of 16 .. 48 sixteenths, L (rounded down to whole chunks), segment 0
-// and the last segment all come to at least 864 tokens: the plan never
-// degenerates (the check below only guards the arithmetic).
+// ratios of 16 .. 48 sixteenths, L (rounded down to whole chunks) and
+// segment 0 come to at least 864 tokens and the last segment to at least
+// 832: the plan never degenerates (the check below only guards the
+// arithmetic).
 Split split_for(int64_t n_seqs, int64_t T, int64_t H, bool bf16_in) {
     const int64_t R0 = bf16_in ? 34 : 32;
     const int64_t R1 = bf16_in ? 26 : 28;
@@ -74,9 +75,11 @@ Split split_for(int64_t n_seqs, int64_t T, int64_t H, bool bf16_in) {
 }
 
 // A second stream per device (default priority, not synchronising with the
-// null stream) on which the backward's chunk-matrix pass runs beside the
-// forward pass it does not depend on, and the two events that order it
-// against the caller's stream.  Created on first use and kept until the
+// null stream) on which one launch of a pair runs beside the other (the
+// backward's chunk-matrix pass beside the forward pass it does not depend
+// on; the sequence-parallel prefill's first or last segment beside its
+// middle segments), and the two events that order it against the caller's
+// stream.  Created on first use and kept until the
 // process ends (events are never destroyed while a wait may still refer to
 // them); a call holds the device's lock while it enqueues, so calls from
 // several host threads cannot interleave their records.

@@ -300,11 +300,40 @@ def collect_phases(out, profiles_dir, run=True):
     print(f"contraction phases -> {path}", flush=True)
 
 
+def code_only(text):
+    """C/C++ source without its comments, indentation or blank lines, so that
+    a record stays valid while only the comments around a kernel change.
+    String and character literals are kept as written."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (" ".join(line.split()) for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
 def sources_hash(kind):
+    """Hash of the code (comments and blank space removed) of the sources a
+    profiled kernel is built from."""
     h = hashlib.sha256()
     for name in TARGETS[kind][2]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
