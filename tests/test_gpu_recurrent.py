@@ -102,6 +102,37 @@ def test_speculative_replay(commit):
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
 
 
+@pytest.mark.parametrize("T,Tr", [(2, 0), (3, 0), (9, 0), (1, 1), (1, 2), (2, 1), (0, 3)])
+def test_forms_around_the_threshold(T, Tr):
+    """Two tokens per state (new plus replayed) run the 1024-thread form,
+    three or more the 512-thread form (eight tokens per staging pass, so 9
+    takes two passes): each against the oracle, with the replay count of
+    every request drawn below or at Tr, committing after all tokens."""
+    B, H = 6, 3
+    rep, _ = tokens(B, max(Tr, 1), H, seed=7)
+    new, _ = tokens(B, max(T, 1), H, seed=8)
+    rep = {x: a[:, :Tr] for x, a in rep.items()}
+    new = {x: a[:, :T] for x, a in new.items()}
+    S0 = state(B, H, seed=9)
+    n = (np.arange(B) % (Tr + 1)).astype(np.int32)
+    dr, dn = dev(rep, "bf16"), dev(new, "bf16")
+    S = torch.from_numpy(S0).cuda()
+    say(f"[recurrent] T={T} Tr={Tr}: GPU")
+    o = kda.recurrent_fwd(dn["q"], dn["k"], dn["v"], dn["log_alpha"], dn["beta"], S,
+                          replay=tuple(dr[x] for x in NAMES) if Tr else None,
+                          n_replay=torch.from_numpy(n).cuda() if Tr else None, commit=True)
+    torch.cuda.synchronize()
+    s_mid = oracle_run(rep, S0, n)[1] if Tr else S0.astype(np.float64)
+    if T:
+        ro, s_end = oracle_run(new, s_mid.astype(np.float64))
+        eo = rel_err(o.cpu().numpy(), ro)
+    else:
+        s_end, eo = s_mid, 0.0
+    es = rel_err(S.cpu().numpy(), s_end)
+    say(f"[recurrent] T={T} Tr={Tr}: rel err o {eo:.3e} S {es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
 def test_replay_all_and_state_only():
     """n_replay omitted (all replay tokens) and no new tokens: the state
     advances by the replay alone."""
