@@ -163,10 +163,15 @@ def multi_token_decode(torch, kda, W, dev, T=8, reps=5):
                                               commit=False, o=o4))
     del S, new, rep, drafts, o, o4
     torch.cuda.empty_cache()
+    # algorithmic bytes: the fp32 state read and written once, and per token
+    # q, k, v (bf16), log alpha, o (fp32) and beta
+    nbytes = B * H * (2 * 128 * 128 * 4 + T * (3 * 128 * 2 + 2 * 128 * 4 + 4))
     return {"workload": f"KDA recurrent decode B={B} H={H} d=128, {T} tokens per request, "
                         "fp32 state in place (device-drawn inputs)",
             "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
             "ms_per_token": ms / T,
+            "hbm_bytes_algorithmic": nbytes,
+            "hbm_frac": nbytes / (ms * 1e-3) / (PEAK_HBM_GBPS * 1e9),
             "speculative_step_ms": ms_spec,
             "speculative_step": "replay of up to 4 accepted drafts + 4 new drafts, commit after replay"}
 
