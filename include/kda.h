@@ -245,6 +245,11 @@ int kda_decode_step(const void* q, const void* k, const void* v, int in_dtype,
  *         S [B, H, dk, dv] float32, read and overwritten in place;
  *         o [B, T, H, dv] float32 (must not overlap any input or S).
  * Sizes: 0 <= T <= 64, 0 <= Tr <= 64.  Replay and new tokens share in_dtype.
+ * Numerics: fp32 throughout.  With T + Tr <= 2 the kernel is the one of
+ * kda_decode_step (T = 1, Tr = 0 gives its bits exactly); with T + Tr >= 3
+ * a form with two workgroups per compute unit runs, whose sums over key
+ * rows are formed in a different order, so results agree with the other
+ * form to fp32 rounding, not bitwise.  Both are deterministic.
  */
 int kda_recurrent_fwd(const void* q, const void* k, const void* v, int in_dtype,
                       const float* log_alpha, const float* beta, const void* rq,
