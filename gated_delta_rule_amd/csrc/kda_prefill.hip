@@ -9,8 +9,9 @@
 //   S   <- Diag(e^{g_C}) S + K_end^T U,  k_end = k e^{g_C - g}          (66)
 //
 // This kernel runs fp32 inputs, and bf16 inputs with 32 value columns per
-// consumer wave (one workgroup per head, used when there are 256 or more
-// (sequence, head) units); bf16 with two 64-column slices per head runs the
+// consumer wave (one workgroup per head: with 256 or more (sequence, head)
+// units, and for the sequence-parallel path's dual-chain pass and the rerun
+// of its middle segments); bf16 with two 64-column slices per head runs the
 // pipelined kernel of kda_prefill_pipe.hip instead.
 //
 // MI355X design (not the pages' two-kernel split):
