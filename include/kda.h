@@ -94,9 +94,9 @@ const char* kda_status_str(int status);
  *       pairs) and T is long, the sequence-parallel path cuts every
  *       sequence into P = min(256 / (n_seqs * H), T / 2048) segments, if
  *       that is at least 3 (every segment a whole number of 32-token chunks
- *       but the last; the first and the last about twice as long as the
- *       others), and
- *       needs (3 * P - 4) * n_seqs * H * 64 KiB (the transition and local
+ *       but the last; the first and the last 1.6 to 2.1 times as long as
+ *       the others), and needs (3 * P - 4) * n_seqs * H * 64 KiB (the
+ *       transition and local
  *       final state of each of the P - 2 middle segments, the incoming state
  *       of each of the P - 1 later segments and the first segment's final
  *       state).  That workspace is optional: without it (NULL or smaller),
